@@ -1,0 +1,268 @@
+/*
+ * TriAttention KV-cache pruning: reference oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is a plain, slow, fp64 CPU implementation of
+ * what the pruning path computes.  It exists to check the HIP library against;
+ * only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load it.  It shares no code, header, table or constant with the HIP library.
+ *
+ * Sources (web pages describing TriAttention; their formulas were lost in
+ * extraction, so every step below restates the prose in my own notation):
+ *   [YY] "实现单卡4090跑通OpenClaw!英伟达&浙大等提出长上下文推理KV压缩新方法
+ *        TriAttention" (yeyulingfeng.com), section 主要方法.
+ *   [ZN] "TriAttention：用三角级数压缩KV缓存，让长推理模型跑在消费级显卡上"
+ *        (zingnex.cn), sections 预RoPE空间的发现 and
+ *        TriAttention的核心机制：三角级数距离建模.
+ *
+ * Notation.  d = head_dim, F = d/2 rotary bands.  Band f of a stored (post-RoPE)
+ * row x is the complex number x[f] + i x[f+F] (half-split pairing) with angular
+ * frequency w_f = theta^(-2f/d).  A key stored at position p is the pre-RoPE key
+ * k_f rotated by e^{i w_f p}.  A query head h has an offline centre per band
+ * with magnitude M[h][f], phase phi[h][f] and concentration R[h][f] (mean
+ * resultant length).  t is the position of the next query; O is the offset set.
+ *
+ * Parity status: every function here is pinned by a CPU test (closed forms,
+ * invariants, brute force on tiny inputs, hand-worked fixtures) except that no
+ * check can reach the paper's own (lost) score formula: the score is this
+ * reconstruction, see orc_score_segment.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Exact value of stored element i (fp32, or bf16 widened by a 16-bit shift). */
+static double stored_value(const void* base, int dtype, int64_t i) {
+    if (dtype == ORC_F32) return (double)((const float*)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Key importance scores of one segment (one KV head of one layer of one
+ * sequence) for its G query heads.
+ *
+ * Steps, in the order [YY] 主要方法 gives them:
+ *  1. Un-rotate.  The key's band representation in the pre-RoPE space:
+ *     magnitude |k_f| = |x_f| (a rotation keeps length) and phase
+ *     psi_f = arg(x_f) - w_f p.
+ *  2. Trigonometric-series term.  Under RoPE the query/key logit is a sum over
+ *     bands of a cosine of (w_f * relative distance + phase difference); with
+ *     the query replaced by its offline centre it depends on the distance only
+ *     ([YY] 主要方法, paragraph on rewriting the RoPE logit; [ZN] 核心机制).
+ *     The key is scored at each future query position t+o, o in O, and the
+ *     scores are averaged ([YY] 主要方法, paragraph on geometric future offsets):
+ *        trig_h = (1/|O|) sum_o sum_f M[h][f] |k_f| cos(w_f (t+o-p) + phi[h][f] - psi_f)
+ *  3. Norm term, which compensates for the centre approximation and is
+ *     suppressed where the band is concentrated and boosted where it is not
+ *     ([YY] 主要方法, paragraph on the norm score; [ZN] 核心机制, Q/K norms as an
+ *     auxiliary signal).  Reading: linear weight (1 - R):
+ *        norm_h = sum_f (1 - R[h][f]) M[h][f] |k_f|
+ *  4. Fusion into one importance score ([YY] 主要方法): S_h = trig_h + norm_h.
+ *     Reading: plain sum, no 1/sqrt(d) (z-scoring makes a common scale moot).
+ *
+ * K: [N][d] stored rows; pos: [N]; M, phi, R: [G][F]; offsets: [n_off].
+ * S: [G][N] output.  trig_out / norm_out: optional [G][N] outputs of the two
+ * parts.  Returns 0, or -1 on bad arguments.
+ */
+int orc_score_segment(const void* K, int dtype, const int32_t* pos, int64_t N, int d,
+                      double theta, int64_t t, const float* M, const float* phi,
+                      const float* R, int G, const int64_t* offsets, int n_off,
+                      double* S, double* trig_out, double* norm_out) {
+    if (d <= 0 || (d & 1) || G <= 0 || n_off <= 0 || N < 0) return -1;
+    const int F = d / 2;
+    double* w = (double*)malloc(sizeof(double) * F);
+    double* mag = (double*)malloc(sizeof(double) * F);
+    double* psi = (double*)malloc(sizeof(double) * F);
+    if (!w || !mag || !psi) {
+        free(w); free(mag); free(psi);
+        return -1;
+    }
+    for (int f = 0; f < F; ++f) w[f] = pow(theta, -2.0 * (double)f / (double)d);
+
+    for (int64_t i = 0; i < N; ++i) {
+        const double p = (double)pos[i];
+        /* step 1 */
+        for (int f = 0; f < F; ++f) {
+            const double re = stored_value(K, dtype, i * d + f);
+            const double im = stored_value(K, dtype, i * d + f + F);
+            mag[f] = hypot(re, im);
+            psi[f] = atan2(im, re) - w[f] * p;
+        }
+        for (int h = 0; h < G; ++h) {
+            const float* Mh = M + (int64_t)h * F;
+            const float* ph = phi + (int64_t)h * F;
+            const float* Rh = R + (int64_t)h * F;
+            /* step 2: brute force over every offset and band */
+            double trig = 0.0;
+            for (int o = 0; o < n_off; ++o) {
+                const double delta = (double)(t + offsets[o]) - p;
+                for (int f = 0; f < F; ++f)
+                    trig += (double)Mh[f] * mag[f] * cos(w[f] * delta + (double)ph[f] - psi[f]);
+            }
+            trig /= (double)n_off;
+            /* step 3 */
+            double norm = 0.0;
+            for (int f = 0; f < F; ++f) norm += (1.0 - (double)Rh[f]) * (double)Mh[f] * mag[f];
+            /* step 4 */
+            S[(int64_t)h * N + i] = trig + norm;
+            if (trig_out) trig_out[(int64_t)h * N + i] = trig;
+            if (norm_out) norm_out[(int64_t)h * N + i] = norm;
+        }
+    }
+    free(w); free(mag); free(psi);
+    return 0;
+}
+
+/*
+ * GQA aggregation ([YY] 主要方法, paragraph on GQA): z-score the scores inside
+ * each query head, then take the maximum over the query heads that share the
+ * KV head, so that heads are comparable.
+ * Readings: population mean/standard deviation over all N keys of the segment
+ * (two passes); a head whose scores are all equal (sigma = 0) contributes z = 0.
+ * S: [G][N]; mu, sigma: [G] outputs; A: [N] output.
+ */
+int orc_zscore_max(const double* S, int G, int64_t N, double* mu, double* sigma, double* A) {
+    if (G <= 0 || N < 0) return -1;
+    for (int h = 0; h < G; ++h) {
+        const double* Sh = S + (int64_t)h * N;
+        double sum = 0.0;
+        for (int64_t i = 0; i < N; ++i) sum += Sh[i];
+        const double m = N > 0 ? sum / (double)N : 0.0;
+        double ss = 0.0;
+        for (int64_t i = 0; i < N; ++i) ss += (Sh[i] - m) * (Sh[i] - m);
+        mu[h] = m;
+        sigma[h] = N > 0 ? sqrt(ss / (double)N) : 0.0;
+    }
+    for (int64_t i = 0; i < N; ++i) {
+        double best = -INFINITY;
+        for (int h = 0; h < G; ++h) {
+            const double z = sigma[h] > 0.0 ? (S[(int64_t)h * N + i] - mu[h]) / sigma[h] : 0.0;
+            if (z > best) best = z;
+        }
+        A[i] = best;
+    }
+    return 0;
+}
+
+typedef struct {
+    double a;
+    int32_t slot;
+} ranked_key;
+
+/* Higher aggregated score first; among equal scores the lower slot first. */
+static int by_score_then_slot(const void* x, const void* y) {
+    const ranked_key* p = (const ranked_key*)x;
+    const ranked_key* q = (const ranked_key*)y;
+    if (p->a > q->a) return -1;
+    if (p->a < q->a) return 1;
+    return (p->slot > q->slot) - (p->slot < q->slot);
+}
+
+static int ascending_i32(const void* x, const void* y) {
+    const int32_t a = *(const int32_t*)x, b = *(const int32_t*)y;
+    return (a > b) - (a < b);
+}
+
+/*
+ * Budgeted selection ([YY] 主要方法, paragraph on windowed batch pruning): when
+ * the segment holds more than B keys keep only the B best by aggregated score;
+ * otherwise keep everything.  Reading: ties at the cut go to the lower slot
+ * (earlier key); the kept slots are returned in ascending order.
+ * A: [N]; idx: [min(N,B)] output; *n_kept = min(N, B).
+ */
+int orc_select_topb(const double* A, int64_t N, int64_t B, int32_t* idx, int64_t* n_kept) {
+    if (B <= 0 || N < 0) return -1;
+    if (N <= B) {
+        for (int64_t i = 0; i < N; ++i) idx[i] = (int32_t)i;
+        *n_kept = N;
+        return 0;
+    }
+    ranked_key* r = (ranked_key*)malloc(sizeof(ranked_key) * (size_t)N);
+    if (!r) return -1;
+    for (int64_t i = 0; i < N; ++i) {
+        r[i].a = A[i];
+        r[i].slot = (int32_t)i;
+    }
+    qsort(r, (size_t)N, sizeof(ranked_key), by_score_then_slot);
+    for (int64_t j = 0; j < B; ++j) idx[j] = r[j].slot;
+    qsort(idx, (size_t)B, sizeof(int32_t), ascending_i32);
+    free(r);
+    *n_kept = B;
+    return 0;
+}
+
+/* Same selection on single-precision scores (widened exactly to double, so
+ * -0 and +0 compare equal, as IEEE comparison has them). */
+int orc_select_topb_f32(const float* A, int64_t N, int64_t B, int32_t* idx, int64_t* n_kept) {
+    if (N < 0) return -1;
+    double* a = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    if (!a) return -1;
+    for (int64_t i = 0; i < N; ++i) a[i] = (double)A[i];
+    const int rc = orc_select_topb(a, N, B, idx, n_kept);
+    free(a);
+    return rc;
+}
+
+/* Compaction: dst row j = src row idx[j], byte for byte, j < n. */
+int orc_gather_rows(const void* src, int64_t row_bytes, const int32_t* idx, int64_t n, void* dst) {
+    if (row_bytes <= 0 || n < 0) return -1;
+    for (int64_t j = 0; j < n; ++j)
+        memcpy((char*)dst + j * row_bytes, (const char*)src + (int64_t)idx[j] * row_bytes,
+               (size_t)row_bytes);
+    return 0;
+}
+
+/* A paged segment read out in slot order: slot i lives in row (i % page_size)
+ * of page page_table[i / page_size] of the pool. */
+int orc_paged_rows(const void* pool, int64_t row_bytes, const int32_t* page_table,
+                   int page_size, int64_t n, void* dst) {
+    if (row_bytes <= 0 || page_size <= 0 || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t page = page_table[i / page_size];
+        const int64_t row = page * page_size + i % page_size;
+        memcpy((char*)dst + i * row_bytes, (const char*)pool + row * row_bytes, (size_t)row_bytes);
+    }
+    return 0;
+}
+
+/*
+ * Single-query decode attention over a (pruned) cache for the G query heads
+ * that share one KV head: out_h = sum_i softmax_i(scale * q_h . k_i) v_i.
+ * The pages describe decode as re-attending to the whole cache for every new
+ * token ([ZN] 长推理的内存困境); this is that textbook softmax attention.
+ * q: [G][d] stored; K, V: [N][d] stored; out: [G][d] (fp64).
+ */
+int orc_decode_attn(const void* q, int q_dtype, const void* K, const void* V, int kv_dtype,
+                    int64_t N, int d, int G, double scale, double* out) {
+    if (d <= 0 || G <= 0 || N <= 0) return -1;
+    double* logit = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!logit) return -1;
+    for (int h = 0; h < G; ++h) {
+        double mx = -INFINITY;
+        for (int64_t i = 0; i < N; ++i) {
+            double dot = 0.0;
+            for (int e = 0; e < d; ++e)
+                dot += stored_value(q, q_dtype, (int64_t)h * d + e) * stored_value(K, kv_dtype, i * d + e);
+            logit[i] = scale * dot;
+            if (logit[i] > mx) mx = logit[i];
+        }
+        double den = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            logit[i] = exp(logit[i] - mx);
+            den += logit[i];
+        }
+        for (int e = 0; e < d; ++e) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < N; ++i) acc += logit[i] * stored_value(V, kv_dtype, i * d + e);
+            out[(int64_t)h * d + e] = acc / den;
+        }
+    }
+    free(logit);
+    return 0;
+}

@@ -1,0 +1,241 @@
+"""Pins for the oracle: checks against what the pages and the mathematics fix,
+never against the oracle itself.
+
+* A hand-derived worked example (tests/golden/hand_example.json).
+* Closed form at full concentration (R = 1): the score is then the exact
+  RoPE logit of the centre query at t + o, averaged over offsets, computed
+  here by rotating the centre vector (not by un-rotating the key).
+* Invariants: offset averaging is linear, relative-position (shift)
+  invariance, monotonicity in R, zero key scores zero.
+* z-score / max against numpy's mean/std/max; invariance to per-head affine
+  maps; G = 1.
+* Top-B against a brute-force rank count on tiny inputs with ties.
+* Gather, paged read-out and decode attention against numpy / torch.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _tiny(**kw):
+    return W.CONFIGS["tiny"].replace(**kw)
+
+
+def _segment(cfg, n=None, seed=0):
+    """A small fp32/bf16 segment from the synthetic key model (CPU)."""
+    cfg = cfg.replace(seed=seed, n_keys=n or cfg.n_keys)
+    c = W.dense_cache(cfg, "cpu")
+    cal = W.calibration(cfg)
+    K = W.to_stored_numpy(c["k"][0])
+    V = W.to_stored_numpy(c["v"][0])
+    pos = c["pos"][0].numpy()
+    G = cfg.group
+    return cfg, K, V, pos, int(c["t"][0]), cal["mag"][0, :G].numpy(), cal["phase"][0, :G].numpy(), \
+        cal["conc"][0, :G].numpy()
+
+
+def _as_float(K):
+    if K.dtype == np.uint16:
+        return (K.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return K.astype(np.float64)
+
+
+def _rope_rotate(vec, p, theta):
+    """Textbook RoPE (rotate-half pairing) of a real d-vector at position p."""
+    d = vec.shape[-1]
+    F = d // 2
+    w = theta ** (-2.0 * np.arange(F) / d)
+    c, s = np.cos(w * p), np.sin(w * p)
+    x1, x2 = vec[..., :F], vec[..., F:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)
+
+
+# ---------------------------------------------------------------- worked example
+def test_hand_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    env = {"cos": math.cos, "sin": math.sin, "pi": math.pi}
+    rows = np.array([[eval(e, env) for e in r] for r in ex["rows_expr"]], dtype=np.float32)
+    expect = np.array([[eval(e, env) for e in r] for r in ex["expected_expr"]])
+    S = oracle.score_segment(rows, np.array(ex["positions"]), ex["t"], ex["theta"],
+                             np.array(ex["mag"]), np.array(ex["phase"]), np.array(ex["conc"]),
+                             ex["offsets"])
+    np.testing.assert_allclose(S, expect, rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------- closed form at R = 1
+@pytest.mark.parametrize("dtype,d,theta", [(torch.float32, 64, 1e4), (torch.bfloat16, 128, 1e6),
+                                           (torch.bfloat16, 64, 150000.0)])
+def test_full_concentration_equals_rope_logit(dtype, d, theta):
+    cfg, K, _, pos, t, M, phi, _ = _segment(_tiny(dtype=dtype, head_dim=d, theta=theta), n=48)
+    R = np.ones_like(M)
+    offs = [1, 2, 4, 8, 16, 1024, 32768]
+    S = oracle.score_segment(K, pos, t, theta, M, phi, R, offs)
+    M64, phi64 = M.astype(np.float64), phi.astype(np.float64)
+    centre = np.concatenate([M64 * np.cos(phi64), M64 * np.sin(phi64)], axis=-1)      # [G][d]
+    Kf = _as_float(K)
+    expect = np.zeros_like(S)
+    for o in offs:
+        q = _rope_rotate(centre.astype(np.float64), t + o, theta)           # [G][d]
+        expect += q @ Kf.T
+    expect /= len(offs)
+    scale = np.abs(expect).max()
+    np.testing.assert_allclose(S, expect, rtol=0, atol=1e-10 * scale)
+
+
+def test_single_offset_is_plain_rope_logit_at_large_positions():
+    # Positions near 65536 with w0 = 1: the oracle's fp64 phase must hold there.
+    cfg = _tiny(head_dim=128, theta=1e6, dtype=torch.float32)
+    rng = np.random.default_rng(3)
+    N, d, F, G = 16, 128, 64, 2
+    pos = rng.integers(60000, 65536, size=N).astype(np.int32)
+    pre = rng.normal(size=(N, d))
+    K = np.stack([_rope_rotate(pre[i], pos[i], cfg.theta) for i in range(N)]).astype(np.float32)
+    M = rng.uniform(0.5, 2, size=(G, F)).astype(np.float32)
+    phi = rng.uniform(0, 2 * np.pi, size=(G, F)).astype(np.float32)
+    t, o = 65536, 65536
+    S = oracle.score_segment(K, pos, t, cfg.theta, M, phi, np.ones_like(M), [o])
+    M64, phi64 = M.astype(np.float64), phi.astype(np.float64)
+    centre = np.concatenate([M64 * np.cos(phi64), M64 * np.sin(phi64)], axis=-1)
+    expect = _rope_rotate(centre, t + o, cfg.theta) @ K.astype(np.float64).T
+    np.testing.assert_allclose(S, expect, rtol=0, atol=1e-9 * np.abs(expect).max())
+
+
+# ---------------------------------------------------------------- invariants
+def test_offset_average_is_linear():
+    cfg, K, _, pos, t, M, phi, R = _segment(_tiny(), n=40)
+    offs = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]
+    S = oracle.score_segment(K, pos, t, cfg.theta, M, phi, R, offs)
+    singles = [oracle.score_segment(K, pos, t, cfg.theta, M, phi, R, [o]) for o in offs]
+    np.testing.assert_allclose(S, np.mean(singles, axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_relative_position_shift_invariance():
+    """Keys re-rotated at p + s, queried at t + s: same scores (up to fp32 storage)."""
+    cfg = _tiny()
+    rng = np.random.default_rng(1)
+    N, d, G = 32, cfg.head_dim, cfg.group
+    F = d // 2
+    pre = torch.tensor(rng.normal(size=(N, d)))
+    p = torch.arange(N, dtype=torch.int64) * 7
+    cal = W.calibration(cfg)
+    M, phi, R = (cal[k][0].numpy() for k in ("mag", "phase", "conc"))
+    out = []
+    for s in (0, 12345):
+        re, im = W.rotate(pre[:, :F], pre[:, F:], p + s, cfg)
+        K = torch.cat([re, im], -1).to(torch.float32).numpy()
+        out.append(oracle.score_segment(K, (p + s).numpy().astype(np.int32), 5000 + s, cfg.theta,
+                                        M, phi, R, cfg.offsets))
+    np.testing.assert_allclose(out[0], out[1], rtol=0, atol=1e-5 * np.abs(out[0]).max())
+
+
+def test_norm_term_grows_as_concentration_falls_and_zero_key_scores_zero():
+    cfg, K, _, pos, t, M, phi, R = _segment(_tiny(), n=24)
+    S_hi = oracle.score_segment(K, pos, t, cfg.theta, M, phi, np.full_like(R, 0.875), cfg.offsets)
+    S_lo = oracle.score_segment(K, pos, t, cfg.theta, M, phi, np.full_like(R, 0.125), cfg.offsets)
+    S_mid = oracle.score_segment(K, pos, t, cfg.theta, M, phi, np.full_like(R, 0.5), cfg.offsets)
+    assert np.all(S_lo > S_hi)
+    # the weight is affine in R (midpoint of R gives the midpoint of scores)
+    np.testing.assert_allclose(S_mid, 0.5 * (S_hi + S_lo), rtol=1e-12, atol=1e-12)
+    Kz = np.zeros_like(K)
+    Sz = oracle.score_segment(Kz, pos, t, cfg.theta, M, phi, R, cfg.offsets)
+    assert np.all(Sz == 0.0)
+
+
+# ---------------------------------------------------------------- z-score and max
+def test_zscore_max_against_numpy():
+    rng = np.random.default_rng(2)
+    S = rng.normal(size=(4, 501)) * np.array([[3.0], [0.5], [10.0], [1.0]]) + np.array([[100.0], [-3], [0], [7]])
+    mu, sigma, A = oracle.zscore_max(S)
+    np.testing.assert_allclose(mu, S.mean(axis=1), rtol=1e-13)
+    np.testing.assert_allclose(sigma, S.std(axis=1, ddof=0), rtol=1e-12)
+    z = (S - S.mean(axis=1, keepdims=True)) / S.std(axis=1, keepdims=True)
+    np.testing.assert_allclose(A, z.max(axis=0), rtol=0, atol=1e-12)
+    # per-head positive affine maps leave the aggregate unchanged
+    S2 = S * np.array([[2.0], [0.1], [7.0], [1.0]]) + np.array([[5.0], [1.0], [-9.0], [0.0]])
+    np.testing.assert_allclose(oracle.zscore_max(S2)[2], A, rtol=0, atol=1e-10)
+    # one head: A is that head's z-score
+    np.testing.assert_allclose(oracle.zscore_max(S[:1])[2], z[0], rtol=0, atol=1e-12)
+
+
+def test_zscore_constant_head_gives_zero():
+    S = np.vstack([np.full(10, 3.25), np.arange(10.0)])
+    mu, sigma, A = oracle.zscore_max(S)
+    assert sigma[0] == 0.0 and mu[0] == 3.25
+    z1 = (np.arange(10.0) - 4.5) / np.arange(10.0).std()
+    np.testing.assert_allclose(A, np.maximum(z1, 0.0), atol=1e-12)
+
+
+# ---------------------------------------------------------------- selection
+@pytest.mark.parametrize("seed", range(12))
+def test_select_matches_brute_force_rank(seed):
+    rng = np.random.default_rng(seed)
+    N = int(rng.integers(1, 65))
+    B = int(rng.integers(1, N + 4))
+    A = rng.integers(-3, 4, size=N).astype(np.float64) * 0.5     # many ties
+    if seed % 3 == 0:
+        A = rng.normal(size=N)
+    idx = oracle.select_topb(A, B)
+    kept = [i for i in range(N)
+            if sum(1 for j in range(N) if A[j] > A[i] or (A[j] == A[i] and j < i)) < B]
+    assert list(idx) == kept
+    assert len(idx) == min(N, B)
+
+
+def test_select_f32_signed_zero_and_budget_at_least_n():
+    A = np.array([0.0, -0.0, 1.0, -0.0, 0.0], dtype=np.float32)
+    assert list(oracle.select_topb(A, 3)) == [0, 1, 2]
+    assert list(oracle.select_topb(np.array([3.0, 1.0, 2.0]), 3)) == [0, 1, 2]
+    assert list(oracle.select_topb(np.array([3.0, 1.0, 2.0]), 10)) == [0, 1, 2]
+    assert len(oracle.select_topb(np.zeros(0), 4)) == 0
+
+
+# ---------------------------------------------------------------- data movement
+def test_gather_and_paged_rows_are_byte_copies():
+    rng = np.random.default_rng(4)
+    src = rng.integers(0, 2 ** 16, size=(50, 8), dtype=np.uint16)
+    idx = np.array([0, 3, 4, 17, 49], dtype=np.int32)
+    assert np.array_equal(oracle.gather_rows(src, idx), src[idx])
+    pool = rng.integers(0, 2 ** 16, size=(7, 4, 8), dtype=np.uint16)
+    pt = np.array([5, 0, 3], dtype=np.int32)
+    rows = oracle.paged_rows(pool, pt, 4, 10)
+    assert np.array_equal(rows, pool[pt].reshape(12, 8)[:10])
+
+
+# ---------------------------------------------------------------- decode attention
+def test_decode_attention_against_torch_sdpa():
+    rng = np.random.default_rng(5)
+    G, d, N = 8, 64, 77
+    q = torch.tensor(rng.normal(size=(G, d)), dtype=torch.float32).to(torch.bfloat16)
+    K = torch.tensor(rng.normal(size=(N, d)), dtype=torch.float32).to(torch.bfloat16)
+    V = torch.tensor(rng.normal(size=(N, d)), dtype=torch.float32).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    out = oracle.decode_attn(W.to_stored_numpy(q), W.to_stored_numpy(K), W.to_stored_numpy(V), scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.double()[None, :, None, :], K.double()[None, None].expand(1, G, N, d),
+        V.double()[None, None].expand(1, G, N, d), scale=scale)[0, :, 0]
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+    # equal logits: the output is the mean of V
+    out0 = oracle.decode_attn(np.zeros((G, d), np.float32), K.float().numpy(), V.float().numpy(), 1.0)
+    np.testing.assert_allclose(out0, np.broadcast_to(V.double().mean(0).numpy(), (G, d)), atol=1e-12)
+
+
+# ---------------------------------------------------------------- whole chain
+def test_prune_chain_tiny_shapes_and_budget_cases():
+    cfg, K, V, pos, t, M, phi, R = _segment(_tiny(), n=300)
+    r = oracle.prune_segment(K, V, pos, t, cfg.theta, M, phi, R, cfg.offsets, 100)
+    assert r["idx"].shape == (100,) and np.all(np.diff(r["idx"]) > 0)
+    assert np.array_equal(r["K"], K[r["idx"]]) and np.array_equal(r["pos"], pos[r["idx"]])
+    # the kept keys are exactly the 100 largest aggregated scores
+    thr = np.sort(r["A"])[-100]
+    assert np.all(r["A"][r["idx"]] >= thr)
+    r2 = oracle.prune_segment(K, V, pos, t, cfg.theta, M, phi, R, cfg.offsets, 300)
+    assert np.array_equal(r2["idx"], np.arange(300)) and np.array_equal(r2["V"], V)
