@@ -1,0 +1,201 @@
+"""Benchmark of the TriAttention pruning pass on one MI355X.
+
+A step is one tri_prune_window call over the whole synthetic cache (score every
+key, z-score/max per GQA group, select the top-B per KV head, compact K/V and
+positions into a second cache).  Default workload: a Qwen3-8B-shaped full-model
+cache, 36 layers x 16 sequences x 8 KV heads x 32768 keys, head_dim 128, bf16,
+GQA 4, B = 2048, 16 geometric offsets.  Inputs are generated on the GPU before
+timing and stay resident in HBM.
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded by
+the library on the launch stream over the timed steps (tri_timing_*).
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "keys scored+pruned/sec (G keys/s) and % of HBM roofline, 32K cache, B=2048"
+HBM_PEAK_GBS = 8000.0
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "long_reasoning_decode_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(n_keys_total, n_seg, n_kept_total, d, es):
+    """Bytes the method must move: every key read once for scoring, kept K and
+    V rows read and written, kept positions read and written."""
+    score = n_keys_total * d * es
+    gather = n_kept_total * (4 * d * es + 8)
+    return score, gather
+
+
+def cpu_baseline(W, cfg, g, cal, B, n_sample):
+    import numpy as np
+
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1, n_sample))
+    per_l = cfg.n_seq * cfg.n_kv_heads
+    segs = [int(s) for s in np.linspace(0, cfg.n_seg - 1, n_sample).round()]
+    data = {s: (W.to_stored_numpy(g["k"][s]), W.to_stored_numpy(g["v"][s]), g["pos"][s].cpu().numpy())
+            for s in segs}
+    t = int(g["t"][0])
+    G = cfg.group
+
+    def one(s):
+        l, h = s // per_l, s % cfg.n_kv_heads
+        sl = slice(h * G, (h + 1) * G)
+        K, V, P = data[s]
+        return oracle.prune_segment(K, V, P, t, cfg.theta, cal["mag"][l, sl].numpy(), cal["phase"][l, sl].numpy(),
+                                    cal["conc"][l, sl].numpy(), cfg.offsets, B)
+
+    t0 = time.perf_counter()
+    oracle.run_parallel(one, segs, threads=threads)
+    dt = time.perf_counter() - t0
+    keys = len(segs) * cfg.n_keys
+    return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(segs)} whole segments ({cfg.n_keys} keys each, full prune chain) spread over "
+                      f"layers/sequences/heads; {dt:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l"])
+    ap.add_argument("--cpu-sample", type=int, default=8, help="oracle segments for the CPU baseline (0: skip)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); the pruning "
+              "path has no cross-GPU step and this build runs on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from long_reasoning_decode_amd import triattn as T
+
+    T.load()
+    torch.cuda.set_device(0)
+    cfg = W.CONFIGS[args.workload]
+    B = cfg.budget
+    t_gen = time.perf_counter()
+    g = W.dense_cache(cfg, "cuda")
+    cal = W.calibration(cfg)
+    calib = T.tri_calib_load(cal["mag"], cal["phase"], cal["conc"], cal["offsets"], n_kv_heads=cfg.n_kv_heads,
+                             rope_theta=cfg.theta)
+    src = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=cfg.n_layers, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads)
+    out = {"k": torch.empty((cfg.n_seg, B, cfg.head_dim), dtype=cfg.dtype, device="cuda"),
+           "pos": torch.empty((cfg.n_seg, B), dtype=torch.int32, device="cuda"),
+           "lengths": torch.zeros((cfg.n_seg,), dtype=torch.int32, device="cuda")}
+    out["v"] = torch.empty_like(out["k"])
+    dst = T.cache_desc(out["k"], out["v"], out["pos"], out["lengths"], n_layers=cfg.n_layers, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads)
+    ws = T.workspace(calib, src, B)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"# inputs ready in {t_gen:.1f} s: {cfg.n_seg} segments x {cfg.n_keys} keys", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        T.tri_prune_window(calib, src, g["t"], B, dst, out["lengths"], ws, stream=stream)
+    torch.cuda.synchronize()
+    T.tri_timing_reset()
+    T.tri_timing_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        T.tri_prune_window(calib, src, g["t"], B, dst, out["lengths"], ws, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    T.tri_timing_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kt = T.tri_timing_read()
+    print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    n_keys = cfg.n_seg * cfg.n_keys
+    n_kept = int(out["lengths"].long().sum())
+    es = 2 if cfg.dtype == torch.bfloat16 else 4
+    b_score, b_gather = algorithmic_bytes(n_keys, cfg.n_seg, n_kept, cfg.head_dim, es)
+    kernels = {}
+    for name, bytes_per_launch in (("score", b_score), ("select_gather", b_gather)):
+        launches, total = kt.get(name, (0, 0.0))
+        if launches:
+            avg = total / launches
+            kernels[name] = {"avg_ms": round(avg, 4), "launches": launches,
+                             "algorithmic_bytes": bytes_per_launch,
+                             "achieved_GBs": round(bytes_per_launch / (avg * 1e-3) / 1e9, 1)}
+    for name in ("phase",):
+        launches, total = kt.get(name, (0, 0.0))
+        if launches:
+            kernels[name] = {"avg_ms": round(total / launches, 4), "launches": launches}
+    dom = max(("score", "select_gather"), key=lambda k: kernels.get(k, {}).get("avg_ms", 0.0))
+    achieved = kernels[dom]["achieved_GBs"]
+    traffic = read_traffic(dom, args.workload)
+    pass_gbs = (b_score + b_gather) / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(n_keys / (ms * 1e-3) / 1e9, 3),
+        "unit": "G keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: Qwen3-8B-shaped cache, {cfg.n_layers} layers x {cfg.n_seq} sequences x "
+                         f"{cfg.n_kv_heads} KV heads x {cfg.n_keys} keys, head_dim {cfg.head_dim}, GQA {cfg.group}, "
+                         f"B={B}, {len(cfg.offsets)} geometric offsets, one prune pass"),
+            "kv_dtype": "bf16" if es == 2 else "f32", "keys_per_step": n_keys, "kept_per_step": n_kept,
+        },
+        "pass_hbm": {"algorithmic_bytes": b_score + b_gather, "achieved_GBs": round(pass_gbs, 1),
+                     "frac_of_peak": round(pass_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "kernels": kernels,
+    }
+    if args.cpu_sample > 0:
+        result["cpu_baseline"] = cpu_baseline(W, cfg, g, cal, B, args.cpu_sample)
+    calib.free()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

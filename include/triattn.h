@@ -1,0 +1,205 @@
+/*
+ * triattn.h — C ABI of the MI355X (gfx950) TriAttention KV-cache pruning library.
+ *
+ * Method (web pages describing TriAttention; formulas there were lost, the
+ * prose is restated here):
+ *   [YY] yeyulingfeng.com, "实现单卡4090跑通OpenClaw!英伟达&浙大等提出长上下文推理KV
+ *        压缩新方法TriAttention", section 主要方法.
+ *   [ZN] zingnex.cn, "TriAttention：用三角级数压缩KV缓存，让长推理模型跑在消费级显卡上",
+ *        sections 预RoPE空间的发现 and TriAttention的核心机制：三角级数距离建模.
+ *
+ * Offline, each query head h of each layer gets per-band centre statistics:
+ * magnitude M[h][f], phase phi[h][f] and concentration R[h][f] (mean resultant
+ * length).  Online, every cached key is scored by
+ *     S_h = (1/|O|) sum_{o in O} sum_f M |k_f| cos(w_f (t + o - p) + phi - psi_f)
+ *         + sum_f (1 - R) M |k_f|
+ * (the centre query's RoPE logit at future positions t + o, averaged over a
+ * geometric offset set, plus a norm term that grows where the band is not
+ * concentrated), z-scored inside each query head, max-aggregated over the GQA
+ * group, and when a segment holds more than B keys only the B best survive
+ * (ties to the earlier slot) and K/V/positions are compacted in slot order.
+ *
+ * Conventions shared by every entry point
+ *  - Rotary layout: half-split pairing.  Band f of a row x is x[f] + i x[f+F],
+ *    F = head_dim/2, frequency w_f = rope_theta^(-2f/head_dim).  The cache holds
+ *    post-RoPE keys.
+ *  - A segment is one (layer, sequence, KV head).  Segments are numbered
+ *    s = (l * n_seq + b) * n_kv_heads + h; query heads h*G .. h*G+G-1 share it.
+ *  - Pointers marked "device" are device memory owned by the caller; pointers
+ *    marked "host" are host memory read during the call.  The library never
+ *    allocates per call; only tri_calib_load allocates (a small table it owns).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
+ *    Return codes report host-side validation and launch errors only; on any
+ *    error nothing is launched and outputs are untouched.
+ *  - Supported: head_dim 64 or 128, GQA group 1, 2, 4 or 8, bf16 or fp32
+ *    storage, segments of at most 65536 keys, budget at most 8192.
+ */
+#ifndef TRIATTN_H
+#define TRIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define TRI_OK 0
+#define TRI_ERR_INVALID_ARG (-1) /* malformed argument (null, negative, inconsistent shape) */
+#define TRI_ERR_UNSUPPORTED (-2) /* well-formed but outside the supported set above        */
+#define TRI_ERR_WORKSPACE (-3)   /* workspace missing or smaller than tri_workspace_size   */
+#define TRI_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed             */
+#define TRI_ERR_NO_DEVICE (-5)   /* no GPU visible to the process                          */
+
+/* ---- storage types and layouts ---- */
+#define TRI_DTYPE_F32 0
+#define TRI_DTYPE_BF16 1
+#define TRI_LAYOUT_DENSE 0
+#define TRI_LAYOUT_PAGED 1
+
+typedef void* tri_stream_t;                 /* hipStream_t */
+typedef struct tri_calib_s* tri_calib_t;    /* opaque calibration handle */
+
+/*
+ * A KV cache.  All pointers are device memory owned by the caller.
+ *  dense : k, v are [n_seg][capacity][head_dim] (row = head_dim elements),
+ *          pos is int32 [n_seg][capacity].
+ *  paged : k, v are a pool [n_pages][page_size][head_dim], pos is int32
+ *          [n_pages][page_size]; slot i of segment s lives in row i % page_size
+ *          of page page_table[s * max_pages + i / page_size].
+ *  lengths : int32 [n_seg], valid keys per segment (slots 0..lengths[s]-1).
+ *  layer0  : calibration layer of this cache's layer 0 (layer l uses
+ *            calibration layer layer0 + l).
+ */
+typedef struct tri_cache_desc {
+    int32_t dtype;        /* TRI_DTYPE_*                         */
+    int32_t layout;       /* TRI_LAYOUT_*                        */
+    int32_t n_layers;
+    int32_t layer0;
+    int32_t n_seq;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t capacity;     /* dense: slots per segment; paged: max_pages * page_size */
+    void* k;
+    void* v;
+    int32_t* pos;
+    int32_t* lengths;
+    int32_t page_size;    /* paged only */
+    int32_t max_pages;    /* paged only */
+    const int32_t* page_table; /* paged only: int32 [n_seg][max_pages] */
+} tri_cache_desc;
+
+/*
+ * Offline calibration -> device constants ([YY] 主要方法: centres, norms and
+ * concentration are gathered offline; the future offsets are a geometric set).
+ *   mag, phase, conc : host fp32 [n_layers][n_q_heads][head_dim/2]
+ *                      (M >= 0, phase in radians, 0 <= conc <= 1).
+ *   offsets          : host int32 [n_offsets], each >= 0.
+ * Folds the offset average into one complex coefficient per band in fp64
+ * (the average of e^{i w_f (t+o)} over o factors as e^{i w_f t} times a
+ * constant), and stores it with the weights (1 - R) M on the device.
+ * n_q_heads must be a multiple of n_kv_heads (group G = n_q_heads/n_kv_heads).
+ * *out receives a handle (freed with tri_calib_free).  Synchronous.
+ */
+int tri_calib_load(tri_calib_t* out, int n_layers, int n_q_heads, int n_kv_heads, int head_dim,
+                   double rope_theta, const float* mag, const float* phase, const float* conc,
+                   const int32_t* offsets, int n_offsets, tri_stream_t stream);
+
+/* Releases a handle (NULL is a no-op).  Waits for the device to be idle. */
+int tri_calib_free(tri_calib_t calib);
+
+/*
+ * Bytes of device workspace tri_score / tri_select_topb / tri_prune_window
+ * need for this cache and budget (host-only; no device call).
+ */
+int tri_workspace_size(tri_calib_t calib, const tri_cache_desc* kv, int budget, size_t* bytes);
+
+/*
+ * Key scores and GQA aggregation ([YY] 主要方法: two-part key score fused into
+ * one, averaged over future offsets; z-score inside each query head and max
+ * over the heads sharing a KV head).
+ *   t        : device int32 [n_seq], position of the next query of each sequence.
+ *   scores   : optional device fp32 [n_seg][G][capacity]: raw S_h per key.
+ *   agg      : device fp32 [n_seg][capacity]: A = max_h (S_h - mu_h) / sigma_h
+ *              (population statistics over the segment's valid keys; a head
+ *              with sigma = 0 contributes 0).  Slots >= lengths[s] untouched.
+ *   mu_sigma : optional device fp32 [n_seg][G][2]: (mu_h, sigma_h).
+ *   ws       : device workspace of tri_workspace_size bytes.
+ */
+int tri_score(tri_calib_t calib, const tri_cache_desc* kv, const int32_t* t, float* scores,
+              float* agg, float* mu_sigma, void* ws, size_t ws_bytes, tri_stream_t stream);
+
+/*
+ * Top-B selection per segment ([YY] 主要方法: keep only the top-B keys).
+ *   agg     : device fp32 [n_seg][capacity] aggregated scores.
+ *   lengths : device int32 [n_seg].
+ *   idx     : device int32 [n_seg][budget]; row s receives the kept slots in
+ *             ascending order: the budget largest scores, ties at the cut to
+ *             the lower slot (-0 and +0 are equal); all slots when
+ *             lengths[s] <= budget.
+ *   n_kept  : device int32 [n_seg], min(lengths[s], budget).
+ */
+int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int capacity, int budget,
+                    int32_t* idx, int32_t* n_kept, void* ws, size_t ws_bytes, tri_stream_t stream);
+
+/*
+ * Compaction: for each segment, dst slot j <- src slot idx[s][j] for
+ * j < n_kept[s] (K row, V row and position, bit-exact).  Out of place: dst
+ * must not share memory with src.  dst describes a cache with the same
+ * n_layers/n_seq/n_kv_heads/head_dim/dtype; its lengths are not written
+ * (n_kept holds them).  idx rows are budget apart.
+ */
+int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_kept, int budget,
+                const tri_cache_desc* dst, tri_stream_t stream);
+
+/*
+ * One pruning pass over every segment ([YY] 主要方法: windowed batch pruning
+ * every 128 generated tokens when the cache exceeds its budget): score,
+ * aggregate, select and compact in one call, the fused hot path.  Segments
+ * with lengths[s] <= budget are copied through unchanged, so dst is always a
+ * complete cache; n_kept (device int32 [n_seg]) gets min(lengths[s], budget).
+ */
+int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
+                     const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,
+                     tri_stream_t stream);
+
+/*
+ * Appends one token to every segment: row lengths[s] of segment s receives
+ * k_new[s], v_new[s] (device [n_seg][head_dim], cache dtype) and position
+ * pos_new[b] (device int32 [n_seq]); lengths[s] then grows by one.  A segment
+ * already at capacity is left unchanged (its length stays at capacity).
+ * Dense caches only.
+ */
+int tri_append(const tri_cache_desc* kv, const void* k_new, const void* v_new,
+               const int32_t* pos_new, tri_stream_t stream);
+
+/*
+ * Single-query decode attention over the current cache, for every layer,
+ * sequence and query head ([ZN] 长推理的内存困境: each decode step re-attends
+ * to the whole cache):  out = softmax(scale * q . K^T) V over the segment's
+ * valid keys.  q : device [n_layers][n_seq][n_q_heads][head_dim] (cache dtype);
+ * out : device fp32, same shape.  Dense caches only; lengths[s] >= 1.
+ */
+int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, float scale, float* out,
+                    tri_stream_t stream);
+
+/* Static description of a status code. */
+const char* tri_strerror(int code);
+
+/*
+ * Kernel timing (instrumentation).  When enabled, every kernel launched by
+ * the library is bracketed by HIP events on its stream; tri_timing_read
+ * synchronises those events and returns, for kernel id `which` (0-based, see
+ * tri_timing_name), the number of launches and their summed duration in ms
+ * since the last reset.  Returns TRI_ERR_INVALID_ARG past the last id.
+ */
+int tri_timing_enable(int enable);
+int tri_timing_reset(void);
+int tri_timing_read(int which, int64_t* launches, double* total_ms);
+const char* tri_timing_name(int which);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRIATTN_H */

@@ -1,0 +1,517 @@
+// C ABI of the TriAttention pruning library: argument validation, the
+// calibration handle, workspace planning, kernel dispatch and the optional
+// kernel timing.  Declarations and contracts: include/triattn.h.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "../../include/triattn.h"
+#include "launch.h"
+
+using namespace tri;
+
+struct tri_calib_s {
+    int L, Hq, Hkv, G, D, F, n_off;
+    double theta;
+    void* dev;         // one device allocation holding the three tables below
+    double2* P;        // [L][Hq][F]  M e^{i phi} * mean_o e^{i w_f o}
+    float* wnorm;      // [L][Hq][F]  (1 - R) M
+    double* omega;     // [F]
+};
+
+namespace {
+
+constexpr int kMaxLen = 65536;
+constexpr int kMaxBudget = 8192;
+constexpr int kMinChunk = 512;
+
+// ---------------------------------------------------------------- timing
+struct PendingTiming {
+    int id;
+    hipEvent_t start, stop;
+};
+std::mutex g_tmu;
+bool g_timing = false;
+std::vector<PendingTiming> g_pending;
+int64_t g_launches[KID_COUNT] = {};
+double g_ms[KID_COUNT] = {};
+const char* kKernelNames[KID_COUNT] = {"phase",  "score",  "zmax",   "select",
+                                       "select_gather", "gather", "append", "decode_attn"};
+
+void drain_timing_locked() {
+    for (auto& p : g_pending) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(p.stop) == hipSuccess && hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+            g_ms[p.id] += ms;
+            g_launches[p.id] += 1;
+        }
+        (void)hipEventDestroy(p.start);
+        (void)hipEventDestroy(p.stop);
+    }
+    g_pending.clear();
+}
+
+// ---------------------------------------------------------------- helpers
+int device_present() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return 1;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int elem_size(int dtype) { return dtype == TRI_DTYPE_BF16 ? 2 : 4; }
+
+int64_t n_segments(const tri_cache_desc* kv) {
+    return (int64_t)kv->n_layers * kv->n_seq * kv->n_kv_heads;
+}
+
+// Validates the shape and pointers of a cache descriptor.
+int check_cache(const tri_cache_desc* kv) {
+    if (!kv) return TRI_ERR_INVALID_ARG;
+    if (kv->dtype != TRI_DTYPE_F32 && kv->dtype != TRI_DTYPE_BF16) return TRI_ERR_INVALID_ARG;
+    if (kv->layout != TRI_LAYOUT_DENSE && kv->layout != TRI_LAYOUT_PAGED) return TRI_ERR_INVALID_ARG;
+    if (kv->n_layers < 1 || kv->layer0 < 0 || kv->n_seq < 1 || kv->n_kv_heads < 1) return TRI_ERR_INVALID_ARG;
+    if (kv->head_dim <= 0 || (kv->head_dim & 1) || kv->capacity < 1) return TRI_ERR_INVALID_ARG;
+    if (!kv->k || !kv->v || !kv->pos || !kv->lengths) return TRI_ERR_INVALID_ARG;
+    if (kv->layout == TRI_LAYOUT_PAGED) {
+        if (kv->page_size < 1 || kv->max_pages < 1 || !kv->page_table) return TRI_ERR_INVALID_ARG;
+        if ((int64_t)kv->page_size * kv->max_pages != kv->capacity) return TRI_ERR_INVALID_ARG;
+    }
+    if (n_segments(kv) > (int64_t)0x7fffffff) return TRI_ERR_UNSUPPORTED;
+    if (kv->head_dim != 64 && kv->head_dim != 128) return TRI_ERR_UNSUPPORTED;
+    return TRI_OK;
+}
+
+int check_calib_vs_cache(const tri_calib_s* c, const tri_cache_desc* kv) {
+    if (!c) return TRI_ERR_INVALID_ARG;
+    if (kv->head_dim != c->D || kv->n_kv_heads != c->Hkv) return TRI_ERR_INVALID_ARG;
+    if ((int64_t)kv->layer0 + kv->n_layers > c->L) return TRI_ERR_INVALID_ARG;
+    return TRI_OK;
+}
+
+CacheView view_of(const tri_cache_desc* kv) {
+    CacheView v;
+    v.k = static_cast<const uint8_t*>(kv->k);
+    v.v = static_cast<const uint8_t*>(kv->v);
+    v.pos = kv->pos;
+    v.page_table = kv->layout == TRI_LAYOUT_PAGED ? kv->page_table : nullptr;
+    v.capacity = kv->capacity;
+    v.page_size = kv->layout == TRI_LAYOUT_PAGED ? kv->page_size : 0;
+    v.max_pages = kv->layout == TRI_LAYOUT_PAGED ? kv->max_pages : 0;
+    v.row_bytes = kv->head_dim * elem_size(kv->dtype);
+    return v;
+}
+
+CacheOut out_of(const tri_cache_desc* kv) {
+    CacheOut o;
+    o.k = static_cast<uint8_t*>(kv->k);
+    o.v = static_cast<uint8_t*>(kv->v);
+    o.pos = kv->pos;
+    o.page_table = kv->layout == TRI_LAYOUT_PAGED ? kv->page_table : nullptr;
+    o.capacity = kv->capacity;
+    o.page_size = kv->layout == TRI_LAYOUT_PAGED ? kv->page_size : 0;
+    o.max_pages = kv->layout == TRI_LAYOUT_PAGED ? kv->max_pages : 0;
+    return o;
+}
+
+SegShape shape_of(const tri_cache_desc* kv) {
+    SegShape s;
+    s.n_seq = kv->n_seq;
+    s.n_kv_heads = kv->n_kv_heads;
+    return s;
+}
+
+// Keys per scoring workgroup: 2048 when that still gives >= 2048 workgroups,
+// else smaller (down to 512) so small caches spread over the chip.
+int pick_chunk(int64_t n_seg, int64_t cap) {
+    int chunk = 2048;
+    while (chunk > kMinChunk && n_seg * ((cap + chunk - 1) / chunk) < 2048) chunk >>= 1;
+    return chunk;
+}
+
+struct WsPlan {
+    size_t ctab, stats, s_int, total;
+};
+
+WsPlan plan_workspace(const tri_calib_s* c, const tri_cache_desc* kv) {
+    const int64_t n_seg = n_segments(kv);
+    const int64_t max_chunks = (kv->capacity + kMinChunk - 1) / kMinChunk;
+    WsPlan p;
+    p.ctab = 0;
+    p.stats = align256((size_t)kv->n_layers * kv->n_seq * c->Hq * c->D * sizeof(float));
+    p.s_int = p.stats + align256((size_t)n_seg * max_chunks * c->G * sizeof(double2));
+    p.total = p.s_int + align256((size_t)n_seg * kv->capacity * c->G * sizeof(float));
+    return p;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TRI_OK : TRI_ERR_HIP; }
+
+// phase + score shared by tri_score and tri_prune_window.
+int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const int32_t* t, float* s_raw,
+                        float* s_int, double2* stats, float* ctab, int chunk, hipStream_t st) {
+    PhaseArgs pa;
+    pa.P = c->P;
+    pa.omega = c->omega;
+    pa.t = t;
+    pa.ctab = ctab;
+    pa.layer0 = kv->layer0;
+    pa.n_layers = kv->n_layers;
+    pa.n_seq = kv->n_seq;
+    pa.n_q_heads = c->Hq;
+    pa.head_dim = c->D;
+    int rc = hip_status(launch_phase(pa, st));
+    if (rc) return rc;
+
+    ScoreArgs sa;
+    sa.kv = view_of(kv);
+    sa.shape = shape_of(kv);
+    sa.lengths = kv->lengths;
+    sa.ctab = ctab;
+    sa.wtab = c->wnorm + (int64_t)kv->layer0 * c->Hq * c->F;
+    sa.s_raw = s_raw;
+    sa.s_int = s_int;
+    sa.stats = stats;
+    sa.cap = kv->capacity;
+    sa.n_q_heads = c->Hq;
+    sa.chunk = chunk;
+    sa.n_chunks = (int)((kv->capacity + chunk - 1) / chunk);
+    sa.n_seg = (int)n_segments(kv);
+    return hip_status(launch_score(sa, c->D, c->G, kv->dtype == TRI_DTYPE_BF16, st));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- timing hooks
+namespace tri {
+TimedLaunch::TimedLaunch(int id_, hipStream_t s) : id(id_), stream(s) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (!g_timing) return;
+    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess) {
+        start = stop = nullptr;
+        return;
+    }
+    (void)hipEventRecord(start, stream);
+}
+TimedLaunch::~TimedLaunch() {
+    if (!start) return;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    (void)hipEventRecord(stop, stream);
+    g_pending.push_back({id, start, stop});
+}
+}  // namespace tri
+
+extern "C" {
+
+const char* tri_strerror(int code) {
+    switch (code) {
+        case TRI_OK: return "ok";
+        case TRI_ERR_INVALID_ARG: return "invalid argument";
+        case TRI_ERR_UNSUPPORTED: return "unsupported shape or type";
+        case TRI_ERR_WORKSPACE: return "workspace missing or too small";
+        case TRI_ERR_HIP: return "HIP runtime or launch error";
+        case TRI_ERR_NO_DEVICE: return "no GPU device";
+        default: return "unknown status";
+    }
+}
+
+int tri_calib_load(tri_calib_t* out, int n_layers, int n_q_heads, int n_kv_heads, int head_dim,
+                   double rope_theta, const float* mag, const float* phase, const float* conc,
+                   const int32_t* offsets, int n_offsets, tri_stream_t stream) {
+    if (!out || n_layers < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim <= 0 || (head_dim & 1))
+        return TRI_ERR_INVALID_ARG;
+    if (n_q_heads % n_kv_heads) return TRI_ERR_INVALID_ARG;
+    if (!(rope_theta > 0.0) || !isfinite(rope_theta)) return TRI_ERR_INVALID_ARG;
+    if (!mag || !phase || !conc || !offsets || n_offsets < 1) return TRI_ERR_INVALID_ARG;
+    const int F = head_dim / 2;
+    const int64_t n = (int64_t)n_layers * n_q_heads * F;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!isfinite(mag[i]) || mag[i] < 0.0f || !isfinite(phase[i])) return TRI_ERR_INVALID_ARG;
+        if (!(conc[i] >= 0.0f && conc[i] <= 1.0f)) return TRI_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < n_offsets; ++i)
+        if (offsets[i] < 0) return TRI_ERR_INVALID_ARG;
+    const int G = n_q_heads / n_kv_heads;
+    if ((head_dim != 64 && head_dim != 128) || !supported_group(G)) return TRI_ERR_UNSUPPORTED;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+
+    // Host-side fp64 folding of the offset average into one coefficient per band.
+    std::vector<double> omega(F);
+    std::vector<double2> A(F);
+    for (int f = 0; f < F; ++f) {
+        omega[f] = pow(rope_theta, -2.0 * (double)f / (double)head_dim);
+        double re = 0.0, im = 0.0;
+        for (int o = 0; o < n_offsets; ++o) {
+            re += cos(omega[f] * (double)offsets[o]);
+            im += sin(omega[f] * (double)offsets[o]);
+        }
+        A[f] = make_double2(re / n_offsets, im / n_offsets);
+    }
+    std::vector<double2> P((size_t)n);
+    std::vector<float> wn((size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+        const int f = (int)(i % F);
+        const double cr = (double)mag[i] * cos((double)phase[i]);
+        const double ci = (double)mag[i] * sin((double)phase[i]);
+        P[i] = make_double2(cr * A[f].x - ci * A[f].y, cr * A[f].y + ci * A[f].x);
+        wn[i] = (float)((1.0 - (double)conc[i]) * (double)mag[i]);
+    }
+
+    tri_calib_s* c = new (std::nothrow) tri_calib_s();
+    if (!c) return TRI_ERR_INVALID_ARG;
+    const size_t bP = align256(sizeof(double2) * (size_t)n);
+    const size_t bW = align256(sizeof(float) * (size_t)n);
+    const size_t bO = align256(sizeof(double) * (size_t)F);
+    if (hipMalloc(&c->dev, bP + bW + bO) != hipSuccess) {
+        delete c;
+        return TRI_ERR_HIP;
+    }
+    c->P = static_cast<double2*>(c->dev);
+    c->wnorm = reinterpret_cast<float*>(static_cast<char*>(c->dev) + bP);
+    c->omega = reinterpret_cast<double*>(static_cast<char*>(c->dev) + bP + bW);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(c->P, P.data(), sizeof(double2) * n, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->wnorm, wn.data(), sizeof(float) * n, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(c->omega, omega.data(), sizeof(double) * F, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        (void)hipFree(c->dev);
+        delete c;
+        return TRI_ERR_HIP;
+    }
+    c->L = n_layers;
+    c->Hq = n_q_heads;
+    c->Hkv = n_kv_heads;
+    c->G = G;
+    c->D = head_dim;
+    c->F = F;
+    c->n_off = n_offsets;
+    c->theta = rope_theta;
+    *out = c;
+    return TRI_OK;
+}
+
+int tri_calib_free(tri_calib_t calib) {
+    if (!calib) return TRI_OK;
+    int rc = TRI_OK;
+    if (hipDeviceSynchronize() != hipSuccess) rc = TRI_ERR_HIP;
+    if (hipFree(calib->dev) != hipSuccess) rc = TRI_ERR_HIP;
+    delete calib;
+    return rc;
+}
+
+int tri_workspace_size(tri_calib_t calib, const tri_cache_desc* kv, int budget, size_t* bytes) {
+    if (!bytes || !calib) return TRI_ERR_INVALID_ARG;
+    int rc = check_cache(kv);
+    if (rc) return rc;
+    if ((rc = check_calib_vs_cache(calib, kv))) return rc;
+    if (budget < 1) return TRI_ERR_INVALID_ARG;
+    *bytes = plan_workspace(calib, kv).total;
+    return TRI_OK;
+}
+
+int tri_score(tri_calib_t calib, const tri_cache_desc* kv, const int32_t* t, float* scores, float* agg,
+              float* mu_sigma, void* ws, size_t ws_bytes, tri_stream_t stream) {
+    int rc = check_cache(kv);
+    if (rc) return rc;
+    if ((rc = check_calib_vs_cache(calib, kv))) return rc;
+    if (!t || !agg) return TRI_ERR_INVALID_ARG;
+    if (kv->capacity > kMaxLen) return TRI_ERR_UNSUPPORTED;
+    const WsPlan p = plan_workspace(calib, kv);
+    if (!ws || ws_bytes < p.total) return TRI_ERR_WORKSPACE;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    float* ctab = reinterpret_cast<float*>(w + p.ctab);
+    double2* stats = reinterpret_cast<double2*>(w + p.stats);
+    float* s_int = scores ? nullptr : reinterpret_cast<float*>(w + p.s_int);
+    const int chunk = pick_chunk(n_segments(kv), kv->capacity);
+    if ((rc = run_phase_and_score(calib, kv, t, scores, s_int, stats, ctab, chunk, st))) return rc;
+    ZmaxArgs za;
+    za.s_raw = scores;
+    za.s_int = s_int;
+    za.stats = stats;
+    za.lengths = kv->lengths;
+    za.agg = agg;
+    za.mu_sigma = mu_sigma;
+    za.cap = kv->capacity;
+    za.chunk = chunk;
+    za.n_chunks = (int)((kv->capacity + chunk - 1) / chunk);
+    za.n_seg = (int)n_segments(kv);
+    return hip_status(launch_zmax(za, calib->G, st));
+}
+
+int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int capacity, int budget,
+                    int32_t* idx, int32_t* n_kept, void* ws, size_t ws_bytes, tri_stream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!agg || !lengths || !idx || n_seg < 0 || capacity < 1 || budget < 1) return TRI_ERR_INVALID_ARG;
+    if (capacity > kMaxLen || budget > kMaxBudget) return TRI_ERR_UNSUPPORTED;
+    if (n_seg == 0) return TRI_OK;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+    SelectArgs a;
+    memset(&a, 0, sizeof a);
+    a.agg = agg;
+    a.agg_stride = capacity;
+    a.lengths = lengths;
+    a.budget = budget;
+    a.idx_out = idx;
+    a.idx_stride = budget;
+    a.n_kept = n_kept;
+    a.gather = 0;
+    a.n_seg = n_seg;
+    a.cap = capacity;
+    return hip_status(launch_select(a, 0, capacity, static_cast<hipStream_t>(stream)));
+}
+
+static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int budget) {
+    int rc = check_cache(src);
+    if (rc) return rc;
+    if ((rc = check_cache(dst))) return rc;
+    if (src->dtype != dst->dtype || src->head_dim != dst->head_dim || src->n_layers != dst->n_layers ||
+        src->n_seq != dst->n_seq || src->n_kv_heads != dst->n_kv_heads)
+        return TRI_ERR_INVALID_ARG;
+    if (budget < 1) return TRI_ERR_INVALID_ARG;
+    if (dst->capacity < budget) return TRI_ERR_INVALID_ARG;
+    if (dst->k == src->k || dst->v == src->v || dst->pos == src->pos || dst->k == src->v || dst->v == src->k)
+        return TRI_ERR_INVALID_ARG;
+    if (budget > kMaxBudget) return TRI_ERR_UNSUPPORTED;
+    return TRI_OK;
+}
+
+int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_kept, int budget,
+                const tri_cache_desc* dst, tri_stream_t stream) {
+    int rc = check_pair(src, dst, budget);
+    if (rc) return rc;
+    if (!idx || !n_kept) return TRI_ERR_INVALID_ARG;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+    GatherArgs a;
+    a.src = view_of(src);
+    a.dst = out_of(dst);
+    a.idx = idx;
+    a.idx_stride = budget;
+    a.n_kept = n_kept;
+    a.row_bytes = src->head_dim * elem_size(src->dtype);
+    a.rows_per_block = 64;
+    a.blocks_per_seg = (budget + 63) / 64;
+    a.n_seg = (int)n_segments(src);
+    return hip_status(launch_gather(a, static_cast<hipStream_t>(stream)));
+}
+
+int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
+                     const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,
+                     tri_stream_t stream) {
+    int rc = check_pair(src, dst, budget);
+    if (rc) return rc;
+    if ((rc = check_calib_vs_cache(calib, src))) return rc;
+    if (!t || !n_kept) return TRI_ERR_INVALID_ARG;
+    if (src->capacity > kMaxLen) return TRI_ERR_UNSUPPORTED;
+    const WsPlan p = plan_workspace(calib, src);
+    if (!ws || ws_bytes < p.total) return TRI_ERR_WORKSPACE;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* w = static_cast<char*>(ws);
+    float* ctab = reinterpret_cast<float*>(w + p.ctab);
+    double2* stats = reinterpret_cast<double2*>(w + p.stats);
+    float* s_int = reinterpret_cast<float*>(w + p.s_int);
+    const int chunk = pick_chunk(n_segments(src), src->capacity);
+    if ((rc = run_phase_and_score(calib, src, t, nullptr, s_int, stats, ctab, chunk, st))) return rc;
+    SelectArgs a;
+    memset(&a, 0, sizeof a);
+    a.s_int = s_int;
+    a.stats = stats;
+    a.chunk = chunk;
+    a.n_chunks = (int)((src->capacity + chunk - 1) / chunk);
+    a.cap = src->capacity;
+    a.lengths = src->lengths;
+    a.budget = budget;
+    a.n_kept = n_kept;
+    a.gather = 1;
+    a.src = view_of(src);
+    a.dst = out_of(dst);
+    a.row_bytes = src->head_dim * elem_size(src->dtype);
+    a.n_seg = (int)n_segments(src);
+    return hip_status(launch_select(a, calib->G, src->capacity, st));
+}
+
+int tri_append(const tri_cache_desc* kv, const void* k_new, const void* v_new, const int32_t* pos_new,
+               tri_stream_t stream) {
+    int rc = check_cache(kv);
+    if (rc) return rc;
+    if (!k_new || !v_new || !pos_new) return TRI_ERR_INVALID_ARG;
+    if (kv->layout != TRI_LAYOUT_DENSE) return TRI_ERR_UNSUPPORTED;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+    AppendArgs a;
+    a.kv = out_of(kv);
+    a.lengths = kv->lengths;
+    a.k_new = static_cast<const uint8_t*>(k_new);
+    a.v_new = static_cast<const uint8_t*>(v_new);
+    a.pos_new = pos_new;
+    a.shape = shape_of(kv);
+    a.row_bytes = kv->head_dim * elem_size(kv->dtype);
+    a.n_seg = (int)n_segments(kv);
+    return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, float scale, float* out,
+                    tri_stream_t stream) {
+    int rc = check_cache(kv);
+    if (rc) return rc;
+    if (!q || !out || n_q_heads < 1 || n_q_heads % kv->n_kv_heads || !isfinite(scale)) return TRI_ERR_INVALID_ARG;
+    if (kv->layout != TRI_LAYOUT_DENSE) return TRI_ERR_UNSUPPORTED;
+    const int G = n_q_heads / kv->n_kv_heads;
+    if (!supported_group(G)) return TRI_ERR_UNSUPPORTED;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+    AttnArgs a;
+    a.kv = view_of(kv);
+    a.shape = shape_of(kv);
+    a.lengths = kv->lengths;
+    a.q = static_cast<const uint8_t*>(q);
+    a.out = out;
+    a.scale = scale;
+    a.n_q_heads = n_q_heads;
+    a.n_seg = (int)n_segments(kv);
+    return hip_status(launch_decode_attn(a, kv->head_dim, G, kv->dtype == TRI_DTYPE_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int tri_timing_enable(int enable) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing = enable != 0;
+    return TRI_OK;
+}
+
+int tri_timing_reset(void) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    drain_timing_locked();
+    for (int i = 0; i < KID_COUNT; ++i) {
+        g_ms[i] = 0.0;
+        g_launches[i] = 0;
+    }
+    return TRI_OK;
+}
+
+int tri_timing_read(int which, int64_t* launches, double* total_ms) {
+    if (which < 0 || which >= KID_COUNT || !launches || !total_ms) return TRI_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_tmu);
+    drain_timing_locked();
+    *launches = g_launches[which];
+    *total_ms = g_ms[which];
+    return TRI_OK;
+}
+
+const char* tri_timing_name(int which) {
+    if (which < 0 || which >= KID_COUNT) return nullptr;
+    return kKernelNames[which];
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Shared device helpers and launch-argument records for the TriAttention
+// pruning kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tri {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- stored elements
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element e of a 16-byte chunk holding E stored values (E = 8 bf16 or 4 fp32).
+template <bool BF16>
+__device__ __forceinline__ float chunk_elem(const uint4& c, int e) {
+    const uint32_t w = e < (BF16 ? 2 : 1) ? c.x : e < (BF16 ? 4 : 2) ? c.y : e < (BF16 ? 6 : 3) ? c.z : c.w;
+    if (BF16) return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    return __uint_as_float(w);
+}
+
+// Orderable 32-bit key of an fp32 score: larger score <=> larger key.
+// -0 is folded onto +0 so the two compare equal (IEEE comparison semantics).
+__device__ __forceinline__ uint32_t order_key(float a) {
+    uint32_t u = __float_as_uint(a);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- cache addressing
+// Where slot n of segment s lives, as a row index into k/v (rows of head_dim
+// elements) and pos (one int32 per row).
+struct CacheView {
+    const uint8_t* k;
+    const uint8_t* v;
+    const int32_t* pos;
+    const int32_t* page_table;   // paged only
+    int64_t capacity;            // dense: rows per segment
+    int32_t page_size;           // paged only (>0 means paged)
+    int32_t max_pages;
+    int32_t row_bytes;           // head_dim * element size
+
+    __device__ __forceinline__ int64_t row(int64_t s, int64_t n) const {
+        if (page_size > 0) {
+            const int64_t page = page_table[s * max_pages + n / page_size];
+            return page * page_size + n % page_size;
+        }
+        return s * capacity + n;
+    }
+};
+
+struct CacheOut {
+    uint8_t* k;
+    uint8_t* v;
+    int32_t* pos;
+    const int32_t* page_table;
+    int64_t capacity;
+    int32_t page_size;
+    int32_t max_pages;
+
+    __device__ __forceinline__ int64_t row(int64_t s, int64_t n) const {
+        if (page_size > 0) {
+            const int64_t page = page_table[s * max_pages + n / page_size];
+            return page * page_size + n % page_size;
+        }
+        return s * capacity + n;
+    }
+};
+
+// Segment s -> (layer, sequence, kv head) for s = (l * n_seq + b) * Hkv + h.
+struct SegShape {
+    int32_t n_seq;
+    int32_t n_kv_heads;
+    __device__ __forceinline__ int layer(int s) const { return s / (n_seq * n_kv_heads); }
+    __device__ __forceinline__ int seq(int s) const { return (s / n_kv_heads) % n_seq; }
+    __device__ __forceinline__ int head(int s) const { return s % n_kv_heads; }
+};
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+    return x;
+}
+__device__ __forceinline__ float wave_sumf(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+
+// Inclusive prefix sum of a uint32 across the wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+}  // namespace tri

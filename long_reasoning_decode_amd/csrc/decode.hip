@@ -1,0 +1,201 @@
+// Decode-loop kernels for gfx950: appending a generated token to every
+// segment, and single-query decode attention over the (pruned) cache.
+//
+// Between two pruning passes the cache grows by one token per step and every
+// step re-attends to the whole cache (zingnex.cn TriAttention page, section
+// 长推理的内存困境); the attention here is plain softmax(scale q.K^T) V per
+// query head, over the keys the pruning kept plus those appended since.
+#include "launch.h"
+
+namespace tri {
+
+// ------------------------------------------------------------------ append
+__global__ __launch_bounds__(64) void k_append(AppendArgs a) {
+    const int s = blockIdx.x;
+    const int n = a.lengths[s];
+    __syncthreads();                               // every lane has read the length
+    if (n < 0 || n >= a.kv.capacity) return;       // full (or corrupt) segment: unchanged
+    const int64_t r = a.kv.row(s, n);
+    const int cpr = a.row_bytes >> 4;
+    for (int q = threadIdx.x; q < cpr; q += 64) {
+        reinterpret_cast<uint4*>(a.kv.k + r * a.row_bytes)[q] =
+            reinterpret_cast<const uint4*>(a.k_new + (int64_t)s * a.row_bytes)[q];
+        reinterpret_cast<uint4*>(a.kv.v + r * a.row_bytes)[q] =
+            reinterpret_cast<const uint4*>(a.v_new + (int64_t)s * a.row_bytes)[q];
+    }
+    if (threadIdx.x == 0) {
+        a.kv.pos[r] = a.pos_new[a.shape.seq(s)];
+        a.lengths[s] = n + 1;
+    }
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+    if (a.n_seg == 0) return hipSuccess;
+    TimedLaunch tl(KID_APPEND, stream);
+    hipLaunchKernelGGL(k_append, dim3((unsigned)a.n_seg), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ decode attention
+// One 256-thread workgroup per segment (the G query heads sharing one KV head).
+// Each wave walks 64-key tiles with an online softmax:
+//  * logits: lane = key; the key row is held in registers and the G query
+//    vectors are wave-uniform (scalar operands of the FMAs);
+//  * probabilities go through a per-wave LDS tile;
+//  * P.V: lane = output dimension (D/64 dims per lane), broadcast LDS reads of
+//    four probabilities at a time.
+// The four waves' (max, sum, partial output) are merged at the end.
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(256) void k_decode_attn(AttnArgs a) {
+    constexpr int E = BF16 ? 8 : 4;     // elements per 16-byte chunk
+    constexpr int NC = D / E;           // chunks per row
+    constexpr int DPL = D / kWave;      // output dims per lane
+    constexpr int ES = BF16 ? 2 : 4;
+    constexpr float kLog2e = 1.4426950408889634f;
+    __shared__ float4 ptile[4][G][kWave / 4];
+    __shared__ float wm[4][G], wl[4][G];
+    __shared__ float wo[4][G][D];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int s = blockIdx.x;
+    const int N = min(max(a.lengths[s], 0), (int)a.kv.capacity);
+    const int l = a.shape.layer(s), b = a.shape.seq(s), h = a.shape.head(s);
+    const uint8_t* qb = a.q + (((int64_t)l * a.shape.n_seq + b) * a.n_q_heads + (int64_t)h * G) * D * ES;
+    const float sl2 = a.scale * kLog2e;
+
+    float m[G], lsum[G], o[G][DPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -__builtin_inff();
+        lsum[g] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) o[g][d] = 0.0f;
+    }
+
+    for (int t0 = w * kWave; t0 < N; t0 += 4 * kWave) {
+        const int n = t0 + lane;
+        const bool valid = n < N;
+        float lg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) lg[g] = 0.0f;
+        if (valid) {
+            const uint4* row = reinterpret_cast<const uint4*>(a.kv.k + a.kv.row(s, n) * (D * ES));
+            uint4 kc[NC];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) kc[q] = row[q];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                float kf[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) kf[e] = chunk_elem<BF16>(kc[q], e);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const uint4 qc = reinterpret_cast<const uint4*>(qb + (int64_t)g * D * ES)[q];
+                    float acc = lg[g];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc = fmaf(chunk_elem<BF16>(qc, e), kf[e], acc);
+                    lg[g] = acc;
+                }
+            }
+        }
+        // online softmax update (base 2); the tile's first key is valid, so the
+        // new running maximum is finite
+        float* pt = reinterpret_cast<float*>(&ptile[w][0][0]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float x = valid ? lg[g] * sl2 : -__builtin_inff();
+            const float mn = fmaxf(m[g], wave_max(x));
+            const float alpha = __builtin_amdgcn_exp2f(m[g] - mn);
+            const float p = valid ? __builtin_amdgcn_exp2f(x - mn) : 0.0f;
+            lsum[g] = lsum[g] * alpha + wave_sumf(p);
+            m[g] = mn;
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) o[g][d] *= alpha;
+            pt[g * kWave + lane] = p;
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int cnt = min(kWave, N - t0);
+        for (int i4 = 0; i4 < cnt; i4 += 4) {
+            float4 p4[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) p4[g] = ptile[w][g][i4 >> 2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (i4 + u < cnt) {
+                    const uint8_t* vrow = a.kv.v + a.kv.row(s, t0 + i4 + u) * (D * ES);
+#pragma unroll
+                    for (int d = 0; d < DPL; ++d) {
+                        const int dim = lane + d * kWave;
+                        float v;
+                        if (BF16) v = bf16_lo((uint32_t)reinterpret_cast<const uint16_t*>(vrow)[dim]);
+                        else v = reinterpret_cast<const float*>(vrow)[dim];
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            const float pg = u == 0 ? p4[g].x : u == 1 ? p4[g].y : u == 2 ? p4[g].z : p4[g].w;
+                            o[g][d] = fmaf(pg, v, o[g][d]);
+                        }
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // merge the four waves
+    if (lane == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            wm[w][g] = m[g];
+            wl[w][g] = lsum[g];
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) wo[w][g][lane + d * kWave] = o[g][d];
+    __syncthreads();
+    float* out = a.out + (((int64_t)l * a.shape.n_seq + b) * a.n_q_heads + (int64_t)h * G) * D;
+    for (int i = tid; i < G * D; i += 256) {
+        const int g = i / D, d = i - g * D;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, wm[v][g]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float sc = wl[v][g] > 0.0f ? __builtin_amdgcn_exp2f(wm[v][g] - M) : 0.0f;
+            num = fmaf(wo[v][g][d], sc, num);
+            den = fmaf(wl[v][g], sc, den);
+        }
+        out[(int64_t)g * D + d] = den > 0.0f ? num / den : 0.0f;
+    }
+}
+
+template <int D, int G>
+static void attn_dtype(const AttnArgs& a, bool bf16, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_seg), block(256);
+    if (bf16) hipLaunchKernelGGL((k_decode_attn<D, G, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_decode_attn<D, G, false>), grid, block, 0, stream, a);
+}
+
+template <int D>
+static bool attn_group(const AttnArgs& a, int group, bool bf16, hipStream_t stream) {
+    switch (group) {
+        case 1: attn_dtype<D, 1>(a, bf16, stream); return true;
+        case 2: attn_dtype<D, 2>(a, bf16, stream); return true;
+        case 4: attn_dtype<D, 4>(a, bf16, stream); return true;
+        case 8: attn_dtype<D, 8>(a, bf16, stream); return true;
+        default: return false;
+    }
+}
+
+hipError_t launch_decode_attn(const AttnArgs& a, int head_dim, int group, bool bf16, hipStream_t stream) {
+    if (a.n_seg == 0) return hipSuccess;
+    TimedLaunch tl(KID_DECODE_ATTN, stream);
+    bool ok = head_dim == 64 ? attn_group<64>(a, group, bf16, stream)
+            : head_dim == 128 ? attn_group<128>(a, group, bf16, stream) : false;
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace tri

@@ -1,0 +1,260 @@
+// Top-B selection and compaction kernels for gfx950.
+//
+// Selection (yeyulingfeng.com TriAttention page, section 主要方法: when the cache
+// exceeds its budget, keep only the top-B keys): one 1024-thread workgroup per
+// segment holds the segment's aggregated scores in registers as order-preserving
+// 32-bit keys, finds the exact B-th largest key T with an MSB-first radix select
+// (11 + 11 + 10 bit digits, 2048-bin LDS histograms, one block scan per digit),
+// then keeps every key > T and the lowest-slot keys equal to T.  The kept slots
+// are emitted in ascending order from wave ballots plus one block scan over
+// (register index, wave) counts, so the result is identical run to run.
+//
+// In gather mode the same workgroup then copies the kept K/V rows and positions
+// (bit-exact, slot order) into the destination cache: the fused pruning pass.
+#include "launch.h"
+#include "stats.h"
+
+namespace tri {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kMaxBudget = 8192;
+
+// Inclusive scan of one uint32 per thread over the 1024-thread block.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t x, uint32_t* wsum) {
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    x = wave_incl_scan(x);
+    if (lane == kWave - 1) wsum[w] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int i = 0; i < w; ++i) before += wsum[i];
+    __syncthreads();
+    return x + before;
+}
+
+template <int J, int G>
+__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t wsum[kSelWaves];
+    __shared__ uint32_t pick[2];
+    __shared__ uint32_t cnt_gt[J * kSelWaves], cnt_eq[J * kSelWaves];
+    __shared__ int32_t kept[kMaxBudget];
+    __shared__ double scratch[(kSelWaves + 1) * (G > 0 ? G : 1)];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int s = blockIdx.x;
+    const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
+    const int B = a.budget;
+    const bool all = N <= B;
+
+    uint32_t key[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) key[j] = 0u;
+    uint32_t T = 0u;
+    int need = 0;
+
+    if (!all) {
+        if constexpr (G > 0) {
+            const ZParams<G> z = merge_stats<G, kSelThreads>(a.stats + (int64_t)s * a.n_chunks * G, a.n_chunks,
+                                                            a.chunk, N, scratch);
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int n = j * kSelThreads + tid;
+                if (n < N) {
+                    const float* p = a.s_int + ((int64_t)s * a.cap + n) * G;
+                    float S[G];
+                    if constexpr (G % 4 == 0) {
+#pragma unroll
+                        for (int g = 0; g < G; g += 4) {
+                            const float4 v = *reinterpret_cast<const float4*>(p + g);
+                            S[g] = v.x; S[g + 1] = v.y; S[g + 2] = v.z; S[g + 3] = v.w;
+                        }
+                    } else {
+#pragma unroll
+                        for (int g = 0; g < G; ++g) S[g] = p[g];
+                    }
+                    key[j] = order_key(aggregate<G>(S, z));
+                }
+                // keep the scheduler from hoisting every key's loads at once
+                if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int n = j * kSelThreads + tid;
+                if (n < N) key[j] = order_key(a.agg[(int64_t)s * a.agg_stride + n]);
+                if ((j & 15) == 15) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        // ---- radix select of the B-th largest key
+        uint32_t prefix = 0u, pmask = 0u;
+        need = B;
+#pragma unroll
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+            const uint32_t dmask = pass < 2 ? 0x7ffu : 0x3ffu;
+            hist[tid] = 0u;
+            hist[tid + kSelThreads] = 0u;
+            if (tid == 0) {
+                pick[0] = 0u;
+                pick[1] = 0u;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int n = j * kSelThreads + tid;
+                if (n < N && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+            }
+            __syncthreads();
+            // Thread t owns bins 2047-2t and 2046-2t: a scan in thread order is a
+            // cumulative count from the top bin down.
+            const int b0 = 2047 - 2 * tid, b1 = b0 - 1;
+            const uint32_t h0 = hist[b0], h1 = hist[b1];
+            const uint32_t incl = block_incl_scan(h0 + h1, wsum);
+            const uint32_t above0 = incl - (h0 + h1);
+            const uint32_t above1 = above0 + h0;
+            const uint32_t un = (uint32_t)need;
+            if (above0 < un && above0 + h0 >= un) {
+                pick[0] = (uint32_t)b0;
+                pick[1] = above0;
+            } else if (above1 < un && above1 + h1 >= un) {
+                pick[0] = (uint32_t)b1;
+                pick[1] = above1;
+            }
+            __syncthreads();
+            prefix |= pick[0] << shift;
+            pmask |= dmask << shift;
+            need -= (int)pick[1];
+            __syncthreads();
+        }
+        T = prefix;
+    }
+
+    // ---- ordered emission: slot n = j*1024 + w*64 + lane, in (j, w, lane) order
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int n = j * kSelThreads + tid;
+        const bool valid = n < N;
+        const bool gt = valid && (all || key[j] > T);
+        const bool eq = valid && !all && key[j] == T;
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        if (lane == 0) {
+            cnt_gt[j * kSelWaves + w] = (uint32_t)__popcll(bg);
+            cnt_eq[j * kSelWaves + w] = (uint32_t)__popcll(be);
+        }
+    }
+    __syncthreads();
+    {
+        const uint32_t vg = tid < J * kSelWaves ? cnt_gt[tid] : 0u;
+        const uint32_t ve = tid < J * kSelWaves ? cnt_eq[tid] : 0u;
+        const uint32_t ig = block_incl_scan(vg, wsum);
+        const uint32_t ie = block_incl_scan(ve, wsum);
+        if (tid < J * kSelWaves) {
+            cnt_gt[tid] = ig - vg;
+            cnt_eq[tid] = ie - ve;
+        }
+    }
+    __syncthreads();
+    const int nk = min(N, B);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int n = j * kSelThreads + tid;
+        const bool valid = n < N;
+        const bool gt = valid && (all || key[j] > T);
+        const bool eq = valid && !all && key[j] == T;
+        const uint64_t bg = __ballot(gt), be = __ballot(eq);
+        const int eb = (int)cnt_eq[j * kSelWaves + w] + __popcll(be & below);
+        const int gb = (int)cnt_gt[j * kSelWaves + w] + __popcll(bg & below);
+        const int out = gb + min(eb, need);
+        if ((gt || (eq && eb < need)) && out < nk) {
+            if (a.gather) kept[out] = n;
+            else a.idx_out[(int64_t)s * a.idx_stride + out] = n;
+        }
+    }
+    if (a.n_kept && tid == 0) a.n_kept[s] = nk;
+    if (!a.gather) return;
+    __syncthreads();
+
+    // ---- compaction of the kept rows (16-byte copies), then positions
+    const int cpr = a.row_bytes >> 4;
+    const int lg = 31 - __clz(cpr);
+    const int total = nk * cpr;
+    for (int u = tid; u < total; u += kSelThreads) {
+        const int jrow = u >> lg, q = u & (cpr - 1);
+        const int64_t sr = a.src.row(s, kept[jrow]);
+        const int64_t dr = a.dst.row(s, jrow);
+        const uint4 kv = reinterpret_cast<const uint4*>(a.src.k + sr * a.row_bytes)[q];
+        const uint4 vv = reinterpret_cast<const uint4*>(a.src.v + sr * a.row_bytes)[q];
+        reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[q] = kv;
+        reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[q] = vv;
+    }
+    for (int jrow = tid; jrow < nk; jrow += kSelThreads)
+        a.dst.pos[a.dst.row(s, jrow)] = a.src.pos[a.src.row(s, kept[jrow])];
+}
+
+template <int J>
+static bool select_group(const SelectArgs& a, int group, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_seg), block(kSelThreads);
+    switch (group) {
+        case 0: hipLaunchKernelGGL((k_select<J, 0>), grid, block, 0, stream, a); return true;
+        case 1: hipLaunchKernelGGL((k_select<J, 1>), grid, block, 0, stream, a); return true;
+        case 2: hipLaunchKernelGGL((k_select<J, 2>), grid, block, 0, stream, a); return true;
+        case 4: hipLaunchKernelGGL((k_select<J, 4>), grid, block, 0, stream, a); return true;
+        case 8: hipLaunchKernelGGL((k_select<J, 8>), grid, block, 0, stream, a); return true;
+        default: return false;
+    }
+}
+
+hipError_t launch_select(const SelectArgs& a, int group, int64_t max_len, hipStream_t stream) {
+    if (a.n_seg == 0) return hipSuccess;
+    if (a.budget > kMaxBudget || max_len > 64 * kSelThreads) return hipErrorInvalidValue;
+    TimedLaunch tl(a.gather ? KID_SELECT_GATHER : KID_SELECT, stream);
+    bool ok;
+    if (max_len <= 2 * kSelThreads) ok = select_group<2>(a, group, stream);
+    else if (max_len <= 8 * kSelThreads) ok = select_group<8>(a, group, stream);
+    else if (max_len <= 32 * kSelThreads) ok = select_group<32>(a, group, stream);
+    else ok = select_group<64>(a, group, stream);
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ gather
+// Unfused compaction: workgroup (segment, block of rows) copies kept rows.
+__global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
+    const int s = blockIdx.x / a.blocks_per_seg;
+    const int rb = blockIdx.x - s * a.blocks_per_seg;
+    const int nk = min(max(a.n_kept[s], 0), (int)min(a.idx_stride, a.dst.capacity));
+    const int r0 = rb * a.rows_per_block;
+    if (r0 >= nk) return;
+    const int rows = min(a.rows_per_block, nk - r0);
+    const int cpr = a.row_bytes >> 4;
+    const int lg = 31 - __clz(cpr);
+    const int32_t* idx = a.idx + (int64_t)s * a.idx_stride + r0;
+    for (int u = threadIdx.x; u < rows * cpr; u += 256) {
+        const int jrow = u >> lg, q = u & (cpr - 1);
+        const int32_t i = idx[jrow];
+        if (i < 0 || i >= a.src.capacity) continue;      // out-of-range index: row skipped
+        const int64_t sr = a.src.row(s, i);
+        const int64_t dr = a.dst.row(s, r0 + jrow);
+        const uint4 kv = reinterpret_cast<const uint4*>(a.src.k + sr * a.row_bytes)[q];
+        const uint4 vv = reinterpret_cast<const uint4*>(a.src.v + sr * a.row_bytes)[q];
+        reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[q] = kv;
+        reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[q] = vv;
+    }
+    for (int jrow = threadIdx.x; jrow < rows; jrow += 256) {
+        const int32_t i = idx[jrow];
+        if (i >= 0 && i < a.src.capacity) a.dst.pos[a.dst.row(s, r0 + jrow)] = a.src.pos[a.src.row(s, i)];
+    }
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.n_seg * a.blocks_per_seg;
+    if (blocks == 0) return hipSuccess;
+    TimedLaunch tl(KID_GATHER, stream);
+    hipLaunchKernelGGL(k_gather, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace tri

@@ -1,0 +1,253 @@
+"""Thin Python binding of libtriattn.so (the C ABI in include/triattn.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the pruning path runs in the library's HIP kernels.
+The functions keep the C names.  Failures raise TriError with the library's
+status code; a missing library raises at load time (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtriattn.so")
+
+TRI_OK = 0
+TRI_ERR_INVALID_ARG = -1
+TRI_ERR_UNSUPPORTED = -2
+TRI_ERR_WORKSPACE = -3
+TRI_ERR_HIP = -4
+TRI_ERR_NO_DEVICE = -5
+TRI_DTYPE_F32 = 0
+TRI_DTYPE_BF16 = 1
+TRI_LAYOUT_DENSE = 0
+TRI_LAYOUT_PAGED = 1
+
+EXPORTS = (
+    "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
+    "tri_compact", "tri_prune_window", "tri_append", "tri_decode_attn", "tri_strerror",
+    "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name",
+)
+
+
+class TriError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        msg = _lib.tri_strerror(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{fn} failed: {msg} ({code})")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("layout", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+        ("layer0", ctypes.c_int32), ("n_seq", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+        ("lengths", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+        ("page_table", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load():
+    """Load the built library (no build here: build with long_reasoning_decode_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} missing "
+                           "(run python -m long_reasoning_decode_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, D, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float
+    SZ = ctypes.c_size_t
+    DP = ctypes.POINTER(CacheDesc)
+    sig = {
+        "tri_calib_load": [ctypes.POINTER(P), I, I, I, I, D, P, P, P, P, I, P],
+        "tri_calib_free": [P],
+        "tri_workspace_size": [P, DP, I, ctypes.POINTER(SZ)],
+        "tri_score": [P, DP, P, P, P, P, P, SZ, P],
+        "tri_select_topb": [P, P, I, I, I, P, P, P, SZ, P],
+        "tri_compact": [DP, P, P, I, DP, P],
+        "tri_prune_window": [P, DP, P, I, DP, P, P, SZ, P],
+        "tri_append": [DP, P, P, P, P],
+        "tri_decode_attn": [DP, I, P, F, P, P],
+        "tri_strerror": [I],
+        "tri_timing_enable": [I],
+        "tri_timing_reset": [],
+        "tri_timing_read": [I, ctypes.POINTER(I64), ctypes.POINTER(D)],
+        "tri_timing_name": [I],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name in ("tri_strerror", "tri_timing_name") else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn, rc):
+    if rc != TRI_OK:
+        raise TriError(fn, rc)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return TRI_DTYPE_BF16
+    if dt == torch.float32:
+        return TRI_DTYPE_F32
+    raise ValueError(f"unsupported cache dtype {dt}")
+
+
+def cache_desc(k, v, pos, lengths, *, n_layers, n_seq, n_kv_heads, layer0=0, page_table=None,
+               page_size=0, max_pages=0):
+    """Describe a cache held in torch tensors.  Dense: k/v [n_seg, capacity, d],
+    pos [n_seg, capacity]; paged: k/v [n_pages, page_size, d], pos [n_pages,
+    page_size] plus page_table [n_seg, max_pages]."""
+    for t in (k, v, pos, lengths) + ((page_table,) if page_table is not None else ()):
+        if not t.is_contiguous():
+            raise ValueError("cache tensors must be contiguous")
+    if pos.dtype != torch.int32 or lengths.dtype != torch.int32:
+        raise ValueError("positions and lengths are int32")
+    d = CacheDesc()
+    d.dtype = _dtype_code(k.dtype)
+    d.n_layers, d.layer0, d.n_seq, d.n_kv_heads = n_layers, layer0, n_seq, n_kv_heads
+    d.head_dim = k.shape[-1]
+    d.k, d.v, d.pos, d.lengths = k.data_ptr(), v.data_ptr(), pos.data_ptr(), lengths.data_ptr()
+    if page_table is None:
+        d.layout = TRI_LAYOUT_DENSE
+        d.capacity = k.shape[1]
+        d.page_size, d.max_pages, d.page_table = 0, 0, None
+    else:
+        if page_table.dtype != torch.int32:
+            raise ValueError("page table is int32")
+        d.layout = TRI_LAYOUT_PAGED
+        d.page_size, d.max_pages = page_size, max_pages
+        d.capacity = page_size * max_pages
+        d.page_table = page_table.data_ptr()
+    d._keep = (k, v, pos, lengths, page_table)     # keep the tensors alive with the record
+    return d
+
+
+class Calib:
+    """Owns a tri_calib_t."""
+
+    def __init__(self, handle, n_layers, n_q_heads, n_kv_heads, head_dim):
+        self.handle = handle
+        self.n_layers, self.n_q_heads, self.n_kv_heads, self.head_dim = n_layers, n_q_heads, n_kv_heads, head_dim
+        self.group = n_q_heads // n_kv_heads
+
+    def free(self):
+        if self.handle:
+            _check("tri_calib_free", load().tri_calib_free(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def tri_calib_load(mag, phase, conc, offsets, *, n_kv_heads, rope_theta, stream=None):
+    """mag/phase/conc: host fp32 [L, Hq, F]; offsets: host int32 [n_off]."""
+    lib = load()
+    mag = mag.detach().to("cpu", torch.float32).contiguous()
+    phase = phase.detach().to("cpu", torch.float32).contiguous()
+    conc = conc.detach().to("cpu", torch.float32).contiguous()
+    offsets = torch.as_tensor(offsets, dtype=torch.int32).contiguous()
+    L, Hq, F = mag.shape
+    h = ctypes.c_void_p()
+    rc = lib.tri_calib_load(ctypes.byref(h), L, Hq, n_kv_heads, 2 * F, float(rope_theta), _p(mag),
+                            _p(phase), _p(conc), _p(offsets), int(offsets.numel()), _stream(stream))
+    _check("tri_calib_load", rc)
+    return Calib(h, L, Hq, n_kv_heads, 2 * F)
+
+
+def tri_workspace_size(calib, desc, budget):
+    n = ctypes.c_size_t(0)
+    _check("tri_workspace_size", load().tri_workspace_size(calib.handle, ctypes.byref(desc), int(budget),
+                                                            ctypes.byref(n)))
+    return n.value
+
+
+def workspace(calib, desc, budget, device="cuda"):
+    return torch.empty(tri_workspace_size(calib, desc, budget), dtype=torch.uint8, device=device)
+
+
+def tri_score(calib, desc, t, agg, ws, scores=None, mu_sigma=None, stream=None):
+    rc = load().tri_score(calib.handle, ctypes.byref(desc), _p(t), _p(scores), _p(agg), _p(mu_sigma),
+                          _p(ws), ws.numel(), _stream(stream))
+    _check("tri_score", rc)
+
+
+def tri_select_topb(agg, lengths, budget, idx, n_kept=None, stream=None):
+    n_seg, cap = agg.shape
+    rc = load().tri_select_topb(_p(agg), _p(lengths), n_seg, cap, int(budget), _p(idx), _p(n_kept), None, 0,
+                                _stream(stream))
+    _check("tri_select_topb", rc)
+
+
+def tri_compact(src, idx, n_kept, budget, dst, stream=None):
+    rc = load().tri_compact(ctypes.byref(src), _p(idx), _p(n_kept), int(budget), ctypes.byref(dst),
+                            _stream(stream))
+    _check("tri_compact", rc)
+
+
+def tri_prune_window(calib, src, t, budget, dst, n_kept, ws, stream=None):
+    rc = load().tri_prune_window(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
+                                 _p(n_kept), _p(ws), ws.numel(), _stream(stream))
+    _check("tri_prune_window", rc)
+
+
+def tri_append(desc, k_new, v_new, pos_new, stream=None):
+    rc = load().tri_append(ctypes.byref(desc), _p(k_new), _p(v_new), _p(pos_new), _stream(stream))
+    _check("tri_append", rc)
+
+
+def tri_decode_attn(desc, n_q_heads, q, scale, out, stream=None):
+    rc = load().tri_decode_attn(ctypes.byref(desc), int(n_q_heads), _p(q), float(scale), _p(out),
+                                _stream(stream))
+    _check("tri_decode_attn", rc)
+
+
+def tri_strerror(code):
+    return load().tri_strerror(int(code)).decode()
+
+
+def tri_timing_enable(on=True):
+    _check("tri_timing_enable", load().tri_timing_enable(1 if on else 0))
+
+
+def tri_timing_reset():
+    _check("tri_timing_reset", load().tri_timing_reset())
+
+
+def tri_timing_read():
+    """{kernel name: (launches, total ms)} for every instrumented kernel."""
+    lib = load()
+    out = {}
+    i = 0
+    while True:
+        name = lib.tri_timing_name(i)
+        if name is None:
+            break
+        n = ctypes.c_int64(0)
+        ms = ctypes.c_double(0.0)
+        _check("tri_timing_read", lib.tri_timing_read(i, ctypes.byref(n), ctypes.byref(ms)))
+        out[name.decode()] = (n.value, ms.value)
+        i += 1
+    return out

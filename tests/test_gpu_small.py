@@ -1,0 +1,254 @@
+"""GPU parity at sizes the oracle finishes in seconds: every step of the HIP path
+(through the C ABI) against the oracle on the same seeded inputs, plus the edge
+cases (empty, single-key, under/at/over budget, ragged chunk tails, equal
+scores, every supported GQA group and head size, fp32 and bf16, paged)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import (calib_for, check_agg, check_compaction, check_mu_sigma, check_scores,
+                     check_selection, dense_desc, empty_like_dense, kept_slots_from_positions, log,
+                     oracle_segment, seg_calib, seg_seq, stored)
+
+pytestmark = pytest.mark.gpu
+
+
+def _to(cache, device):
+    return {k: (v.to(device) if torch.is_tensor(v) else v) for k, v in cache.items()}
+
+
+def _run_unfused(T, cfg, g, calib, B):
+    desc = dense_desc(T, cfg, g)
+    ws = T.workspace(calib, desc, B)
+    n_seg, cap = g["k"].shape[0], g["k"].shape[1]
+    G = cfg.group
+    scores = torch.full((n_seg, G, cap), float("nan"), device="cuda")
+    agg = torch.full((n_seg, cap), float("nan"), device="cuda")
+    ms = torch.zeros((n_seg, G, 2), device="cuda")
+    T.tri_score(calib, desc, g["t"], agg, ws, scores=scores, mu_sigma=ms)
+    idx = torch.full((n_seg, B), -1, dtype=torch.int32, device="cuda")
+    nk = torch.full((n_seg,), -1, dtype=torch.int32, device="cuda")
+    T.tri_select_topb(agg, g["lengths"], B, idx, nk)
+    out = empty_like_dense(g, B)
+    T.tri_compact(desc, idx, nk, B, dense_desc(T, cfg, out))
+    # the same cache through the fused entry point
+    out2 = empty_like_dense(g, B)
+    nk2 = torch.full((n_seg,), -1, dtype=torch.int32, device="cuda")
+    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out2), nk2, ws)
+    torch.cuda.synchronize()
+    return dict(scores=scores.cpu(), agg=agg.cpu(), ms=ms.cpu(), idx=idx.cpu(), nk=nk.cpu(), out=_to(out, "cpu"),
+                out2=_to(out2, "cpu"), nk2=nk2.cpu())
+
+
+def _check_all(cfg, cal, cpu, r, B, lengths, what):
+    """Oracle on every segment of a small dense cache, all steps."""
+    n_seg = cpu["k"].shape[0]
+    for s in range(n_seg):
+        N = int(lengths[s])
+        t = int(cpu["t"][seg_seq(cfg, s)])
+        tag = f"{what} seg {s} N={N}"
+        assert int(r["nk"][s]) == min(N, B) and int(r["nk2"][s]) == min(N, B), tag
+        if N == 0:
+            continue
+        K, V = stored(cpu["k"][s, :N]), stored(cpu["v"][s, :N])
+        P = cpu["pos"][s, :N].numpy()
+        ref = oracle_segment(cfg, cal, K, V, P, t, s, B)
+        check_scores(r["scores"][s, :, :N].numpy(), ref["S"], tag)
+        check_mu_sigma(r["ms"][s].numpy(), ref["mu"], ref["sigma"], tag)
+        check_agg(r["agg"][s, :N].numpy(), ref["A"], tag)
+        nk = min(N, B)
+        idx = r["idx"][s, :nk].numpy()
+        check_selection(idx, ref["A"], B, tag)
+        o = r["out"]
+        check_compaction(K, V, P, stored(o["k"][s, :nk]), stored(o["v"][s, :nk]), o["pos"][s, :nk].numpy(), idx, tag)
+        # fused pass: byte-identical to the unfused chain
+        o2 = r["out2"]
+        for key in ("k", "v", "pos"):
+            assert torch.equal(o2[key][s, :nk], o[key][s, :nk]), f"{tag}: fused {key} differs from unfused"
+
+
+def test_tiny_config_every_step(gpu_lib):
+    T = gpu_lib
+    cfg = W.CONFIGS["tiny"]
+    log(f"case tiny: N={cfg.n_keys} B={cfg.budget} d={cfg.head_dim} fp32")
+    cpu = W.dense_cache(cfg, "cpu")
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, cfg.budget)
+    _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "tiny")
+
+
+@pytest.mark.parametrize("d,G,dtype,theta", [
+    (128, 4, torch.bfloat16, 1e6), (64, 8, torch.bfloat16, 150000.0), (128, 1, torch.bfloat16, 1e6),
+    (64, 2, torch.float32, 1e4), (128, 8, torch.float32, 1e6), (64, 4, torch.bfloat16, 1e4)])
+def test_ragged_lengths_every_step(gpu_lib, d, G, dtype, theta):
+    """Segments of length 0, 1, B-1, B, B+1, chunk-straddling and full."""
+    T = gpu_lib
+    B = 200
+    cap = 2600
+    cfg = W.CONFIGS["tiny"].replace(head_dim=d, group=G, dtype=dtype, theta=theta, n_kv_heads=3, n_seq=3,
+                                    n_keys=cap, t=cap + 5, budget=B, sigma=None, seed=7)
+    log(f"case ragged d={d} G={G} {dtype}")
+    cpu = W.dense_cache(cfg, "cpu")
+    lengths = torch.tensor([0, 1, B - 1, B, B + 1, 513, 1024, 2047, cap], dtype=torch.int32)
+    cpu["lengths"] = lengths
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
+    _check_all(cfg, cal, cpu, r, B, lengths.numpy(), f"ragged d{d} G{G}")
+
+
+def test_equal_scores_keep_lowest_slots(gpu_lib):
+    """Identical keys: zero spread, z = 0 everywhere, the cut takes the lowest slots."""
+    T = gpu_lib
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, dtype=torch.bfloat16, theta=1e6, n_keys=3000, t=3000, budget=700)
+    log("case equal scores")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["k"][0, :] = cpu["k"][0, 5]
+    cpu["pos"][0, :] = 5            # same position too, so every score is bit-identical
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, cfg.budget)
+    assert torch.all(r["ms"][0, :, 1] == 0.0)
+    assert torch.all(r["agg"][0, :3000] == 0.0)
+    assert torch.equal(r["idx"][0], torch.arange(700, dtype=torch.int32))
+    _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "equal")
+
+
+@pytest.mark.parametrize("cap", [2048, 8192, 32768, 40000, 65536])
+def test_select_kernel_bit_exact(gpu_lib, cap):
+    """tri_select_topb on seeded score arrays (ties, signed zeros, all-equal)
+    equals the oracle's selection exactly."""
+    T = gpu_lib
+    n_seg = 8
+    A = W.synthetic_scores(n_seg, cap, seed=cap)
+    B = min(4096, cap // 3)
+    lengths = torch.tensor([cap, 0, 1, B, B + 1, cap - 1, cap // 2 + 7, cap], dtype=torch.int32)
+    log(f"case select cap={cap} B={B}")
+    idx = torch.full((n_seg, B), -1, dtype=torch.int32, device="cuda")
+    nk = torch.full((n_seg,), -1, dtype=torch.int32, device="cuda")
+    T.tri_select_topb(A.cuda(), lengths.cuda(), B, idx, nk)
+    torch.cuda.synchronize()
+    idx, nk = idx.cpu(), nk.cpu()
+    for s in range(n_seg):
+        N = int(lengths[s])
+        ref = oracle.select_topb(A[s, :N].numpy(), B)
+        assert int(nk[s]) == len(ref), f"seg {s}"
+        assert np.array_equal(idx[s, :len(ref)].numpy(), ref), f"cap {cap} seg {s} N {N}"
+
+
+def test_paged_small_every_step(gpu_lib):
+    T = gpu_lib
+    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=3)
+    log("case paged small")
+    pc = W.paged_cache(cfg, "cpu")
+    g = _to(pc, "cuda")
+    calib, cal = calib_for(T, cfg)
+    B, G, n_seg = cfg.budget, cfg.group, cfg.n_seg
+    src = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["page_table"], page_size=cfg.page_size,
+                       max_pages=g["max_pages"])
+    cap = cfg.page_size * g["max_pages"]
+    ws = T.workspace(calib, src, B)
+    scores = torch.zeros((n_seg, G, cap), device="cuda")
+    agg = torch.zeros((n_seg, cap), device="cuda")
+    ms = torch.zeros((n_seg, G, 2), device="cuda")
+    T.tri_score(calib, src, g["t"], agg, ws, scores=scores, mu_sigma=ms)
+    idx = torch.full((n_seg, B), -1, dtype=torch.int32, device="cuda")
+    nk = torch.zeros((n_seg,), dtype=torch.int32, device="cuda")
+    T.tri_select_topb(agg, g["lengths"], B, idx, nk)
+    dst = T.cache_desc(g["out_k"], g["out_v"], g["out_pos"], nk, n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["out_page_table"], page_size=cfg.page_size,
+                       max_pages=g["out_max_pages"])
+    T.tri_compact(src, idx, nk, B, dst)
+    torch.cuda.synchronize()
+    first = {k: g[k].clone() for k in ("out_k", "out_v", "out_pos")}
+    for k in ("out_k", "out_v", "out_pos"):
+        g[k].zero_()
+    nk2 = torch.zeros_like(nk)
+    dst2 = T.cache_desc(g["out_k"], g["out_v"], g["out_pos"], nk2, n_layers=1, n_seq=cfg.n_seq,
+                        n_kv_heads=cfg.n_kv_heads, page_table=g["out_page_table"], page_size=cfg.page_size,
+                        max_pages=g["out_max_pages"])
+    T.tri_prune_window(calib, src, g["t"], B, dst2, nk2, ws)
+    torch.cuda.synchronize()
+    for k in ("out_k", "out_v", "out_pos"):
+        assert torch.equal(g[k], first[k]), f"fused paged {k} differs from unfused"
+    lengths = pc["lengths"].numpy()
+    for s in range(n_seg):
+        N = int(lengths[s])
+        t = int(pc["t"][seg_seq(cfg, s)])
+        pt = pc["page_table"][s].numpy()
+        K = oracle.paged_rows(stored(pc["k"]), pt, cfg.page_size, N)
+        V = oracle.paged_rows(stored(pc["v"]), pt, cfg.page_size, N)
+        P = oracle.paged_rows(pc["pos"].numpy(), pt, cfg.page_size, N)
+        ref = oracle_segment(cfg, cal, K, V, P, t, s, B)
+        tag = f"paged seg {s} N={N}"
+        check_scores(scores[s, :, :N].cpu().numpy(), ref["S"], tag)
+        check_agg(agg[s, :N].cpu().numpy(), ref["A"], tag)
+        nks = min(N, B)
+        assert int(nk[s]) == nks
+        ix = idx[s, :nks].cpu().numpy()
+        check_selection(ix, ref["A"], B, tag)
+        opt = pc["out_page_table"][s].numpy()
+        Kd = oracle.paged_rows(stored(first["out_k"].cpu()), opt, cfg.page_size, nks)
+        Vd = oracle.paged_rows(stored(first["out_v"].cpu()), opt, cfg.page_size, nks)
+        Pd = oracle.paged_rows(first["out_pos"].cpu().numpy(), opt, cfg.page_size, nks)
+        check_compaction(K, V, P, Kd, Vd, Pd, ix, tag)
+
+
+def test_decode_loop_small(gpu_lib):
+    """Append + decode attention each step, prune after each window, on a
+    GPT-OSS-shaped but small cache."""
+    T = gpu_lib
+    cfg = W.CONFIGS["gptoss"].replace(n_layers=2, n_seq=3, budget=64, window=8, windows=2, start_pos_range=512)
+    log("case decode small")
+    st = _to(W.decode_start(cfg, "cpu"), "cuda")
+    km = W.key_model(cfg)
+    calib, cal = calib_for(T, cfg)
+    cap = st["capacity"]
+    caches = [st, {**empty_like_dense(st, cap), "t": st["t"]}]
+    cur = 0
+    t = cfg.start_pos_range
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    for w in range(cfg.windows):
+        for j in range(cfg.window):
+            c = caches[cur]
+            desc = dense_desc(T, cfg, c)
+            k_new, v_new, q = W.decode_token(cfg, km, w * cfg.window + j, t, "cpu")
+            pos_new = torch.full((cfg.n_seq,), t, dtype=torch.int32, device="cuda")
+            T.tri_append(desc, k_new.cuda(), v_new.cuda(), pos_new)
+            out = torch.zeros(q.shape, dtype=torch.float32, device="cuda")
+            T.tri_decode_attn(desc, cfg.n_q_heads, q.cuda(), scale, out)
+            torch.cuda.synchronize()
+            if j in (0, cfg.window - 1):
+                for s in range(cfg.n_seg):
+                    N = int(c["lengths"][s])
+                    l, b, h = s // (cfg.n_seq * cfg.n_kv_heads), seg_seq(cfg, s), s % cfg.n_kv_heads
+                    qs = q[l, b, h * cfg.group:(h + 1) * cfg.group]
+                    ref = oracle.decode_attn(stored(qs), stored(c["k"][s, :N].cpu()), stored(c["v"][s, :N].cpu()),
+                                             scale)
+                    got = out[l, b, h * cfg.group:(h + 1) * cfg.group].cpu().numpy()
+                    err = np.abs(got - ref) / np.maximum(np.abs(ref), np.abs(ref).max(axis=1, keepdims=True))
+                    assert err.max() <= 1e-4, f"attention w{w} step {j} seg {s}: {err.max():.2e}"
+            t += 1
+        c = caches[cur]
+        c["t"] = torch.full((cfg.n_seq,), t, dtype=torch.int32, device="cuda")
+        nxt = caches[1 - cur]
+        nk = nxt["lengths"]
+        desc = dense_desc(T, cfg, c)
+        ws = T.workspace(calib, desc, cfg.budget)
+        T.tri_prune_window(calib, desc, c["t"], cfg.budget, dense_desc(T, cfg, nxt), nk, ws)
+        torch.cuda.synchronize()
+        for s in range(cfg.n_seg):
+            N = int(c["lengths"][s])
+            K, V, P = stored(c["k"][s, :N].cpu()), stored(c["v"][s, :N].cpu()), c["pos"][s, :N].cpu().numpy()
+            ref = oracle_segment(cfg, cal, K, V, P, t, s, cfg.budget)
+            nks = int(nk[s])
+            assert nks == min(N, cfg.budget)
+            Pd = nxt["pos"][s, :nks].cpu().numpy()
+            ix = kept_slots_from_positions(P, Pd)
+            check_selection(ix, ref["A"], cfg.budget, f"decode window {w} seg {s}")
+            check_compaction(K, V, P, stored(nxt["k"][s, :nks].cpu()), stored(nxt["v"][s, :nks].cpu()), Pd, ix)
+        nxt["t"] = c["t"]
+        cur = 1 - cur

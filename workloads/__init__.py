@@ -140,14 +140,16 @@ def _pack(re, im, dtype):
     return torch.cat([re, im], dim=-1).to(dtype)
 
 
-def synth_keys(cfg: Config, km, layer: int, heads: torch.Tensor, positions: torch.Tensor, g,
-               device):
-    """Keys drawn from the centre + noise model for KV heads `heads` (broadcast
-    against positions [..., n]) -> stored rows [..., n, d]."""
+def synth_keys(cfg: Config, km, layer, heads, positions: torch.Tensor, g, device):
+    """Keys drawn from the centre + noise model.  `layer` and `heads` are ints or
+    index tensors broadcast against positions [..., n] (one entry per leading
+    index); returns stored rows [..., n, d]."""
     F = cfg.head_dim // 2
-    mag = km["mag"][layer].to(device)[heads]        # [..., F]
-    ph = km["phase"][layer].to(device)[heads]
-    sig = km["sigma"][layer].to(device)[heads]      # [...]
+    layer = torch.as_tensor(layer, device=device)
+    heads = torch.as_tensor(heads, device=device)
+    mag = km["mag"].to(device)[layer, heads]        # [..., F]
+    ph = km["phase"].to(device)[layer, heads]
+    sig = km["sigma"].to(device)[layer, heads]      # [...]
     shape = tuple(positions.shape) + (F,)
     n1 = torch.randn(shape, generator=g, device=device, dtype=torch.float64)
     n2 = torch.randn(shape, generator=g, device=device, dtype=torch.float64)
@@ -293,10 +295,9 @@ def decode_token(cfg: Config, km, step: int, t: int, device="cpu"):
     F = d // 2
     per_l = cfg.n_seq * cfg.n_kv_heads
     g = _gen(device, cfg.seed, 100000 + step)
-    heads = torch.arange(cfg.n_kv_heads, device=device).repeat(cfg.n_seq)
-    pos1 = torch.full((per_l, 1), t, device=device, dtype=torch.int64)
-    k_new = torch.cat([synth_keys(cfg, km, l, heads, pos1, g, device)[:, 0]
-                       for l in range(cfg.n_layers)], dim=0)
+    seg = torch.arange(cfg.n_seg, device=device)
+    pos1 = torch.full((cfg.n_seg, 1), t, device=device, dtype=torch.int64)
+    k_new = synth_keys(cfg, km, seg // per_l, seg % cfg.n_kv_heads, pos1, g, device)[:, 0]
     v_new = torch.randn((cfg.n_seg, d), generator=g, device=device,
                         dtype=torch.float32).to(cfg.dtype)
     cal = calibration(cfg)
@@ -320,3 +321,21 @@ def to_stored_numpy(x: torch.Tensor):
     if x.dtype == torch.float32:
         return x.numpy()
     raise TypeError(x.dtype)
+
+
+def synthetic_scores(n_seg: int, capacity: int, seed: int = 0):
+    """Aggregated-score arrays [n_seg][capacity] (fp32) for exercising top-B
+    selection on its own: per segment one of several value mixes - Gaussian,
+    heavily tied (few distinct levels), signed zeros, all equal."""
+    g = _gen("cpu", seed, 31)
+    A = torch.randn((n_seg, capacity), generator=g, dtype=torch.float32)
+    for s in range(n_seg):
+        kind = s % 4
+        if kind == 1:
+            A[s] = torch.randint(-3, 4, (capacity,), generator=g).float() * 0.25
+        elif kind == 2:
+            z = torch.randint(0, 3, (capacity,), generator=g)
+            A[s] = torch.where(z == 0, torch.tensor(-0.0), torch.where(z == 1, torch.tensor(0.0), A[s]))
+        elif kind == 3 and s % 8 == 3:
+            A[s] = 1.5
+    return A
