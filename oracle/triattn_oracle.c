@@ -131,9 +131,12 @@ int orc_zscore_max(const double* S, int G, int64_t N, double* mu, double* sigma,
     if (G <= 0 || N < 0) return -1;
     for (int h = 0; h < G; ++h) {
         const double* Sh = S + (int64_t)h * N;
+        /* mean = x0 + mean(x - x0): the same number, but a head whose scores are
+         * all equal gets that value back exactly, so its spread is exactly 0 */
+        const double x0 = N > 0 ? Sh[0] : 0.0;
         double sum = 0.0;
-        for (int64_t i = 0; i < N; ++i) sum += Sh[i];
-        const double m = N > 0 ? sum / (double)N : 0.0;
+        for (int64_t i = 0; i < N; ++i) sum += Sh[i] - x0;
+        const double m = N > 0 ? x0 + sum / (double)N : 0.0;
         double ss = 0.0;
         for (int64_t i = 0; i < N; ++i) ss += (Sh[i] - m) * (Sh[i] - m);
         mu[h] = m;
