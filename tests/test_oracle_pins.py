@@ -172,8 +172,8 @@ def test_zscore_constant_head_gives_zero():
     assert sigma[0] == 0.0 and mu[0] == 3.25
     # a value whose naive sum is inexact (0.1 * 3 != 0.3 in binary) still has zero spread
     for v, n in ((0.1, 3), (1.0 / 3.0, 3000), (123.456, 2047)):
-        mu, sigma, A = oracle.zscore_max(np.full((2, n), v))
-        assert np.all(sigma == 0.0) and np.all(mu == v) and np.all(A == 0.0)
+        mu_c, sigma_c, A_c = oracle.zscore_max(np.full((2, n), v))
+        assert np.all(sigma_c == 0.0) and np.all(mu_c == v) and np.all(A_c == 0.0)
     z1 = (np.arange(10.0) - 4.5) / np.arange(10.0).std()
     np.testing.assert_allclose(A, np.maximum(z1, 0.0), atol=1e-12)
 
