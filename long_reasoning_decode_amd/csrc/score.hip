@@ -180,6 +180,220 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ score (bf16, MFMA)
+// The same score as a skinny dense contraction on the matrix cores.  Per 16-key
+// tile, with k-steps of 32 along the row:
+//   S[key][col] += K[key][dims] . Bc[dims][col]        (trig: head_dim/32 steps)
+//   S[key][col] += |K|[key][bands] . Bw[bands][col]    (norm: F/32 steps, |K| as a
+//                                                       bf16 hi + lo pair)
+// Columns are (split q, head h): each fp32 coefficient is carried as the sum of
+// three bf16 values (hi, mid, lo), so the bf16 products keep fp32-level
+// accuracy; the three partial sums of a head are added afterwards.  The key
+// rows feed the A operand straight from HBM (16 rows x 64 contiguous bytes per
+// load); the coefficient fragments are loop-invariant registers.  |k_f| needs
+// the band's real and imaginary parts, which sit in the same lane and slot of
+// two A fragments (dims f and f + F), so the norm operand is built in registers.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Component q (0: hi, 1: mid, 2: lo) of the three-way bf16 split of x.
+__device__ __forceinline__ uint32_t bf16_split3(float x, int q) {
+    const uint32_t h = bf16_rne_bits(x);
+    if (q == 0) return h;
+    const float r1 = x - __uint_as_float(h << 16);
+    const uint32_t m = bf16_rne_bits(r1);
+    if (q == 1) return m;
+    return bf16_rne_bits(r1 - __uint_as_float(m << 16));
+}
+
+// Chan merge of (n, mean, M2) summaries.
+__device__ __forceinline__ void chan_merge(double& n, double& m, double& m2, double nb, double mb, double m2b) {
+    if (nb == 0.0) return;
+    if (n == 0.0) {
+        n = nb; m = mb; m2 = m2b;
+        return;
+    }
+    const double nt = n + nb, dl = mb - m;
+    m += dl * (nb / nt);
+    m2 += m2b + dl * dl * (n * nb / nt);
+    n = nt;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
+    constexpr int F = D / 2;
+    constexpr int TS = D / 32;               // trig k-steps = 16-byte A fragments per key
+    constexpr int NS = F / 32;               // norm k-steps
+    constexpr int NCOL = 3 * G;              // (split, head) columns
+    constexpr int NT = (NCOL + 15) / 16;     // 16-column MFMA tiles
+    constexpr int UT = 2;                    // 16-key tiles per wave iteration
+    constexpr int ROWB = D * 2;
+    __shared__ double part[4][G][3];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, grp = lane >> 4;
+    const int s = blockIdx.x / a.n_chunks;
+    const int c = blockIdx.x - s * a.n_chunks;
+    const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
+    const int start = c * a.chunk;
+    if (start >= N) return;
+    const int cnt = min(a.chunk, N - start);
+
+    // loop-invariant B fragments: column row -> (q, h), k-slot (grp, e)
+    bf16x8_t bt[TS][NT], bn[NS][NT];
+    {
+        const int l = a.shape.layer(s), b = a.shape.seq(s), hk = a.shape.head(s);
+        const float* cb = a.ctab + ((int64_t)(l * a.shape.n_seq + b) * a.n_q_heads + hk * G) * D;
+        const float* wb = a.wtab + ((int64_t)l * a.n_q_heads + hk * G) * F;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int jg = 16 * t + row;
+            const bool used = jg < NCOL;
+            const int q = jg / G, h = jg % G;
+#pragma unroll
+            for (int st = 0; st < TS; ++st) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int d0 = 32 * st + 8 * grp + 2 * e2;
+                    const uint32_t lo = used ? bf16_split3(cb[h * D + d0], q) : 0u;
+                    const uint32_t hi = used ? bf16_split3(cb[h * D + d0 + 1], q) : 0u;
+                    w[e2] = lo | (hi << 16);
+                }
+                bt[st][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+            }
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int f0 = 32 * st + 8 * grp + 2 * e2;
+                    const uint32_t lo = used ? bf16_split3(wb[h * F + f0], q) : 0u;
+                    const uint32_t hi = used ? bf16_split3(wb[h * F + f0 + 1], q) : 0u;
+                    w[e2] = lo | (hi << 16);
+                }
+                bn[st][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+            }
+        }
+    }
+
+    // per-lane running statistics for head `row` (lanes row < G), shifted by
+    // the lane's first score
+    float shift = 0.0f, sd = 0.0f, sd2 = 0.0f;
+    int cntl = 0;
+    const int n_tiles = (cnt + 15) / 16;
+    for (int tb = wave * UT; tb < n_tiles; tb += 4 * UT) {
+        uint4 av[UT][TS];
+#pragma unroll
+        for (int u = 0; u < UT; ++u) {
+            const int key = min((tb + u) * 16 + row, cnt - 1);     // clamped: tail rows re-read a valid row
+            const uint8_t* p = a.kv.k + a.kv.row(s, start + key) * ROWB + grp * 16;
+#pragma unroll
+            for (int st = 0; st < TS; ++st) av[u][st] = *reinterpret_cast<const uint4*>(p + st * 64);
+        }
+#pragma unroll
+        for (int u = 0; u < UT; ++u) {
+            if (tb + u >= n_tiles) break;
+            f32x4_t acc[NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < TS; ++st)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u][st]),
+                                                                     bt[st][t], acc[t], 0, 0, 0);
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const uint4 rv = av[u][st], iv = av[u][st + NS];
+                const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w}, iw[4] = {iv.x, iv.y, iv.z, iv.w};
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const float r0 = bf16_lo(rw[e2]), r1 = bf16_hi(rw[e2]);
+                    const float i0 = bf16_lo(iw[e2]), i1 = bf16_hi(iw[e2]);
+                    const float m0 = __builtin_amdgcn_sqrtf(fmaf(r0, r0, i0 * i0));
+                    const float m1 = __builtin_amdgcn_sqrtf(fmaf(r1, r1, i1 * i1));
+                    const bf16x2_t hp = __builtin_convertvector(f32x2_t{m0, m1}, bf16x2_t);
+                    const uint32_t hb = __builtin_bit_cast(uint32_t, hp);
+                    const f32x2_t res = {m0 - bf16_lo(hb), m1 - bf16_hi(hb)};
+                    hw[e2] = hb;
+                    lw[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(res, bf16x2_t));
+                }
+                const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+                const bf16x8_t al = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bn[st][t], acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bn[st][t], acc[t], 0, 0, 0);
+                }
+            }
+            // lane (grp, row) holds rows 4*grp + r of column row; add the three
+            // split columns of head `row` (lanes row < G keep the result)
+            float S4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    const int t = (q * G) / 16;
+                    const int src = (lane & 48) | ((q * G + row) & 15);
+                    v += __shfl(acc[t][r], src, kWave);
+                }
+                S4[r] = v;
+            }
+            if (row < G) {
+                const int base = (tb + u) * 16 + 4 * grp;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = base + r;
+                    if (key < cnt) {
+                        const int n = start + key;
+                        if (a.s_int) a.s_int[((int64_t)s * a.cap + n) * G + row] = S4[r];
+                        if (a.s_raw) a.s_raw[((int64_t)s * G + row) * a.cap + n] = S4[r];
+                        if (cntl == 0) shift = S4[r];
+                        const float dv = S4[r] - shift;
+                        sd += dv;
+                        sd2 = fmaf(dv, dv, sd2);
+                        ++cntl;
+                    }
+                }
+            }
+        }
+    }
+
+    // merge the lane summaries of each head: across the 4 lane groups, then waves
+    double n = (double)cntl, m = 0.0, m2 = 0.0;
+    if (cntl > 0) {
+        m = (double)shift + (double)sd / n;
+        m2 = fmax((double)sd2 - (double)sd * (double)sd / n, 0.0);
+    }
+#pragma unroll
+    for (int x = 16; x <= 32; x <<= 1) {
+        const double nb = __shfl_xor(n, x, kWave), mb = __shfl_xor(m, x, kWave), m2b = __shfl_xor(m2, x, kWave);
+        chan_merge(n, m, m2, nb, mb, m2b);
+    }
+    if (lane < G) {
+        part[wave][lane][0] = n;
+        part[wave][lane][1] = m;
+        part[wave][lane][2] = m2;
+    }
+    __syncthreads();
+    if (tid < G) {
+        double tn = 0.0, tm = 0.0, tm2 = 0.0;
+        for (int w = 0; w < 4; ++w) chan_merge(tn, tm, tm2, part[w][tid][0], part[w][tid][1], part[w][tid][2]);
+        a.stats[((int64_t)s * a.n_chunks + c) * G + tid] = make_double2(tm, tm2);
+    }
+}
+
 template <int D, int G, bool BF16>
 static void score_kernel(const ScoreArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((k_score<D, G, BF16>), dim3((unsigned)((int64_t)a.n_seg * a.n_chunks)), dim3(256), 0,
@@ -188,8 +402,11 @@ static void score_kernel(const ScoreArgs& a, hipStream_t stream) {
 
 template <int D, int G>
 static void score_dtype(const ScoreArgs& a, bool bf16, hipStream_t stream) {
-    if (bf16) score_kernel<D, G, true>(a, stream);
-    else score_kernel<D, G, false>(a, stream);
+    if (bf16)
+        hipLaunchKernelGGL((k_score_mfma<D, G>), dim3((unsigned)((int64_t)a.n_seg * a.n_chunks)), dim3(256), 0,
+                           stream, a);
+    else
+        score_kernel<D, G, false>(a, stream);
 }
 
 template <int D>
