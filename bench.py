@@ -87,14 +87,41 @@ def cpu_baseline(W, cfg, g, cal, B, n_sample):
                       f"layers/sequences/heads; {dt:.1f} s wall on {threads} threads"}
 
 
+def copy_probe(mib):
+    """Plain device-to-device copies of a known size, for scaling counters."""
+    import torch
+    torch.cuda.set_device(0)
+    n = mib * 1024 * 1024
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        b.copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(ms, 4),
+                      "copy_GBs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l"])
-    ap.add_argument("--cpu-sample", type=int, default=8, help="oracle segments for the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="oracle segments for the CPU baseline (0: skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
+                         "(known-size reference for hardware byte counters)")
     args = ap.parse_args()
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); the pruning "

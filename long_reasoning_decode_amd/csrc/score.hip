@@ -227,6 +227,13 @@ __device__ __forceinline__ void chan_merge(double& n, double& m, double& m2, dou
     n = nt;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediates (gfx9 encoding): wait for all vector-memory operations
+// (this includes LDS-DMA loads), or for all LDS operations.
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
     constexpr int F = D / 2;
@@ -234,8 +241,16 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
     constexpr int NS = F / 32;               // norm k-steps
     constexpr int NCOL = 3 * G;              // (split, head) columns
     constexpr int NT = (NCOL + 15) / 16;     // 16-column MFMA tiles
-    constexpr int UT = 2;                    // 16-key tiles per wave iteration
+    constexpr int UT = 2;                    // 16-key tiles per wave stage
     constexpr int ROWB = D * 2;
+    constexpr int CPR = ROWB / 16;           // 16-byte chunks per key row
+    constexpr int SKEYS = 16 * UT;           // keys per wave stage
+    constexpr int NDMA = SKEYS * CPR / 64;   // LDS-DMA instructions per stage
+    // Each wave stages its keys through its own LDS region: global_load_lds
+    // writes 64 x 16 bytes per instruction (4 whole 256-byte rows for head_dim
+    // 128), with the non-temporal hint; chunk lc of stage key k sits at chunk
+    // position lc ^ (k mod CPR) so the fragment reads below are conflict-free.
+    __shared__ uint4 stage[4][SKEYS * CPR];
     __shared__ double part[4][G][3];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -290,15 +305,34 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
     float shift = 0.0f, sd = 0.0f, sd2 = 0.0f;
     int cntl = 0;
     const int n_tiles = (cnt + 15) / 16;
+    uint4* region = &stage[wave][0];
+    // DMA of the stage whose first tile is tb: instruction i, lane l fills
+    // chunk position P = 64 i + l, i.e. key P / CPR, chunk (P mod CPR) ^ key.
+    auto issue_stage = [&](int tb) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int P = 64 * i + lane;
+            const int kl = P / CPR;
+            const int lc = (P % CPR) ^ (kl % CPR);
+            const int key = min(tb * 16 + kl, cnt - 1);            // clamped: tail rows re-read a valid row
+            const uint8_t* src = a.kv.k + a.kv.row(s, start + key) * ROWB + 16 * lc;
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + 64 * i), 16, 0, 2 /* nt */);
+        }
+    };
+    if (wave * UT < n_tiles) issue_stage(wave * UT);
     for (int tb = wave * UT; tb < n_tiles; tb += 4 * UT) {
         uint4 av[UT][TS];
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);                      // this stage's DMA has landed
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int u = 0; u < UT; ++u) {
-            const int key = min((tb + u) * 16 + row, cnt - 1);     // clamped: tail rows re-read a valid row
-            const uint8_t* p = a.kv.k + a.kv.row(s, start + key) * ROWB + grp * 16;
+            const int kl = 16 * u + row;
 #pragma unroll
-            for (int st = 0; st < TS; ++st) av[u][st] = *reinterpret_cast<const uint4*>(p + st * 64);
+            for (int st = 0; st < TS; ++st) av[u][st] = region[kl * CPR + ((4 * st + grp) ^ (kl % CPR))];
         }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                    // fragments are in registers
+        __builtin_amdgcn_wave_barrier();
+        if (tb + 4 * UT < n_tiles) issue_stage(tb + 4 * UT);       // next stage loads under this compute
 #pragma unroll
         for (int u = 0; u < UT; ++u) {
             if (tb + u >= n_tiles) break;
