@@ -187,6 +187,10 @@ int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, floa
 /* Static description of a status code. */
 const char* tri_strerror(int code);
 
+/* For the calling thread's most recent TRI_ERR_HIP: which step failed and the
+ * HIP error string ("" if none).  Valid until the next failing call. */
+const char* tri_last_error(void);
+
 /*
  * Kernel timing (instrumentation).  When enabled, every kernel launched by
  * the library is bracketed by HIP events on its stream; tri_timing_read

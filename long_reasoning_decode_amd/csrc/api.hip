@@ -2,6 +2,7 @@
 // calibration handle, workspace planning, kernel dispatch and the optional
 // kernel timing.  Declarations and contracts: include/triattn.h.
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -154,7 +155,14 @@ WsPlan plan_workspace(const tri_calib_s* c, const tri_cache_desc* kv) {
     return p;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? TRI_OK : TRI_ERR_HIP; }
+// Detail of the most recent TRI_ERR_HIP on this thread (see tri_last_error).
+thread_local char t_last_error[192] = "";
+
+int hip_status(hipError_t e, const char* step = "launch") {
+    if (e == hipSuccess) return TRI_OK;
+    snprintf(t_last_error, sizeof t_last_error, "%s: %s (%d)", step, hipGetErrorString(e), (int)e);
+    return TRI_ERR_HIP;
+}
 
 // phase + score shared by tri_score and tri_prune_window.
 int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const int32_t* t, float* s_raw,
@@ -169,7 +177,7 @@ int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const in
     pa.n_seq = kv->n_seq;
     pa.n_q_heads = c->Hq;
     pa.head_dim = c->D;
-    int rc = hip_status(launch_phase(pa, st));
+    int rc = hip_status(launch_phase(pa, st), "phase kernel");
     if (rc) return rc;
 
     ScoreArgs sa;
@@ -186,7 +194,7 @@ int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const in
     sa.chunk = chunk;
     sa.n_chunks = (int)((kv->capacity + chunk - 1) / chunk);
     sa.n_seg = (int)n_segments(kv);
-    return hip_status(launch_score(sa, c->D, c->G, kv->dtype == TRI_DTYPE_BF16, st));
+    return hip_status(launch_score(sa, c->D, c->G, kv->dtype == TRI_DTYPE_BF16, st), "score kernel");
 }
 
 }  // namespace
@@ -347,7 +355,7 @@ int tri_score(tri_calib_t calib, const tri_cache_desc* kv, const int32_t* t, flo
     za.chunk = chunk;
     za.n_chunks = (int)((kv->capacity + chunk - 1) / chunk);
     za.n_seg = (int)n_segments(kv);
-    return hip_status(launch_zmax(za, calib->G, st));
+    return hip_status(launch_zmax(za, calib->G, st), "aggregation kernel");
 }
 
 int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int capacity, int budget,
@@ -370,7 +378,7 @@ int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int cap
     a.gather = 0;
     a.n_seg = n_seg;
     a.cap = capacity;
-    return hip_status(launch_select(a, 0, capacity, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_select(a, 0, capacity, static_cast<hipStream_t>(stream)), "select kernel");
 }
 
 static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int budget) {
@@ -404,7 +412,7 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
     a.rows_per_block = 64;
     a.blocks_per_seg = (budget + 63) / 64;
     a.n_seg = (int)n_segments(src);
-    return hip_status(launch_gather(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_gather(a, static_cast<hipStream_t>(stream)), "gather kernel");
 }
 
 int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
@@ -440,7 +448,7 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     a.dst = out_of(dst);
     a.row_bytes = src->head_dim * elem_size(src->dtype);
     a.n_seg = (int)n_segments(src);
-    return hip_status(launch_select(a, calib->G, src->capacity, st));
+    return hip_status(launch_select(a, calib->G, src->capacity, st), "select+gather kernel");
 }
 
 int tri_append(const tri_cache_desc* kv, const void* k_new, const void* v_new, const int32_t* pos_new,
@@ -459,7 +467,7 @@ int tri_append(const tri_cache_desc* kv, const void* k_new, const void* v_new, c
     a.shape = shape_of(kv);
     a.row_bytes = kv->head_dim * elem_size(kv->dtype);
     a.n_seg = (int)n_segments(kv);
-    return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
+    return hip_status(launch_append(a, static_cast<hipStream_t>(stream)), "append kernel");
 }
 
 int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, float scale, float* out,
@@ -481,7 +489,7 @@ int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, floa
     a.n_q_heads = n_q_heads;
     a.n_seg = (int)n_segments(kv);
     return hip_status(launch_decode_attn(a, kv->head_dim, G, kv->dtype == TRI_DTYPE_BF16,
-                                         static_cast<hipStream_t>(stream)));
+                                         static_cast<hipStream_t>(stream)), "decode attention kernel");
 }
 
 int tri_timing_enable(int enable) {
@@ -508,6 +516,8 @@ int tri_timing_read(int which, int64_t* launches, double* total_ms) {
     *total_ms = g_ms[which];
     return TRI_OK;
 }
+
+const char* tri_last_error(void) { return t_last_error; }
 
 const char* tri_timing_name(int which) {
     if (which < 0 || which >= KID_COUNT) return nullptr;

@@ -251,6 +251,7 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
     // 128), with the non-temporal hint; chunk lc of stage key k sits at chunk
     // position lc ^ (k mod CPR) so the fragment reads below are conflict-free.
     __shared__ uint4 stage[4][SKEYS * CPR];
+    __shared__ float tileS[4][16 * G];        // one tile's scores, key-major, for full-line stores
     __shared__ double part[4][G][3];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -384,15 +385,13 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
                 }
                 S4[r] = v;
             }
+            const int tile0 = (tb + u) * 16;
             if (row < G) {
-                const int base = (tb + u) * 16 + 4 * grp;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int key = base + r;
+                    const int key = tile0 + 4 * grp + r;
+                    tileS[wave][(4 * grp + r) * G + row] = S4[r];
                     if (key < cnt) {
-                        const int n = start + key;
-                        if (a.s_int) a.s_int[((int64_t)s * a.cap + n) * G + row] = S4[r];
-                        if (a.s_raw) a.s_raw[((int64_t)s * G + row) * a.cap + n] = S4[r];
                         if (cntl == 0) shift = S4[r];
                         const float dv = S4[r] - shift;
                         sd += dv;
@@ -401,6 +400,30 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
                     }
                 }
             }
+            __builtin_amdgcn_wave_barrier();
+            // Scores leave through LDS so every store instruction writes whole
+            // lines: key-major scratch (lanes 0..15 store one key's G scores,
+            // 16 keys x 4G bytes contiguous) or head-major output (lane (h, k)
+            // stores S_h(k)).  Scattered 4-byte stores mixed into the key stream
+            // made the stream's speed depend on where the scratch was allocated.
+            if (a.s_int && lane < 16 && tile0 + lane < cnt) {
+                float* o = a.s_int + ((int64_t)s * a.cap + start + tile0 + lane) * G;
+                if constexpr (G % 4 == 0) {
+#pragma unroll
+                    for (int g = 0; g < G; g += 4)
+                        *reinterpret_cast<float4*>(o + g) = *reinterpret_cast<const float4*>(&tileS[wave][lane * G + g]);
+                } else {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) o[g] = tileS[wave][lane * G + g];
+                }
+            }
+            if (a.s_raw) {
+                for (int i = lane; i < 16 * G; i += kWave) {
+                    const int h = i / 16, k = i % 16;
+                    if (tile0 + k < cnt) a.s_raw[((int64_t)s * G + h) * a.cap + start + tile0 + k] = tileS[wave][k * G + h];
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
         }
     }
 

@@ -29,7 +29,7 @@ TRI_LAYOUT_PAGED = 1
 EXPORTS = (
     "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
     "tri_compact", "tri_prune_window", "tri_append", "tri_decode_attn", "tri_strerror",
-    "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name",
+    "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name", "tri_last_error",
 )
 
 
@@ -37,7 +37,8 @@ class TriError(RuntimeError):
     def __init__(self, fn, code):
         self.code = code
         msg = _lib.tri_strerror(code).decode() if _lib is not None else str(code)
-        super().__init__(f"{fn} failed: {msg} ({code})")
+        detail = _lib.tri_last_error().decode() if (_lib is not None and code == TRI_ERR_HIP) else ""
+        super().__init__(f"{fn} failed: {msg} ({code})" + (f": {detail}" if detail else ""))
 
 
 class CacheDesc(ctypes.Structure):
@@ -81,11 +82,12 @@ def load():
         "tri_timing_reset": [],
         "tri_timing_read": [I, ctypes.POINTER(I64), ctypes.POINTER(D)],
         "tri_timing_name": [I],
+        "tri_last_error": [],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name in ("tri_strerror", "tri_timing_name") else ctypes.c_int
+        fn.restype = ctypes.c_char_p if name in ("tri_strerror", "tri_timing_name", "tri_last_error") else ctypes.c_int
     _lib = lib
     return lib
 
@@ -226,6 +228,10 @@ def tri_decode_attn(desc, n_q_heads, q, scale, out, stream=None):
 
 def tri_strerror(code):
     return load().tri_strerror(int(code)).decode()
+
+
+def tri_last_error():
+    return load().tri_last_error().decode()
 
 
 def tri_timing_enable(on=True):
