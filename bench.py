@@ -171,6 +171,7 @@ def main():
     T.tri_timing_enable(False)
     ms = ev0.elapsed_time(ev1) / args.steps
     kt = T.tri_timing_read()
+    fallbacks = T.tri_prune_fallbacks(ws)
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     n_keys = cfg.n_seg * cfg.n_keys
@@ -185,7 +186,7 @@ def main():
             kernels[name] = {"avg_ms": round(avg, 4), "launches": launches,
                              "algorithmic_bytes": bytes_per_launch,
                              "achieved_GBs": round(bytes_per_launch / (avg * 1e-3) / 1e9, 1)}
-    for name in ("phase",):
+    for name in ("phase", "sample", "score_fallback", "select_fallback"):
         launches, total = kt.get(name, (0, 0.0))
         if launches:
             kernels[name] = {"avg_ms": round(total / launches, 4), "launches": launches}
@@ -217,6 +218,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernels": kernels,
+        "fallback_segments": fallbacks,
     }
     if args.cpu_sample > 0:
         result["cpu_baseline"] = cpu_baseline(W, cfg, g, cal, B, args.cpu_sample)

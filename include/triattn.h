@@ -163,6 +163,20 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
 int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
                      const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,
                      tri_stream_t stream);
+/*
+ * How the pass runs (the result does not depend on it): for bf16 caches,
+ * segments with N >= 4096 and N >= 8 B first get per-head score thresholds
+ * from a 256-key sample, and only keys reaching a threshold in some head
+ * keep their scores for the select step.  The select step proves, with the
+ * exact per-head statistics, that every other key ranks below the cut;
+ * segments where that proof fails are scored and selected again over all of
+ * their keys within the same call.  The kept set is always the one the
+ * full-score path gives.
+ *
+ * tri_prune_fallbacks: number of segments the last tri_prune_window on this
+ * workspace had to redo in full (host int32 *count).  Synchronises `stream`.
+ */
+int tri_prune_fallbacks(const void* ws, size_t ws_bytes, int32_t* count, tri_stream_t stream);
 
 /*
  * Appends one token to every segment: row lengths[s] of segment s receives

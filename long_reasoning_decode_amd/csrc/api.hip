@@ -40,8 +40,9 @@ bool g_timing = false;
 std::vector<PendingTiming> g_pending;
 int64_t g_launches[KID_COUNT] = {};
 double g_ms[KID_COUNT] = {};
-const char* kKernelNames[KID_COUNT] = {"phase",  "score",  "zmax",   "select",
-                                       "select_gather", "gather", "append", "decode_attn"};
+const char* kKernelNames[KID_COUNT] = {"phase",  "score",  "zmax",   "select",         "select_gather",
+                                       "gather", "append", "decode_attn", "sample", "score_fallback",
+                                       "select_fallback"};
 
 void drain_timing_locked() {
     for (auto& p : g_pending) {
@@ -140,17 +141,25 @@ int pick_chunk(int64_t n_seg, int64_t cap) {
     return chunk;
 }
 
+// Workspace layout.  The fallback counter of the last pruning pass sits at
+// offset 0 so tri_prune_fallbacks can find it without the cache shape.
 struct WsPlan {
-    size_t ctab, stats, s_int, total;
+    size_t fb_count, fb_list, ctab, stats, thr, masks, s_int, total;
+    int64_t mask_stride;
 };
 
 WsPlan plan_workspace(const tri_calib_s* c, const tri_cache_desc* kv) {
     const int64_t n_seg = n_segments(kv);
     const int64_t max_chunks = (kv->capacity + kMinChunk - 1) / kMinChunk;
     WsPlan p;
-    p.ctab = 0;
-    p.stats = align256((size_t)kv->n_layers * kv->n_seq * c->Hq * c->D * sizeof(float));
-    p.s_int = p.stats + align256((size_t)n_seg * max_chunks * c->G * sizeof(double2));
+    p.mask_stride = (kv->capacity + 31) / 32;
+    p.fb_count = 0;
+    p.fb_list = 256;
+    p.ctab = p.fb_list + align256((size_t)n_seg * sizeof(int32_t));
+    p.stats = p.ctab + align256((size_t)kv->n_layers * kv->n_seq * c->Hq * c->D * sizeof(float));
+    p.thr = p.stats + align256((size_t)n_seg * max_chunks * c->G * sizeof(double2));
+    p.masks = p.thr + align256((size_t)n_seg * c->G * sizeof(float));
+    p.s_int = p.masks + align256((size_t)n_seg * p.mask_stride * sizeof(uint32_t));
     p.total = p.s_int + align256((size_t)n_seg * kv->capacity * c->G * sizeof(float));
     return p;
 }
@@ -165,8 +174,11 @@ int hip_status(hipError_t e, const char* step = "launch") {
 }
 
 // phase + score shared by tri_score and tri_prune_window.
+// With `cand` (bf16 pruning pass): the sample kernel sets candidate thresholds
+// and the score kernel writes candidate lists and masks instead of every score.
 int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const int32_t* t, float* s_raw,
-                        float* s_int, double2* stats, float* ctab, int chunk, hipStream_t st) {
+                        float* s_int, double2* stats, float* ctab, int chunk, hipStream_t st,
+                        const WsPlan* cand = nullptr, char* ws = nullptr, int budget = 0) {
     PhaseArgs pa;
     pa.P = c->P;
     pa.omega = c->omega;
@@ -194,7 +206,32 @@ int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const in
     sa.chunk = chunk;
     sa.n_chunks = (int)((kv->capacity + chunk - 1) / chunk);
     sa.n_seg = (int)n_segments(kv);
-    return hip_status(launch_score(sa, c->D, c->G, kv->dtype == TRI_DTYPE_BF16, st), "score kernel");
+    sa.thr = nullptr;
+    sa.masks = nullptr;
+    sa.mask_stride = 0;
+    sa.fb_list = nullptr;
+    sa.fb_count = nullptr;
+    int mode = SCORE_FULL;
+    if (cand) {
+        SampleArgs pa2;
+        pa2.kv = sa.kv;
+        pa2.shape = sa.shape;
+        pa2.lengths = kv->lengths;
+        pa2.ctab = ctab;
+        pa2.wtab = sa.wtab;
+        pa2.thr = reinterpret_cast<float*>(ws + cand->thr);
+        pa2.fb_count = reinterpret_cast<int32_t*>(ws + cand->fb_count);
+        pa2.cap = kv->capacity;
+        pa2.n_q_heads = c->Hq;
+        pa2.budget = budget;
+        pa2.n_seg = sa.n_seg;
+        if ((rc = hip_status(launch_sample(pa2, c->D, c->G, st), "sample kernel"))) return rc;
+        sa.thr = pa2.thr;
+        sa.masks = reinterpret_cast<uint32_t*>(ws + cand->masks);
+        sa.mask_stride = cand->mask_stride;
+        mode = SCORE_CANDIDATES;
+    }
+    return hip_status(launch_score(sa, c->D, c->G, kv->dtype == TRI_DTYPE_BF16, mode, st), "score kernel");
 }
 
 }  // namespace
@@ -378,7 +415,7 @@ int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int cap
     a.gather = 0;
     a.n_seg = n_seg;
     a.cap = capacity;
-    return hip_status(launch_select(a, 0, capacity, static_cast<hipStream_t>(stream)), "select kernel");
+    return hip_status(launch_select(a, 0, SELECT_A, capacity, static_cast<hipStream_t>(stream)), "select kernel");
 }
 
 static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int budget) {
@@ -432,7 +469,13 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     double2* stats = reinterpret_cast<double2*>(w + p.stats);
     float* s_int = reinterpret_cast<float*>(w + p.s_int);
     const int chunk = pick_chunk(n_segments(src), src->capacity);
-    if ((rc = run_phase_and_score(calib, src, t, nullptr, s_int, stats, ctab, chunk, st))) return rc;
+    // bf16 caches: candidate pass (sample -> score lists -> certified select),
+    // then the full path for any segment whose certificate failed (both
+    // fallback kernels exit at once when none did).  fp32 caches: full path.
+    const bool cand = src->dtype == TRI_DTYPE_BF16;
+    if ((rc = run_phase_and_score(calib, src, t, nullptr, s_int, stats, ctab, chunk, st, cand ? &p : nullptr, w,
+                                  budget)))
+        return rc;
     SelectArgs a;
     memset(&a, 0, sizeof a);
     a.s_int = s_int;
@@ -448,7 +491,42 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     a.dst = out_of(dst);
     a.row_bytes = src->head_dim * elem_size(src->dtype);
     a.n_seg = (int)n_segments(src);
-    return hip_status(launch_select(a, calib->G, src->capacity, st), "select+gather kernel");
+    if (!cand) return hip_status(launch_select(a, calib->G, SELECT_S, src->capacity, st), "select+gather kernel");
+    a.thr = reinterpret_cast<const float*>(w + p.thr);
+    a.masks = reinterpret_cast<const uint32_t*>(w + p.masks);
+    a.mask_stride = p.mask_stride;
+    a.fb_list = reinterpret_cast<int32_t*>(w + p.fb_list);
+    a.fb_count = reinterpret_cast<int32_t*>(w + p.fb_count);
+    if ((rc = hip_status(launch_select(a, calib->G, SELECT_C, src->capacity, st), "select+gather kernel")))
+        return rc;
+    ScoreArgs sa;
+    memset(&sa, 0, sizeof sa);
+    sa.kv = a.src;
+    sa.shape = shape_of(src);
+    sa.lengths = src->lengths;
+    sa.ctab = ctab;
+    sa.wtab = calib->wnorm + (int64_t)src->layer0 * calib->Hq * calib->F;
+    sa.s_int = s_int;
+    sa.stats = stats;
+    sa.fb_list = a.fb_list;
+    sa.fb_count = a.fb_count;
+    sa.cap = src->capacity;
+    sa.n_q_heads = calib->Hq;
+    sa.chunk = chunk;
+    sa.n_chunks = a.n_chunks;
+    sa.n_seg = a.n_seg;
+    if ((rc = hip_status(launch_score(sa, calib->D, calib->G, true, SCORE_FALLBACK, st), "fallback score kernel")))
+        return rc;
+    return hip_status(launch_select(a, calib->G, SELECT_S_FALLBACK, src->capacity, st), "fallback select kernel");
+}
+
+int tri_prune_fallbacks(const void* ws, size_t ws_bytes, int32_t* count, tri_stream_t stream) {
+    if (!ws || !count || ws_bytes < sizeof(int32_t)) return TRI_ERR_INVALID_ARG;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(count, ws, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    return hip_status(e, "fallback count read");
 }
 
 int tri_append(const tri_cache_desc* kv, const void* k_new, const void* v_new, const int32_t* pos_new,

@@ -18,8 +18,32 @@ enum KernelId : int {
     KID_GATHER,
     KID_APPEND,
     KID_DECODE_ATTN,
+    KID_SAMPLE,
+    KID_SCORE_FALLBACK,
+    KID_SELECT_FALLBACK,
     KID_COUNT
 };
+
+// Whether the fused pass of a segment with N keys and budget B runs on a
+// candidate list (keys whose score can reach the top B) instead of every key.
+// Small segments, and budgets above 1/8 of the segment, keep every key.
+__host__ __device__ inline bool candidate_mode(int64_t N, int64_t B) { return N >= 4096 && N >= 8 * B; }
+
+// In candidate mode, wave w of a scoring workgroup scores the 32-key blocks
+// w, w+4, w+8, ... of its chunk; its candidate list starts after the keys of
+// waves 0..w-1, so the four lists of a chunk of cnt keys fill at most the
+// scratch rows of those cnt keys.
+__device__ inline int wave_keys(int w, int cnt) {
+    const int full = cnt / 32, rem = cnt % 32;
+    int n = full > w ? (full - w + 3) / 4 * 32 : 0;
+    if (rem && (full & 3) == w) n += rem;
+    return n;
+}
+__device__ inline int wave_list_base(int w, int cnt) {
+    int b = 0;
+    for (int i = 0; i < w; ++i) b += wave_keys(i, cnt);
+    return b;
+}
 
 // Brackets one launch with HIP events when timing is enabled.
 struct TimedLaunch {
@@ -41,6 +65,20 @@ struct PhaseArgs {
 };
 hipError_t launch_phase(const PhaseArgs& a, hipStream_t stream);
 
+// --- candidate thresholds: per segment and head, L_h from a key sample.
+struct SampleArgs {
+    CacheView kv;
+    SegShape shape;
+    const int32_t* lengths;
+    const float* ctab;
+    const float* wtab;
+    float* thr;             // [n_seg][G]
+    int32_t* fb_count;      // zeroed here (the pass's fallback counter)
+    int64_t cap;
+    int32_t n_q_heads, budget, n_seg;
+};
+hipError_t launch_sample(const SampleArgs& a, int head_dim, int group, hipStream_t stream);
+
 // --- score: raw per-head scores of every key, plus per-chunk (mean, M2).
 struct ScoreArgs {
     CacheView kv;
@@ -49,15 +87,21 @@ struct ScoreArgs {
     const float* ctab;      // [n_layers][n_seq][Hq][D]
     const float* wtab;      // [n_layers][Hq][F]  ((1 - R) M, from layer0)
     float* s_raw;           // optional [n_seg][G][cap]
-    float* s_int;           // optional [n_seg][cap][G]
+    float* s_int;           // optional [n_seg][cap][G]; candidate mode: per-wave candidate lists
     double2* stats;         // [n_seg][n_chunks][G]
+    const float* thr;       // candidate mode: [n_seg][G] thresholds L_h
+    uint32_t* masks;        // candidate mode: [n_seg][mask_stride], bit i of word b = key 32 b + i
+    int64_t mask_stride;
+    const int32_t* fb_list; // fallback mode: segments to redo, and their count
+    const int32_t* fb_count;
     int64_t cap;
     int32_t n_q_heads;
-    int32_t chunk;          // keys per block (multiple of 256)
+    int32_t chunk;          // keys per block (multiple of 512)
     int32_t n_chunks;
     int32_t n_seg;
 };
-hipError_t launch_score(const ScoreArgs& a, int head_dim, int group, bool bf16, hipStream_t stream);
+enum ScoreMode : int { SCORE_FULL = 0, SCORE_CANDIDATES = 1, SCORE_FALLBACK = 2 };
+hipError_t launch_score(const ScoreArgs& a, int head_dim, int group, bool bf16, int mode, hipStream_t stream);
 
 // --- zmax: merge chunk statistics, A = max_h z_h for every key.
 struct ZmaxArgs {
@@ -76,8 +120,13 @@ hipError_t launch_zmax(const ZmaxArgs& a, int group, hipStream_t stream);
 struct SelectArgs {
     const float* agg;       // mode A: [n_seg][agg_stride]
     int64_t agg_stride;
-    const float* s_int;     // mode S: [n_seg][cap][G] + chunk stats
+    const float* s_int;     // mode S: [n_seg][cap][G] + chunk stats; mode C: candidate lists
     const double2* stats;
+    const float* thr;       // mode C: thresholds, candidate masks, fallback list
+    const uint32_t* masks;
+    int64_t mask_stride;
+    int32_t* fb_list;
+    int32_t* fb_count;
     int32_t n_chunks, chunk;
     int64_t cap;
     const int32_t* lengths;
@@ -91,8 +140,11 @@ struct SelectArgs {
     int32_t row_bytes;
     int32_t n_seg;
 };
-hipError_t launch_select(const SelectArgs& a, int group /*0 = mode A*/, int64_t max_len,
-                         hipStream_t stream);
+// mode A: select on aggregated scores (group 0); S: on interleaved scores;
+// C: on candidate lists, with the certificate and fallback list; S_FALLBACK:
+// mode S over the segments listed in fb_list.
+enum SelectMode : int { SELECT_A = 0, SELECT_S = 1, SELECT_C = 2, SELECT_S_FALLBACK = 3 };
+hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_len, hipStream_t stream);
 
 // --- gather (unfused compaction)
 struct GatherArgs {

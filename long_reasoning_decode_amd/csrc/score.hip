@@ -234,8 +234,21 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitLgkm0 = 0xC07F;
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
+// Candidate records are staged per wave and leave in groups of kFlush records
+// (kFlush * G floats, whole 128-byte lines).
+constexpr int kFlush = 32;
+constexpr int kMaxChunkBlocks = 2048 / 32;   // 32-key mask words per chunk
+
+// Scores chunk c of segment s.  CAND = false: every key's G scores go to the
+// interleaved scratch (and/or the head-major output).  CAND = true: only keys
+// with some S_h >= L_h (the segment's thresholds) are kept, as G-float records
+// in a per-wave list in slot order, plus one 32-bit mask word per 32-key block
+// saying which keys those are.  Wave w of a chunk scores blocks w, w+4, w+8,
+// ..., so its list holds at most wave_keys(w, cnt) records; the four lists
+// sit back to back in the scratch rows of the chunk's keys.  The chunk
+// statistics always cover every key.
+template <int D, int G, bool CAND>
+__device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s, const int c) {
     constexpr int F = D / 2;
     constexpr int TS = D / 32;               // trig k-steps = 16-byte A fragments per key
     constexpr int NS = F / 32;               // norm k-steps
@@ -250,18 +263,30 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
     // writes 64 x 16 bytes per instruction (4 whole 256-byte rows for head_dim
     // 128), with the non-temporal hint; chunk lc of stage key k sits at chunk
     // position lc ^ (k mod CPR) so the fragment reads below are conflict-free.
+    static_assert(SKEYS == 32, "one stage is one 32-key mask block");
     __shared__ uint4 stage[4][SKEYS * CPR];
-    __shared__ float tileS[4][16 * G];        // one tile's scores, key-major, for full-line stores
+    // one tile's scores (one stage's in candidate mode), key-major
+    __shared__ float tileS[4][(CAND ? 32 : 16) * G];
     __shared__ double part[4][G][3];
+    __shared__ float cbuf[CAND ? 4 : 1][CAND ? (kFlush + 32) * G : 1];
+    __shared__ uint32_t maskbuf[CAND ? kMaxChunkBlocks : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, grp = lane >> 4;
-    const int s = blockIdx.x / a.n_chunks;
-    const int c = blockIdx.x - s * a.n_chunks;
     const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
     const int start = c * a.chunk;
     if (start >= N) return;
     const int cnt = min(a.chunk, N - start);
+
+    float thr[CAND ? G : 1];
+    int nb = 0, nw = 0;            // records staged in LDS / already written (wave-uniform)
+    uint32_t bmask = 0u;
+    float* list = nullptr;
+    if constexpr (CAND) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) thr[g] = a.thr[(int64_t)s * G + g];
+        list = a.s_int + ((int64_t)s * a.cap + start + wave_list_base(wave, cnt)) * G;
+    }
 
     // loop-invariant B fragments: column row -> (q, h), k-slot (grp, e)
     bf16x8_t bt[TS][NT], bn[NS][NT];
@@ -323,7 +348,7 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
     if (wave * UT < n_tiles) issue_stage(wave * UT);
     for (int tb = wave * UT; tb < n_tiles; tb += 4 * UT) {
         uint4 av[UT][TS];
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);                      // this stage's DMA has landed
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);                      // this stage's DMA has landed
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int u = 0; u < UT; ++u) {
@@ -386,11 +411,12 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
                 S4[r] = v;
             }
             const int tile0 = (tb + u) * 16;
+            const int tslot = CAND ? 16 * u : 0;      // candidate mode keeps the stage's two tiles
             if (row < G) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = tile0 + 4 * grp + r;
-                    tileS[wave][(4 * grp + r) * G + row] = S4[r];
+                    tileS[wave][(tslot + 4 * grp + r) * G + row] = S4[r];
                     if (key < cnt) {
                         if (cntl == 0) shift = S4[r];
                         const float dv = S4[r] - shift;
@@ -406,7 +432,7 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
             // 16 keys x 4G bytes contiguous) or head-major output (lane (h, k)
             // stores S_h(k)).  Scattered 4-byte stores mixed into the key stream
             // made the stream's speed depend on where the scratch was allocated.
-            if (a.s_int && lane < 16 && tile0 + lane < cnt) {
+            if (!CAND && a.s_int && lane < 16 && tile0 + lane < cnt) {
                 float* o = a.s_int + ((int64_t)s * a.cap + start + tile0 + lane) * G;
                 if constexpr (G % 4 == 0) {
 #pragma unroll
@@ -425,6 +451,42 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
             }
             __builtin_amdgcn_wave_barrier();
         }
+        if constexpr (CAND) {
+            // lanes 0..31: is key tb*16 + lane a candidate (some S_h >= L_h)?
+            const int key0 = tb * 16;
+            bool isc = false;
+            if (lane < 32 && key0 + lane < cnt) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) isc |= tileS[wave][lane * G + g] >= thr[g];
+            }
+            bmask = (uint32_t)__ballot(isc);
+            if (isc) {
+                const int p = nb + __popc(bmask & ((1u << lane) - 1u));
+#pragma unroll
+                for (int g = 0; g < G; ++g) cbuf[wave][p * G + g] = tileS[wave][lane * G + g];
+            }
+            nb += __popc(bmask);
+            if (lane == 0) maskbuf[tb / UT] = bmask;
+            __builtin_amdgcn_wave_barrier();
+            if (nb >= kFlush) {
+                // kFlush records -> list[nw ..], whole lines; the rest moves to the front
+                if constexpr (G % 4 == 0) {
+                    for (int i = 4 * lane; i < kFlush * G; i += 4 * kWave)
+                        *reinterpret_cast<float4*>(list + (int64_t)nw * G + i) =
+                            *reinterpret_cast<const float4*>(&cbuf[wave][i]);
+                } else {
+                    for (int i = lane; i < kFlush * G; i += kWave) list[(int64_t)nw * G + i] = cbuf[wave][i];
+                }
+                __builtin_amdgcn_wave_barrier();
+                for (int i = lane; i < (nb - kFlush) * G; i += kWave) cbuf[wave][i] = cbuf[wave][kFlush * G + i];
+                nb -= kFlush;
+                nw += kFlush;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    if constexpr (CAND) {
+        for (int i = lane; i < nb * G; i += kWave) list[(int64_t)nw * G + i] = cbuf[wave][i];
     }
 
     // merge the lane summaries of each head: across the 4 lane groups, then waves
@@ -449,6 +511,192 @@ __global__ __launch_bounds__(256) void k_score_mfma(ScoreArgs a) {
         for (int w = 0; w < 4; ++w) chan_merge(tn, tm, tm2, part[w][tid][0], part[w][tid][1], part[w][tid][2]);
         a.stats[((int64_t)s * a.n_chunks + c) * G + tid] = make_double2(tm, tm2);
     }
+    if constexpr (CAND) {
+        for (int i = tid; i < (cnt + 31) / 32; i += 256) a.masks[(int64_t)s * a.mask_stride + start / 32 + i] = maskbuf[i];
+    }
+}
+
+// (at most 128 VGPRs for head_dim 128 with G <= 4, so four workgroups share a CU)
+template <int D, int G, bool CAND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 1))) void k_score_mfma(ScoreArgs a) {
+    const int s = blockIdx.x / a.n_chunks;
+    score_chunk_mfma<D, G, CAND>(a, s, blockIdx.x - s * a.n_chunks);
+}
+
+// Full scoring of the segments whose candidate pass failed its certificate:
+// work items (listed segment, chunk), grid-strided.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_score_mfma_fallback(ScoreArgs a) {
+    const int64_t items = (int64_t)(*a.fb_count) * a.n_chunks;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        __syncthreads();                      // LDS of the previous item is no longer read
+        const int s = a.fb_list[it / a.n_chunks];
+        score_chunk_mfma<D, G, false>(a, s, (int)(it % a.n_chunks));
+    }
+}
+
+// ------------------------------------------------------------------ candidate thresholds
+// One workgroup per segment scores an evenly spaced sample of kSample keys in
+// fp32, estimates each head's mean and spread and the aggregated score at rank
+// kCandMul * B/N of the sample, and stores per-head score thresholds
+// L_h = mean_h + tau * spread_h.  Keys with no S_h >= L_h are left out of the
+// candidate list; the select kernel then proves with the exact statistics that
+// none of them can be among the B kept (else the segment is redone in full).
+// The thresholds only decide how much work is skipped, never the result.
+constexpr int kSample = 256;
+constexpr int kCandMul = 3;
+
+template <int D, int G>
+__global__ __launch_bounds__(kSample) void k_sample(SampleArgs a) {
+    constexpr int F = D / 2;
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int HC = CPR / 2;              // chunks per half row (8 bands each)
+    constexpr int RPI = kWave / CPR;         // rows per wave load
+    constexpr int IT = kSample / 4 / RPI;    // loads per lane
+    __shared__ float cf[G][D];
+    __shared__ float wf[G][F];
+    __shared__ float sS[kSample][G];
+    __shared__ float ah[kSample];
+    __shared__ float red[kSample / kWave][G];
+    __shared__ float tau_s;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int s = blockIdx.x;
+    if (s == 0 && tid == 0) *a.fb_count = 0;
+    const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
+    float* thr = a.thr + (int64_t)s * G;
+    if (!candidate_mode(N, a.budget)) {
+        if (tid < G) thr[tid] = -__builtin_inff();
+        return;
+    }
+    const int l = a.shape.layer(s), b = a.shape.seq(s), hk = a.shape.head(s);
+    const float* cb = a.ctab + ((int64_t)(l * a.shape.n_seq + b) * a.n_q_heads + hk * G) * D;
+    const float* wb = a.wtab + ((int64_t)l * a.n_q_heads + hk * G) * F;
+    for (int i = tid; i < G * D; i += kSample) cf[i / D][i % D] = cb[i];
+    for (int i = tid; i < G * F; i += kSample) wf[i / F][i % F] = wb[i];
+
+    // sample j = w * (kSample/4) + it * RPI + lane / CPR sits at slot j*N/kSample;
+    // its CPR lanes read the row's 16-byte chunks side by side
+    const int sub = lane % CPR, rr = lane / CPR;
+    uint4 v[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int j = w * (kSample / 4) + it * RPI + rr;
+        const int slot = (int)(((int64_t)j * N) / kSample);
+        v[it] = reinterpret_cast<const uint4*>(a.kv.k + a.kv.row(s, slot) * (D * 2))[sub];
+    }
+    __syncthreads();                          // coefficients are in LDS
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        // lanes sub < HC hold 8 bands' real parts; the imaginary parts are HC lanes up
+        uint4 iv;
+        iv.x = __shfl(v[it].x, lane + HC, kWave);
+        iv.y = __shfl(v[it].y, lane + HC, kWave);
+        iv.z = __shfl(v[it].z, lane + HC, kWave);
+        iv.w = __shfl(v[it].w, lane + HC, kWave);
+        float acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = 0.0f;
+        if (sub < HC) {
+            const uint32_t rw[4] = {v[it].x, v[it].y, v[it].z, v[it].w}, iw[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int f = 8 * sub + e;
+                const float re = (e & 1) ? bf16_hi(rw[e >> 1]) : bf16_lo(rw[e >> 1]);
+                const float im = (e & 1) ? bf16_hi(iw[e >> 1]) : bf16_lo(iw[e >> 1]);
+                const float mg = sqrtf(fmaf(re, re, im * im));
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    acc[g] = fmaf(cf[g][f], re, fmaf(cf[g][f + F], im, fmaf(wf[g][f], mg, acc[g])));
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < HC; m <<= 1)
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] += __shfl_xor(acc[g], m, kWave);
+        if (sub == 0) {
+            const int j = w * (kSample / 4) + it * RPI + rr;
+#pragma unroll
+            for (int g = 0; g < G; ++g) sS[j][g] = acc[g];
+        }
+    }
+    __syncthreads();
+    float S[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) S[g] = sS[tid][g];
+
+    // sample mean and spread per head (two passes)
+    float mu[G], sg[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float t = wave_sumf(S[g]);
+        if (lane == 0) red[w][g] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float t = 0.0f;
+        for (int i = 0; i < kSample / kWave; ++i) t += red[i][g];
+        mu[g] = t / kSample;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float dv = S[g] - mu[g];
+        const float t = wave_sumf(dv * dv);
+        if (lane == 0) red[w][g] = t;
+    }
+    __syncthreads();
+    float A = -__builtin_inff();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float t = 0.0f;
+        for (int i = 0; i < kSample / kWave; ++i) t += red[i][g];
+        sg[g] = sqrtf(t / kSample);
+        A = fmaxf(A, sg[g] > 0.0f ? (S[g] - mu[g]) / sg[g] : 0.0f);
+    }
+    ah[tid] = A;
+    if (tid == 0) tau_s = -__builtin_inff();   // (every rank is taken once; NaN scores are unsupported)
+    __syncthreads();
+    // tau = the r-th largest sample aggregate, r = ceil(kCandMul B kSample / N)
+    const int64_t r64 = ((int64_t)kCandMul * a.budget * kSample + N - 1) / N;
+    const int r = (int)(r64 < 1 ? 1 : r64 > kSample ? kSample : r64);
+    int rank = 0;
+    for (int j = 0; j < kSample; ++j) {
+        const float v2 = ah[j];
+        rank += (v2 > A) || (v2 == A && j < tid);
+    }
+    if (rank == r - 1) tau_s = A;
+    __syncthreads();
+    if (tid < G) {
+        float m = 0.0f, sd = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            if (g == tid) { m = mu[g]; sd = sg[g]; }
+        // a head with no spread in the sample admits every key (its scores here
+        // and in the scoring pass may differ in the last bit)
+        thr[tid] = sd > 0.0f ? fmaf(tau_s, sd, m) : -__builtin_inff();
+    }
+}
+
+template <int D>
+static bool sample_group(const SampleArgs& a, int group, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_seg), block(kSample);
+    switch (group) {
+        case 1: hipLaunchKernelGGL((k_sample<D, 1>), grid, block, 0, stream, a); return true;
+        case 2: hipLaunchKernelGGL((k_sample<D, 2>), grid, block, 0, stream, a); return true;
+        case 4: hipLaunchKernelGGL((k_sample<D, 4>), grid, block, 0, stream, a); return true;
+        case 8: hipLaunchKernelGGL((k_sample<D, 8>), grid, block, 0, stream, a); return true;
+        default: return false;
+    }
+}
+
+hipError_t launch_sample(const SampleArgs& a, int head_dim, int group, hipStream_t stream) {
+    if (a.n_seg == 0) return hipSuccess;
+    TimedLaunch tl(KID_SAMPLE, stream);
+    const bool ok = head_dim == 64 ? sample_group<64>(a, group, stream)
+                  : head_dim == 128 ? sample_group<128>(a, group, stream) : false;
+    if (!ok) return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 template <int D, int G, bool BF16>
@@ -458,30 +706,40 @@ static void score_kernel(const ScoreArgs& a, hipStream_t stream) {
 }
 
 template <int D, int G>
-static void score_dtype(const ScoreArgs& a, bool bf16, hipStream_t stream) {
-    if (bf16)
-        hipLaunchKernelGGL((k_score_mfma<D, G>), dim3((unsigned)((int64_t)a.n_seg * a.n_chunks)), dim3(256), 0,
-                           stream, a);
-    else
+static bool score_dtype(const ScoreArgs& a, bool bf16, int mode, hipStream_t stream) {
+    const int64_t items = (int64_t)a.n_seg * a.n_chunks;
+    if (!bf16) {
+        if (mode != SCORE_FULL) return false;         // candidate lists are a bf16 (MFMA) feature
         score_kernel<D, G, false>(a, stream);
+        return true;
+    }
+    if (mode == SCORE_FULL)
+        hipLaunchKernelGGL((k_score_mfma<D, G, false>), dim3((unsigned)items), dim3(256), 0, stream, a);
+    else if (mode == SCORE_CANDIDATES)
+        hipLaunchKernelGGL((k_score_mfma<D, G, true>), dim3((unsigned)items), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_score_mfma_fallback<D, G>), dim3((unsigned)(items < 2048 ? items : 2048)), dim3(256), 0,
+                           stream, a);
+    return true;
 }
 
 template <int D>
-static bool score_group(const ScoreArgs& a, int group, bool bf16, hipStream_t stream) {
+static bool score_group(const ScoreArgs& a, int group, bool bf16, int mode, hipStream_t stream) {
     switch (group) {
-        case 1: score_dtype<D, 1>(a, bf16, stream); return true;
-        case 2: score_dtype<D, 2>(a, bf16, stream); return true;
-        case 4: score_dtype<D, 4>(a, bf16, stream); return true;
-        case 8: score_dtype<D, 8>(a, bf16, stream); return true;
+        case 1: return score_dtype<D, 1>(a, bf16, mode, stream);
+        case 2: return score_dtype<D, 2>(a, bf16, mode, stream);
+        case 4: return score_dtype<D, 4>(a, bf16, mode, stream);
+        case 8: return score_dtype<D, 8>(a, bf16, mode, stream);
         default: return false;
     }
 }
 
-hipError_t launch_score(const ScoreArgs& a, int head_dim, int group, bool bf16, hipStream_t stream) {
+hipError_t launch_score(const ScoreArgs& a, int head_dim, int group, bool bf16, int mode, hipStream_t stream) {
     if ((int64_t)a.n_seg * a.n_chunks == 0) return hipSuccess;
-    TimedLaunch tl(KID_SCORE, stream);
-    bool ok = head_dim == 64 ? score_group<64>(a, group, bf16, stream)
-            : head_dim == 128 ? score_group<128>(a, group, bf16, stream) : false;
+    if (a.chunk % 512 || a.chunk > 2048) return hipErrorInvalidValue;
+    TimedLaunch tl(mode == SCORE_FALLBACK ? KID_SCORE_FALLBACK : KID_SCORE, stream);
+    const bool ok = head_dim == 64 ? score_group<64>(a, group, bf16, mode, stream)
+                  : head_dim == 128 ? score_group<128>(a, group, bf16, mode, stream) : false;
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -32,51 +32,153 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t x, uint32_t* wsum) 
     return x + before;
 }
 
+// Candidate lists of one segment (written by the scoring pass in candidate
+// mode) -> order keys and slots held in registers, in slot order: entry k sits
+// in register k / 1024 of thread k % 1024.  Returns the number of candidates,
+// or -1 when they do not fit in J * 1024 registers.
+// Block b (keys 32b .. 32b+31) was scored by wave w = (b mod bpc) mod 4 of chunk
+// c = b / bpc (bpc = chunk / 32 blocks per chunk), whose list (at
+// wave_list_base in the chunk's scratch rows) holds its blocks' candidates
+// block after block.  Two block scans give, per block, the rank of
+// its first candidate in slot order (pre) and, in the order of the wave lists,
+// the running count (lpos) from which its offset inside its list follows.
 template <int J, int G>
-__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
+__device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s, const int N, const ZParams<G>& z,
+                                               uint32_t (&key)[J], int32_t (&sl)[J], uint32_t* pre, uint32_t* lpos,
+                                               uint32_t* mw, uint32_t* wsum, uint32_t* bcast) {
+    const int tid = threadIdx.x;
+    const int nbk = (N + 31) / 32;                     // <= 2048 (N <= 65536)
+    const int bpc = a.chunk / 32, q4 = bpc / 4;
+    auto perm = [&](int b) {                           // block -> position in wave-list order
+        const int c = b / bpc, r = b - c * bpc;
+        return c * bpc + (r & 3) * q4 + (r >> 2);
+    };
+    const uint32_t* mp = a.masks + (int64_t)s * a.mask_stride;
+    const int b0 = 2 * tid, b1 = 2 * tid + 1;
+    const uint32_t m0 = b0 < nbk ? mp[b0] : 0u, m1 = b1 < nbk ? mp[b1] : 0u;
+    const uint32_t c0 = __popc(m0), c1 = __popc(m1);
+    mw[b0] = m0;
+    mw[b1] = m1;
+    lpos[b0] = 0u;
+    lpos[b1] = 0u;
+    const uint32_t inc = block_incl_scan(c0 + c1, wsum);     // (synchronises)
+    pre[b0] = inc - c0 - c1;
+    pre[b1] = inc - c1;
+    if (tid == kSelThreads - 1) bcast[0] = inc;
+    if (b0 < nbk) lpos[perm(b0)] = c0;
+    if (b1 < nbk) lpos[perm(b1)] = c1;
+    __syncthreads();
+    const uint32_t t0 = lpos[b0], t1 = lpos[b1];
+    const uint32_t inc2 = block_incl_scan(t0 + t1, wsum);
+    lpos[b0] = inc2 - t0 - t1;
+    lpos[b1] = inc2 - t1;
+    __syncthreads();
+    const int nc = (int)bcast[0];
+    if (nc > J * kSelThreads) return -1;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int k = j * kSelThreads + tid;
+        if (k < nc) {
+            int lo = 0, hi = nbk;                          // last block with pre <= k
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if ((int)pre[mid] <= k) lo = mid;
+                else hi = mid;
+            }
+            const int q = k - (int)pre[lo];
+            uint32_t m = mw[lo];
+            for (int i = 0; i < q; ++i) m &= m - 1u;
+            const int c = lo / bpc, r = lo - c * bpc;
+            const int head = c * bpc + (r & 3) * q4;
+            const int off = (int)(lpos[head + (r >> 2)] - lpos[head]) + q;
+            const int base = wave_list_base(r & 3, min(a.chunk, N - c * a.chunk));
+            const float* p = a.s_int + ((int64_t)s * a.cap + (int64_t)c * a.chunk + base + off) * G;
+            float S[G];
+            if constexpr (G % 4 == 0) {
+#pragma unroll
+                for (int g = 0; g < G; g += 4) {
+                    const float4 v = *reinterpret_cast<const float4*>(p + g);
+                    S[g] = v.x; S[g + 1] = v.y; S[g + 2] = v.z; S[g + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < G; ++g) S[g] = p[g];
+            }
+            key[j] = order_key(aggregate<G>(S, z));
+            sl[j] = 32 * lo + __builtin_ctz(m);
+        }
+        if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    return nc;
+}
+
+// Top-B of segment s.  MODE: SELECT_A reads aggregated scores, SELECT_S the
+// interleaved per-head scores and chunk statistics, SELECT_C the candidate
+// lists.  In mode C the result stands only if every key left out of the list
+// provably ranks below the cut: a key off the list has S_h < L_h for every
+// head, and the aggregate ((S - mu_hi) - mu_lo) * inv, max over heads, is
+// monotone in each S_h in fp32 as well, so its A is at most A(L); the cut T
+// (the B-th largest candidate) must then exceed A(L).  Otherwise the segment
+// goes on the fallback list and nothing is written for it here.
+template <int J, int G, int MODE>
+__device__ __forceinline__ void select_segment(const SelectArgs& a, const int s) {
+    constexpr bool CAND = MODE == SELECT_C;
+    constexpr int NB = CAND ? 2048 : 1;
+    constexpr int GZ = G > 0 ? G : 1;
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t wsum[kSelWaves];
     __shared__ uint32_t pick[2];
     __shared__ uint32_t cnt_gt[J * kSelWaves], cnt_eq[J * kSelWaves];
     __shared__ int32_t kept[kMaxBudget];
-    __shared__ double scratch[(kSelWaves + 1) * (G > 0 ? G : 1)];
+    __shared__ double scratch[(kSelWaves + 1) * GZ];
+    __shared__ uint32_t pre[NB], lpos[NB], mw[NB];
+    __shared__ uint32_t bcast[1];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-    const int s = blockIdx.x;
     const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
     const int B = a.budget;
     const bool all = N <= B;
 
     uint32_t key[J];
+    int32_t sl[CAND ? J : 1];
 #pragma unroll
     for (int j = 0; j < J; ++j) key[j] = 0u;
     uint32_t T = 0u;
     int need = 0;
+    int nv = N;                                         // register entries, in slot order
 
     if (!all) {
+        ZParams<GZ> z;
         if constexpr (G > 0) {
-            const ZParams<G> z = merge_stats<G, kSelThreads>(a.stats + (int64_t)s * a.n_chunks * G, a.n_chunks,
-                                                            a.chunk, N, scratch);
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int n = j * kSelThreads + tid;
-                if (n < N) {
-                    const float* p = a.s_int + ((int64_t)s * a.cap + n) * G;
-                    float S[G];
-                    if constexpr (G % 4 == 0) {
-#pragma unroll
-                        for (int g = 0; g < G; g += 4) {
-                            const float4 v = *reinterpret_cast<const float4*>(p + g);
-                            S[g] = v.x; S[g + 1] = v.y; S[g + 2] = v.z; S[g + 3] = v.w;
-                        }
-                    } else {
-#pragma unroll
-                        for (int g = 0; g < G; ++g) S[g] = p[g];
-                    }
-                    key[j] = order_key(aggregate<G>(S, z));
+            z = merge_stats<G, kSelThreads>(a.stats + (int64_t)s * a.n_chunks * G, a.n_chunks, a.chunk, N, scratch);
+            if constexpr (CAND) {
+                nv = load_candidates<J, G>(a, s, N, z, key, sl, pre, lpos, mw, wsum, bcast);
+                if (nv < B) {                           // overflow (-1) or too few to hold the cut
+                    if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1)] = s;
+                    return;
                 }
-                // keep the scheduler from hoisting every key's loads at once
-                if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+            } else {
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const int n = j * kSelThreads + tid;
+                    if (n < N) {
+                        const float* p = a.s_int + ((int64_t)s * a.cap + n) * G;
+                        float S[G];
+                        if constexpr (G % 4 == 0) {
+#pragma unroll
+                            for (int g = 0; g < G; g += 4) {
+                                const float4 v = *reinterpret_cast<const float4*>(p + g);
+                                S[g] = v.x; S[g + 1] = v.y; S[g + 2] = v.z; S[g + 3] = v.w;
+                            }
+                        } else {
+#pragma unroll
+                            for (int g = 0; g < G; ++g) S[g] = p[g];
+                        }
+                        key[j] = order_key(aggregate<G>(S, z));
+                    }
+                    // keep the scheduler from hoisting every key's loads at once
+                    if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+                }
             }
         } else {
 #pragma unroll
@@ -104,7 +206,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
 #pragma unroll
             for (int j = 0; j < J; ++j) {
                 const int n = j * kSelThreads + tid;
-                if (n < N && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+                if (n < nv && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
             }
             __syncthreads();
             // Thread t owns bins 2047-2t and 2046-2t: a scan in thread order is a
@@ -129,14 +231,26 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
             __syncthreads();
         }
         T = prefix;
+
+        if constexpr (CAND) {
+            if (nv < N) {                               // certificate for the keys left out
+                float L[GZ];
+#pragma unroll
+                for (int g = 0; g < GZ; ++g) L[g] = a.thr[(int64_t)s * GZ + g];
+                if (!(T > order_key(aggregate<GZ>(L, z)))) {
+                    if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1)] = s;
+                    return;
+                }
+            }
+        }
     }
 
-    // ---- ordered emission: slot n = j*1024 + w*64 + lane, in (j, w, lane) order
+    // ---- ordered emission: entry k = j*1024 + w*64 + lane, in (j, w, lane) order
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int n = j * kSelThreads + tid;
-        const bool valid = n < N;
+        const bool valid = n < nv;
         const bool gt = valid && (all || key[j] > T);
         const bool eq = valid && !all && key[j] == T;
         const uint64_t bg = __ballot(gt), be = __ballot(eq);
@@ -161,7 +275,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int n = j * kSelThreads + tid;
-        const bool valid = n < N;
+        const bool valid = n < nv;
         const bool gt = valid && (all || key[j] > T);
         const bool eq = valid && !all && key[j] == T;
         const uint64_t bg = __ballot(gt), be = __ballot(eq);
@@ -169,8 +283,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
         const int gb = (int)cnt_gt[j * kSelWaves + w] + __popcll(bg & below);
         const int out = gb + min(eb, need);
         if ((gt || (eq && eb < need)) && out < nk) {
-            if (a.gather) kept[out] = n;
-            else a.idx_out[(int64_t)s * a.idx_stride + out] = n;
+            int slot = n;
+            if constexpr (CAND) slot = all ? n : sl[j];
+            if (a.gather) kept[out] = slot;
+            else a.idx_out[(int64_t)s * a.idx_stride + out] = slot;
         }
     }
     if (a.n_kept && tid == 0) a.n_kept[s] = nk;
@@ -194,28 +310,69 @@ __global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
         a.dst.pos[a.dst.row(s, jrow)] = a.src.pos[a.src.row(s, kept[jrow])];
 }
 
+template <int J, int G, int MODE>
+__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
+    select_segment<J, G, MODE>(a, blockIdx.x);
+}
+
+// Mode S over the segments whose candidate pass failed its certificate.
+template <int J, int G>
+__global__ __launch_bounds__(kSelThreads) void k_select_fallback(SelectArgs a) {
+    const int n = *a.fb_count;
+    for (int i = blockIdx.x; i < n; i += gridDim.x) {
+        __syncthreads();                                // LDS of the previous segment is no longer read
+        select_segment<J, G, SELECT_S>(a, a.fb_list[i]);
+    }
+}
+
+template <int J, int G>
+static void select_launch(const SelectArgs& a, int mode, hipStream_t stream) {
+    const dim3 block(kSelThreads);
+    if (mode == SELECT_S_FALLBACK) {
+        if constexpr (G > 0)
+            hipLaunchKernelGGL((k_select_fallback<J, G>), dim3((unsigned)(a.n_seg < 512 ? a.n_seg : 512)), block, 0, stream, a);
+        return;
+    }
+    const dim3 grid((unsigned)a.n_seg);
+    if constexpr (G == 0) hipLaunchKernelGGL((k_select<J, 0, SELECT_A>), grid, block, 0, stream, a);
+    else if (mode == SELECT_C) hipLaunchKernelGGL((k_select<J, G, SELECT_C>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_select<J, G, SELECT_S>), grid, block, 0, stream, a);
+}
+
 template <int J>
-static bool select_group(const SelectArgs& a, int group, hipStream_t stream) {
-    const dim3 grid((unsigned)a.n_seg), block(kSelThreads);
+static bool select_group(const SelectArgs& a, int group, int mode, hipStream_t stream) {
+    if ((group == 0) != (mode == SELECT_A)) return false;
     switch (group) {
-        case 0: hipLaunchKernelGGL((k_select<J, 0>), grid, block, 0, stream, a); return true;
-        case 1: hipLaunchKernelGGL((k_select<J, 1>), grid, block, 0, stream, a); return true;
-        case 2: hipLaunchKernelGGL((k_select<J, 2>), grid, block, 0, stream, a); return true;
-        case 4: hipLaunchKernelGGL((k_select<J, 4>), grid, block, 0, stream, a); return true;
-        case 8: hipLaunchKernelGGL((k_select<J, 8>), grid, block, 0, stream, a); return true;
+        case 0: select_launch<J, 0>(a, mode, stream); return true;
+        case 1: select_launch<J, 1>(a, mode, stream); return true;
+        case 2: select_launch<J, 2>(a, mode, stream); return true;
+        case 4: select_launch<J, 4>(a, mode, stream); return true;
+        case 8: select_launch<J, 8>(a, mode, stream); return true;
         default: return false;
     }
 }
 
-hipError_t launch_select(const SelectArgs& a, int group, int64_t max_len, hipStream_t stream) {
+hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_len, hipStream_t stream) {
     if (a.n_seg == 0) return hipSuccess;
     if (a.budget > kMaxBudget || max_len > 64 * kSelThreads) return hipErrorInvalidValue;
-    TimedLaunch tl(a.gather ? KID_SELECT_GATHER : KID_SELECT, stream);
+    int64_t held = max_len;                             // entries one thread block holds in registers
+    if (mode == SELECT_C) {
+        // every key of a segment outside candidate mode (N < max(4096, 8B)), or
+        // half of the longest segment's keys (the expected candidates are 2.5 B/N
+        // of them, at most 5/16); a longer list falls back to mode S
+        const int64_t small = 8 * (int64_t)a.budget > 4096 ? 8 * (int64_t)a.budget : 4096;
+        const int64_t half = (max_len + 1) / 2 > small ? (max_len + 1) / 2 : small;
+        held = half < max_len ? half : max_len;
+        if (a.chunk % 512 || a.chunk > 2048) return hipErrorInvalidValue;
+    }
+    const KernelId id = mode == SELECT_S_FALLBACK ? KID_SELECT_FALLBACK : a.gather ? KID_SELECT_GATHER : KID_SELECT;
+    TimedLaunch tl(id, stream);
     bool ok;
-    if (max_len <= 2 * kSelThreads) ok = select_group<2>(a, group, stream);
-    else if (max_len <= 8 * kSelThreads) ok = select_group<8>(a, group, stream);
-    else if (max_len <= 32 * kSelThreads) ok = select_group<32>(a, group, stream);
-    else ok = select_group<64>(a, group, stream);
+    if (held <= 2 * kSelThreads) ok = select_group<2>(a, group, mode, stream);
+    else if (held <= 8 * kSelThreads) ok = select_group<8>(a, group, mode, stream);
+    else if (mode == SELECT_C && held <= 16 * kSelThreads) ok = select_group<16>(a, group, mode, stream);
+    else if (held <= 32 * kSelThreads) ok = select_group<32>(a, group, mode, stream);
+    else ok = select_group<64>(a, group, mode, stream);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -30,6 +30,7 @@ EXPORTS = (
     "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
     "tri_compact", "tri_prune_window", "tri_append", "tri_decode_attn", "tri_strerror",
     "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name", "tri_last_error",
+    "tri_prune_fallbacks",
 )
 
 
@@ -65,6 +66,7 @@ def load():
                            "(run python -m long_reasoning_decode_amd.build)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, I64, D, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float
+    I32 = ctypes.c_int32
     SZ = ctypes.c_size_t
     DP = ctypes.POINTER(CacheDesc)
     sig = {
@@ -83,6 +85,7 @@ def load():
         "tri_timing_read": [I, ctypes.POINTER(I64), ctypes.POINTER(D)],
         "tri_timing_name": [I],
         "tri_last_error": [],
+        "tri_prune_fallbacks": [P, SZ, ctypes.POINTER(I32), P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -213,6 +216,13 @@ def tri_prune_window(calib, src, t, budget, dst, n_kept, ws, stream=None):
     rc = load().tri_prune_window(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
                                  _p(n_kept), _p(ws), ws.numel(), _stream(stream))
     _check("tri_prune_window", rc)
+
+
+def tri_prune_fallbacks(ws, stream=None):
+    """Segments the last tri_prune_window on `ws` redid over all keys (synchronising)."""
+    n = ctypes.c_int32(0)
+    _check("tri_prune_fallbacks", load().tri_prune_fallbacks(_p(ws), ws.numel(), ctypes.byref(n), _stream(stream)))
+    return n.value
 
 
 def tri_append(desc, k_new, v_new, pos_new, stream=None):

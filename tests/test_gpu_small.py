@@ -39,9 +39,10 @@ def _run_unfused(T, cfg, g, calib, B):
     out2 = empty_like_dense(g, B)
     nk2 = torch.full((n_seg,), -1, dtype=torch.int32, device="cuda")
     T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out2), nk2, ws)
+    fallbacks = T.tri_prune_fallbacks(ws)
     torch.cuda.synchronize()
     return dict(scores=scores.cpu(), agg=agg.cpu(), ms=ms.cpu(), idx=idx.cpu(), nk=nk.cpu(), out=_to(out, "cpu"),
-                out2=_to(out2, "cpu"), nk2=nk2.cpu())
+                out2=_to(out2, "cpu"), nk2=nk2.cpu(), fallbacks=fallbacks)
 
 
 def _check_all(cfg, cal, cpu, r, B, lengths, what):
@@ -252,3 +253,65 @@ def test_decode_loop_small(gpu_lib):
             check_compaction(K, V, P, stored(nxt["k"][s, :nks].cpu()), stored(nxt["v"][s, :nks].cpu()), Pd, ix)
         nxt["t"] = c["t"]
         cur = 1 - cur
+
+
+# ---------------------------------------------------------------- candidate pass
+# bf16 segments with N >= 4096 and N >= 8B run the fused pass on candidate lists
+# (keys reaching a sampled per-head threshold) with a certificate and a full
+# fallback; the result must equal the unfused chain byte for byte.
+
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 8), (128, 1), (64, 2)])
+def test_candidate_pass_every_step(gpu_lib, d, G):
+    """Lengths around the candidate-mode boundaries (4096 and 8B), ragged tails."""
+    T = gpu_lib
+    B = 600
+    cap = 12000
+    cfg = W.CONFIGS["tiny"].replace(head_dim=d, group=G, dtype=torch.bfloat16, theta=1e6, n_kv_heads=3, n_seq=3,
+                                    n_keys=cap, t=cap + 3, budget=B, sigma=None, seed=11)
+    log(f"case candidate pass d={d} G={G}")
+    cpu = W.dense_cache(cfg, "cpu")
+    lengths = torch.tensor([cap, 4095, 4096, 8 * B - 1, 8 * B, 8 * B + 1, 9001, B + 1, cap - 17], dtype=torch.int32)
+    cpu["lengths"] = lengths
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
+    log(f"  fallbacks: {r['fallbacks']}")
+    assert r["fallbacks"] == 0
+    _check_all(cfg, cal, cpu, r, B, lengths.numpy(), f"candidate d{d} G{G}")
+
+
+def test_candidate_pass_fallback_redoes_segment(gpu_lib):
+    """Segment 0's sampled keys are scaled up 4x, so its thresholds sit far
+    above the rest of its keys: too few candidates, the certificate fails and
+    the segment is redone over every key.  Segment 1 is ordinary."""
+    T = gpu_lib
+    B = 300
+    cap = 8192
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, group=4, dtype=torch.bfloat16, theta=1e6, n_kv_heads=2, n_seq=1,
+                                    n_keys=cap, t=cap, budget=B, sigma=None, seed=5)
+    log("case candidate fallback")
+    cpu = W.dense_cache(cfg, "cpu")
+    sampled = (torch.arange(256) * cap) // 256
+    cpu["k"][0, sampled] = cpu["k"][0, sampled] * 4           # exact in bf16
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
+    log(f"  fallbacks: {r['fallbacks']}")
+    assert r["fallbacks"] == 1
+    _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), "fallback")
+
+
+def test_candidate_pass_equal_scores(gpu_lib):
+    """All keys identical in candidate mode (N = 8B): the sample has no spread,
+    so every key is a candidate (N of them, which the select step can hold),
+    and the kept set is the lowest B slots."""
+    T = gpu_lib
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, dtype=torch.bfloat16, theta=1e6, n_keys=9000, t=9000, budget=1125)
+    log("case candidate equal scores")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["k"][0, :] = cpu["k"][0, 5]
+    cpu["v"][0, :] = torch.arange(9000, dtype=torch.float32)[:, None].to(torch.bfloat16)
+    cpu["pos"][0, :] = 5
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, cfg.budget)
+    assert r["fallbacks"] == 0
+    assert torch.equal(r["out2"]["v"][0], cpu["v"][0, :1125])
+    _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "candidate equal")
