@@ -234,6 +234,111 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitLgkm0 = 0xC07F;
 
+// B fragments of one segment's G query heads for v_mfma_f32_16x16x32_bf16:
+// column 16t + (lane % 16) is (split q, head h) = ((16t + lane%16) / G, % G),
+// k-slot (lane / 16, e); trig fragments cover the head_dim row elements,
+// norm fragments the F bands.  Coefficients are carried as three bf16 parts.
+template <int D, int G>
+__device__ __forceinline__ void mfma_coef_fragments(const float* ctab, const float* wtab, const SegShape& shape,
+                                                    int n_q_heads, int s, bf16x8_t (&bt)[D / 32][(3 * G + 15) / 16],
+                                                    bf16x8_t (&bn)[D / 64][(3 * G + 15) / 16]) {
+    constexpr int F = D / 2, TS = D / 32, NS = F / 32, NCOL = 3 * G, NT = (NCOL + 15) / 16;
+    const int lane = threadIdx.x & 63, row = lane & 15, grp = lane >> 4;
+    const int l = shape.layer(s), b = shape.seq(s), hk = shape.head(s);
+    const float* cb = ctab + ((int64_t)(l * shape.n_seq + b) * n_q_heads + hk * G) * D;
+    const float* wb = wtab + ((int64_t)l * n_q_heads + hk * G) * F;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int jg = 16 * t + row;
+        const bool used = jg < NCOL;
+        const int q = jg / G, h = jg % G;
+#pragma unroll
+        for (int st = 0; st < TS; ++st) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int d0 = 32 * st + 8 * grp + 2 * e2;
+                const uint32_t lo = used ? bf16_split3(cb[h * D + d0], q) : 0u;
+                const uint32_t hi = used ? bf16_split3(cb[h * D + d0 + 1], q) : 0u;
+                w[e2] = lo | (hi << 16);
+            }
+            bt[st][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int f0 = 32 * st + 8 * grp + 2 * e2;
+                const uint32_t lo = used ? bf16_split3(wb[h * F + f0], q) : 0u;
+                const uint32_t hi = used ? bf16_split3(wb[h * F + f0 + 1], q) : 0u;
+                w[e2] = lo | (hi << 16);
+            }
+            bn[st][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+    }
+}
+
+// Scores of one 16-key tile.  av[st] is lane (grp, row)'s A fragment: the
+// 16-byte chunk 4*st + grp of key row `row`.  On return, lanes with
+// row < G hold S_row of keys 4*grp + r in S4[r].
+template <int D, int G>
+__device__ __forceinline__ void mfma_tile_scores(const uint4 (&av)[D / 32],
+                                                 const bf16x8_t (&bt)[D / 32][(3 * G + 15) / 16],
+                                                 const bf16x8_t (&bn)[D / 64][(3 * G + 15) / 16], float (&S4)[4]) {
+    constexpr int TS = D / 32, NS = D / 64, NT = (3 * G + 15) / 16;
+    const int lane = threadIdx.x & 63, row = lane & 15;
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int st = 0; st < TS; ++st)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[st]), bt[st][t], acc[t], 0,
+                                                             0, 0);
+    // |k_f|: the band's real and imaginary parts sit in the same lane and slot
+    // of fragments st and st + NS; fed as a bf16 hi + lo pair
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const uint4 rv = av[st], iv = av[st + NS];
+        const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w}, iw[4] = {iv.x, iv.y, iv.z, iv.w};
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const float r0 = bf16_lo(rw[e2]), r1 = bf16_hi(rw[e2]);
+            const float i0 = bf16_lo(iw[e2]), i1 = bf16_hi(iw[e2]);
+            const float m0 = __builtin_amdgcn_sqrtf(fmaf(r0, r0, i0 * i0));
+            const float m1 = __builtin_amdgcn_sqrtf(fmaf(r1, r1, i1 * i1));
+            const bf16x2_t hp = __builtin_convertvector(f32x2_t{m0, m1}, bf16x2_t);
+            const uint32_t hb = __builtin_bit_cast(uint32_t, hp);
+            const f32x2_t res = {m0 - bf16_lo(hb), m1 - bf16_hi(hb)};
+            hw[e2] = hb;
+            lw[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(res, bf16x2_t));
+        }
+        const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        const bf16x8_t al = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bn[st][t], acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bn[st][t], acc[t], 0, 0, 0);
+        }
+    }
+    // lane (grp, row) holds rows 4*grp + r of column row; add the three split
+    // columns of head `row`
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float v = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            const int t = (q * G) / 16;
+            const int src = (lane & 48) | ((q * G + row) & 15);
+            v += __shfl(acc[t][r], src, kWave);
+        }
+        S4[r] = v;
+    }
+}
+
 // Candidate records are staged per wave and leave in groups of kFlush records
 // (kFlush * G floats, whole 128-byte lines).
 constexpr int kFlush = 32;
@@ -288,43 +393,9 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
         list = a.s_int + ((int64_t)s * a.cap + start + wave_list_base(wave, cnt)) * G;
     }
 
-    // loop-invariant B fragments: column row -> (q, h), k-slot (grp, e)
+    // loop-invariant B fragments
     bf16x8_t bt[TS][NT], bn[NS][NT];
-    {
-        const int l = a.shape.layer(s), b = a.shape.seq(s), hk = a.shape.head(s);
-        const float* cb = a.ctab + ((int64_t)(l * a.shape.n_seq + b) * a.n_q_heads + hk * G) * D;
-        const float* wb = a.wtab + ((int64_t)l * a.n_q_heads + hk * G) * F;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int jg = 16 * t + row;
-            const bool used = jg < NCOL;
-            const int q = jg / G, h = jg % G;
-#pragma unroll
-            for (int st = 0; st < TS; ++st) {
-                uint32_t w[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int d0 = 32 * st + 8 * grp + 2 * e2;
-                    const uint32_t lo = used ? bf16_split3(cb[h * D + d0], q) : 0u;
-                    const uint32_t hi = used ? bf16_split3(cb[h * D + d0 + 1], q) : 0u;
-                    w[e2] = lo | (hi << 16);
-                }
-                bt[st][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-            }
-#pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                uint32_t w[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int f0 = 32 * st + 8 * grp + 2 * e2;
-                    const uint32_t lo = used ? bf16_split3(wb[h * F + f0], q) : 0u;
-                    const uint32_t hi = used ? bf16_split3(wb[h * F + f0 + 1], q) : 0u;
-                    w[e2] = lo | (hi << 16);
-                }
-                bn[st][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-            }
-        }
-    }
+    mfma_coef_fragments<D, G>(a.ctab, a.wtab, a.shape, a.n_q_heads, s, bt, bn);
 
     // per-lane running statistics for head `row` (lanes row < G), shifted by
     // the lane's first score
@@ -362,54 +433,8 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
 #pragma unroll
         for (int u = 0; u < UT; ++u) {
             if (tb + u >= n_tiles) break;
-            f32x4_t acc[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int st = 0; st < TS; ++st)
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u][st]),
-                                                                     bt[st][t], acc[t], 0, 0, 0);
-#pragma unroll
-            for (int st = 0; st < NS; ++st) {
-                const uint4 rv = av[u][st], iv = av[u][st + NS];
-                const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w}, iw[4] = {iv.x, iv.y, iv.z, iv.w};
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const float r0 = bf16_lo(rw[e2]), r1 = bf16_hi(rw[e2]);
-                    const float i0 = bf16_lo(iw[e2]), i1 = bf16_hi(iw[e2]);
-                    const float m0 = __builtin_amdgcn_sqrtf(fmaf(r0, r0, i0 * i0));
-                    const float m1 = __builtin_amdgcn_sqrtf(fmaf(r1, r1, i1 * i1));
-                    const bf16x2_t hp = __builtin_convertvector(f32x2_t{m0, m1}, bf16x2_t);
-                    const uint32_t hb = __builtin_bit_cast(uint32_t, hp);
-                    const f32x2_t res = {m0 - bf16_lo(hb), m1 - bf16_hi(hb)};
-                    hw[e2] = hb;
-                    lw[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(res, bf16x2_t));
-                }
-                const bf16x8_t ah = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-                const bf16x8_t al = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bn[st][t], acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bn[st][t], acc[t], 0, 0, 0);
-                }
-            }
-            // lane (grp, row) holds rows 4*grp + r of column row; add the three
-            // split columns of head `row` (lanes row < G keep the result)
             float S4[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 3; ++q) {
-                    const int t = (q * G) / 16;
-                    const int src = (lane & 48) | ((q * G + row) & 15);
-                    v += __shfl(acc[t][r], src, kWave);
-                }
-                S4[r] = v;
-            }
+            mfma_tile_scores<D, G>(av[u], bt, bn, S4);
             const int tile0 = (tb + u) * 16;
             const int tslot = CAND ? 16 * u : 0;      // candidate mode keeps the stage's two tiles
             if (row < G) {
@@ -544,22 +569,19 @@ __global__ __launch_bounds__(256) void k_score_mfma_fallback(ScoreArgs a) {
 // none of them can be among the B kept (else the segment is redone in full).
 // The thresholds only decide how much work is skipped, never the result.
 constexpr int kSample = 256;
+static_assert(kSample <= 256, "sample index fits the low 8 bits of a rank key");
 constexpr int kCandMul = 3;
 
 template <int D, int G>
 __global__ __launch_bounds__(kSample) void k_sample(SampleArgs a) {
-    constexpr int F = D / 2;
-    constexpr int CPR = D / 8;               // 16-byte chunks per row
-    constexpr int HC = CPR / 2;              // chunks per half row (8 bands each)
-    constexpr int RPI = kWave / CPR;         // rows per wave load
-    constexpr int IT = kSample / 4 / RPI;    // loads per lane
-    __shared__ float cf[G][D];
-    __shared__ float wf[G][F];
+    constexpr int TS = D / 32, NS = D / 64, NT = (3 * G + 15) / 16;
+    constexpr int TPW = kSample / 4 / 16;    // 16-key tiles per wave
     __shared__ float sS[kSample][G];
-    __shared__ float ah[kSample];
+    __shared__ __align__(16) uint32_t ak[kSample];
     __shared__ float red[kSample / kWave][G];
     __shared__ float tau_s;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int row = lane & 15, grp = lane >> 4;
     const int s = blockIdx.x;
     if (s == 0 && tid == 0) *a.fb_count = 0;
     const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
@@ -568,55 +590,28 @@ __global__ __launch_bounds__(kSample) void k_sample(SampleArgs a) {
         if (tid < G) thr[tid] = -__builtin_inff();
         return;
     }
-    const int l = a.shape.layer(s), b = a.shape.seq(s), hk = a.shape.head(s);
-    const float* cb = a.ctab + ((int64_t)(l * a.shape.n_seq + b) * a.n_q_heads + hk * G) * D;
-    const float* wb = a.wtab + ((int64_t)l * a.n_q_heads + hk * G) * F;
-    for (int i = tid; i < G * D; i += kSample) cf[i / D][i % D] = cb[i];
-    for (int i = tid; i < G * F; i += kSample) wf[i / F][i % F] = wb[i];
-
-    // sample j = w * (kSample/4) + it * RPI + lane / CPR sits at slot j*N/kSample;
-    // its CPR lanes read the row's 16-byte chunks side by side
-    const int sub = lane % CPR, rr = lane / CPR;
-    uint4 v[IT];
+    // Sample j = 64 w + 16 u + row sits in stratum j of N/kSample keys, at an
+    // offset that varies with j and the segment.  Its scores come from the same
+    // tile contraction as the scoring pass, so they are the exact fp32 scores.
+    const int stride = N / kSample;           // >= 16 in candidate mode
+    uint4 av[TPW][TS];
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int j = w * (kSample / 4) + it * RPI + rr;
-        const int slot = (int)(((int64_t)j * N) / kSample);
-        v[it] = reinterpret_cast<const uint4*>(a.kv.k + a.kv.row(s, slot) * (D * 2))[sub];
+    for (int u = 0; u < TPW; ++u) {
+        const int j = w * (kSample / 4) + 16 * u + row;
+        const int slot = j * stride + (int)(((uint32_t)j * 2654435761u + (uint32_t)s * 40503u) >> 8) % stride;
+        const uint4* rp = reinterpret_cast<const uint4*>(a.kv.k + a.kv.row(s, slot) * (D * 2));
+#pragma unroll
+        for (int st = 0; st < TS; ++st) av[u][st] = rp[4 * st + grp];
     }
-    __syncthreads();                          // coefficients are in LDS
+    bf16x8_t bt[TS][NT], bn[NS][NT];
+    mfma_coef_fragments<D, G>(a.ctab, a.wtab, a.shape, a.n_q_heads, s, bt, bn);
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        // lanes sub < HC hold 8 bands' real parts; the imaginary parts are HC lanes up
-        uint4 iv;
-        iv.x = __shfl(v[it].x, lane + HC, kWave);
-        iv.y = __shfl(v[it].y, lane + HC, kWave);
-        iv.z = __shfl(v[it].z, lane + HC, kWave);
-        iv.w = __shfl(v[it].w, lane + HC, kWave);
-        float acc[G];
+    for (int u = 0; u < TPW; ++u) {
+        float S4[4];
+        mfma_tile_scores<D, G>(av[u], bt, bn, S4);
+        if (row < G) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) acc[g] = 0.0f;
-        if (sub < HC) {
-            const uint32_t rw[4] = {v[it].x, v[it].y, v[it].z, v[it].w}, iw[4] = {iv.x, iv.y, iv.z, iv.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int f = 8 * sub + e;
-                const float re = (e & 1) ? bf16_hi(rw[e >> 1]) : bf16_lo(rw[e >> 1]);
-                const float im = (e & 1) ? bf16_hi(iw[e >> 1]) : bf16_lo(iw[e >> 1]);
-                const float mg = sqrtf(fmaf(re, re, im * im));
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    acc[g] = fmaf(cf[g][f], re, fmaf(cf[g][f + F], im, fmaf(wf[g][f], mg, acc[g])));
-            }
-        }
-#pragma unroll
-        for (int m = 1; m < HC; m <<= 1)
-#pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] += __shfl_xor(acc[g], m, kWave);
-        if (sub == 0) {
-            const int j = w * (kSample / 4) + it * RPI + rr;
-#pragma unroll
-            for (int g = 0; g < G; ++g) sS[j][g] = acc[g];
+            for (int r = 0; r < 4; ++r) sS[w * (kSample / 4) + 16 * u + 4 * grp + r][row] = S4[r];
         }
     }
     __syncthreads();
@@ -654,16 +649,22 @@ __global__ __launch_bounds__(kSample) void k_sample(SampleArgs a) {
         sg[g] = sqrtf(t / kSample);
         A = fmaxf(A, sg[g] > 0.0f ? (S[g] - mu[g]) / sg[g] : 0.0f);
     }
-    ah[tid] = A;
-    if (tid == 0) tau_s = -__builtin_inff();   // (every rank is taken once; NaN scores are unsupported)
+    // Distinct ordered keys: the sample index replaces the low 8 bits of the
+    // order-preserving pattern of A (a relative change below 2^-15, immaterial
+    // for a threshold), so a rank is one unsigned compare per sample.
+    const uint32_t mykey = (order_key(A) & ~0xFFu) | (uint32_t)(kSample - 1 - tid);
+    ak[tid] = mykey;
+    if (tid == 0) tau_s = -__builtin_inff();   // (every rank is taken once)
     __syncthreads();
     // tau = the r-th largest sample aggregate, r = ceil(kCandMul B kSample / N)
     const int64_t r64 = ((int64_t)kCandMul * a.budget * kSample + N - 1) / N;
     const int r = (int)(r64 < 1 ? 1 : r64 > kSample ? kSample : r64);
     int rank = 0;
-    for (int j = 0; j < kSample; ++j) {
-        const float v2 = ah[j];
-        rank += (v2 > A) || (v2 == A && j < tid);
+    const uint4* ak4 = reinterpret_cast<const uint4*>(ak);
+#pragma unroll 8
+    for (int j4 = 0; j4 < kSample / 4; ++j4) {
+        const uint4 q = ak4[j4];
+        rank += (q.x > mykey) + (q.y > mykey) + (q.z > mykey) + (q.w > mykey);
     }
     if (rank == r - 1) tau_s = A;
     __syncthreads();

@@ -279,6 +279,13 @@ def test_candidate_pass_every_step(gpu_lib, d, G):
     _check_all(cfg, cal, cpu, r, B, lengths.numpy(), f"candidate d{d} G{G}")
 
 
+def _sampled_slots(N, s, n_sample=256):
+    """Slots the threshold sample of segment s reads: one per stratum of
+    N // n_sample keys, at a hashed offset (the kernel's stratified rule)."""
+    stride = N // n_sample
+    return [j * stride + (((j * 2654435761 + s * 40503) & 0xFFFFFFFF) >> 8) % stride for j in range(n_sample)]
+
+
 def test_candidate_pass_fallback_redoes_segment(gpu_lib):
     """Segment 0's sampled keys are scaled up 4x, so its thresholds sit far
     above the rest of its keys: too few candidates, the certificate fails and
@@ -290,7 +297,7 @@ def test_candidate_pass_fallback_redoes_segment(gpu_lib):
                                     n_keys=cap, t=cap, budget=B, sigma=None, seed=5)
     log("case candidate fallback")
     cpu = W.dense_cache(cfg, "cpu")
-    sampled = (torch.arange(256) * cap) // 256
+    sampled = torch.tensor(_sampled_slots(cap, 0))
     cpu["k"][0, sampled] = cpu["k"][0, sampled] * 4           # exact in bf16
     calib, cal = calib_for(T, cfg)
     r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
@@ -315,3 +322,21 @@ def test_candidate_pass_equal_scores(gpu_lib):
     assert r["fallbacks"] == 0
     assert torch.equal(r["out2"]["v"][0], cpu["v"][0, :1125])
     _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "candidate equal")
+
+
+def test_candidate_pass_overflow_falls_back(gpu_lib):
+    """All keys identical with N > 8B: every key is a candidate, more than the
+    select step holds for this budget (max(N/2, 8B) = 7200 < 9000), so the
+    segment is redone in full; the kept set is the lowest B slots."""
+    T = gpu_lib
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, dtype=torch.bfloat16, theta=1e6, n_keys=9000, t=9000, budget=900)
+    log("case candidate overflow")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["k"][0, :] = cpu["k"][0, 5]
+    cpu["v"][0, :] = torch.arange(9000, dtype=torch.float32)[:, None].to(torch.bfloat16)
+    cpu["pos"][0, :] = 5
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, cfg.budget)
+    assert r["fallbacks"] == 1
+    assert torch.equal(r["out2"]["v"][0], cpu["v"][0, :900])
+    _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "candidate overflow")
