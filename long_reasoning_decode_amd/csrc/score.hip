@@ -339,10 +339,9 @@ __device__ __forceinline__ void mfma_tile_scores(const uint4 (&av)[D / 32],
     }
 }
 
-// Candidate records are staged per wave and leave in groups of kFlush records
-// (kFlush * G floats, whole 128-byte lines).
-constexpr int kFlush = 32;
 constexpr int kMaxChunkBlocks = 2048 / 32;   // 32-key mask words per chunk
+// LDS per scoring workgroup that still lets four of them share a CU.
+constexpr int kScoreLds = 40960;
 
 // Scores chunk c of segment s.  CAND = false: every key's G scores go to the
 // interleaved scratch (and/or the head-major output).  CAND = true: only keys
@@ -369,11 +368,19 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
     // 128), with the non-temporal hint; chunk lc of stage key k sits at chunk
     // position lc ^ (k mod CPR) so the fragment reads below are conflict-free.
     static_assert(SKEYS == 32, "one stage is one 32-key mask block");
+    // Candidate mode: each wave keeps its records (G floats per candidate, in
+    // slot order) in LDS and writes them out only when the buffer cannot take
+    // another stage, and at the end of the chunk.  Stores share the wait
+    // counter with the staging DMA, so every store in the stream delays the
+    // wave's next stage; the buffer takes whatever LDS four workgroups per CU
+    // leave (118 records per wave for head_dim 128, G = 4).
+    constexpr int FIXED = (int)sizeof(uint4) * 4 * SKEYS * CPR + 4 * G * 3 * 8 + kMaxChunkBlocks * 4;
+    constexpr int CAPR0 = (kScoreLds - FIXED) / (4 * G * 4);
+    constexpr int CAPR = CAND ? (CAPR0 > 64 ? CAPR0 : 64) : 1;   // records per wave buffer
     __shared__ uint4 stage[4][SKEYS * CPR];
-    // one tile's scores (one stage's in candidate mode), key-major
-    __shared__ float tileS[4][(CAND ? 32 : 16) * G];
+    __shared__ float tileS[CAND ? 1 : 4][CAND ? 1 : 16 * G];      // one tile's scores, key-major
     __shared__ double part[4][G][3];
-    __shared__ float cbuf[CAND ? 4 : 1][CAND ? (kFlush + 32) * G : 1];
+    __shared__ float cbuf[CAND ? 4 : 1][CAND ? CAPR * G : 1];
     __shared__ uint32_t maskbuf[CAND ? kMaxChunkBlocks : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -416,6 +423,21 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
             __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + 64 * i), 16, 0, 2 /* nt */);
         }
     };
+    // all nb buffered records -> list[nw ..]
+    auto flush_records = [&]() {
+        if constexpr (CAND) {
+            if constexpr (G % 4 == 0) {
+                for (int i = 4 * lane; i < nb * G; i += 4 * kWave)
+                    *reinterpret_cast<float4*>(list + (int64_t)nw * G + i) =
+                        *reinterpret_cast<const float4*>(&cbuf[wave][i]);
+            } else {
+                for (int i = lane; i < nb * G; i += kWave) list[(int64_t)nw * G + i] = cbuf[wave][i];
+            }
+            nw += nb;
+            nb = 0;
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
     if (wave * UT < n_tiles) issue_stage(wave * UT);
     for (int tb = wave * UT; tb < n_tiles; tb += 4 * UT) {
         uint4 av[UT][TS];
@@ -430,18 +452,22 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                    // fragments are in registers
         __builtin_amdgcn_wave_barrier();
         if (tb + 4 * UT < n_tiles) issue_stage(tb + 4 * UT);       // next stage loads under this compute
+        if constexpr (CAND) {
+            if (nb + SKEYS > CAPR) flush_records();                  // no room to stage this stage's scores
+        }
 #pragma unroll
         for (int u = 0; u < UT; ++u) {
             if (tb + u >= n_tiles) break;
             float S4[4];
             mfma_tile_scores<D, G>(av[u], bt, bn, S4);
             const int tile0 = (tb + u) * 16;
-            const int tslot = CAND ? 16 * u : 0;      // candidate mode keeps the stage's two tiles
             if (row < G) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = tile0 + 4 * grp + r;
-                    tileS[wave][(tslot + 4 * grp + r) * G + row] = S4[r];
+                    // candidate mode: the stage's 32 keys are staged after the kept records
+                    if constexpr (CAND) cbuf[wave][(nb + 16 * u + 4 * grp + r) * G + row] = S4[r];
+                    else tileS[wave][(4 * grp + r) * G + row] = S4[r];
                     if (key < cnt) {
                         if (cntl == 0) shift = S4[r];
                         const float dv = S4[r] - shift;
@@ -468,7 +494,7 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
                     for (int g = 0; g < G; ++g) o[g] = tileS[wave][lane * G + g];
                 }
             }
-            if (a.s_raw) {
+            if (!CAND && a.s_raw) {
                 for (int i = lane; i < 16 * G; i += kWave) {
                     const int h = i / 16, k = i % 16;
                     if (tile0 + k < cnt) a.s_raw[((int64_t)s * G + h) * a.cap + start + tile0 + k] = tileS[wave][k * G + h];
@@ -477,41 +503,33 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
             __builtin_amdgcn_wave_barrier();
         }
         if constexpr (CAND) {
-            // lanes 0..31: is key tb*16 + lane a candidate (some S_h >= L_h)?
+            // lanes 0..31: is staged key tb*16 + lane a candidate (some S_h >= L_h)?
+            // Candidates move down onto the kept records (reads before writes).
             const int key0 = tb * 16;
+            float rec[G];
             bool isc = false;
-            if (lane < 32 && key0 + lane < cnt) {
+            if (lane < 32) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) isc |= tileS[wave][lane * G + g] >= thr[g];
+                for (int g = 0; g < G; ++g) rec[g] = cbuf[wave][(nb + lane) * G + g];
+                if (key0 + lane < cnt) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) isc |= rec[g] >= thr[g];
+                }
             }
             bmask = (uint32_t)__ballot(isc);
+            __builtin_amdgcn_wave_barrier();
             if (isc) {
                 const int p = nb + __popc(bmask & ((1u << lane) - 1u));
 #pragma unroll
-                for (int g = 0; g < G; ++g) cbuf[wave][p * G + g] = tileS[wave][lane * G + g];
+                for (int g = 0; g < G; ++g) cbuf[wave][p * G + g] = rec[g];
             }
             nb += __popc(bmask);
             if (lane == 0) maskbuf[tb / UT] = bmask;
             __builtin_amdgcn_wave_barrier();
-            if (nb >= kFlush) {
-                // kFlush records -> list[nw ..], whole lines; the rest moves to the front
-                if constexpr (G % 4 == 0) {
-                    for (int i = 4 * lane; i < kFlush * G; i += 4 * kWave)
-                        *reinterpret_cast<float4*>(list + (int64_t)nw * G + i) =
-                            *reinterpret_cast<const float4*>(&cbuf[wave][i]);
-                } else {
-                    for (int i = lane; i < kFlush * G; i += kWave) list[(int64_t)nw * G + i] = cbuf[wave][i];
-                }
-                __builtin_amdgcn_wave_barrier();
-                for (int i = lane; i < (nb - kFlush) * G; i += kWave) cbuf[wave][i] = cbuf[wave][kFlush * G + i];
-                nb -= kFlush;
-                nw += kFlush;
-            }
-            __builtin_amdgcn_wave_barrier();
         }
     }
     if constexpr (CAND) {
-        for (int i = lane; i < nb * G; i += kWave) list[(int64_t)nw * G + i] = cbuf[wave][i];
+        if (nb > 0) flush_records();
     }
 
     // merge the lane summaries of each head: across the 4 lane groups, then waves

@@ -42,9 +42,29 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t x, uint32_t* wsum) 
 // block after block.  Two block scans give, per block, the rank of
 // its first candidate in slot order (pre) and, in the order of the wave lists,
 // the running count (lpos) from which its offset inside its list follows.
+// Block of candidate k (the last block whose first candidate rank is <= k) and
+// k's rank q inside it.
+__device__ __forceinline__ void cand_block(int k, int nbk, const uint32_t* pre, int& b, int& q) {
+    int lo = 0, hi = nbk;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)pre[mid] <= k) lo = mid;
+        else hi = mid;
+    }
+    b = lo;
+    q = k - (int)pre[lo];
+}
+
+// Slot of the q-th candidate (0-based) of block b.
+__device__ __forceinline__ int cand_slot(int b, int q, const uint32_t* mw) {
+    uint32_t m = mw[b];
+    for (int i = 0; i < q; ++i) m &= m - 1u;
+    return 32 * b + __builtin_ctz(m);
+}
+
 template <int J, int G>
 __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s, const int N, const ZParams<G>& z,
-                                               uint32_t (&key)[J], int32_t (&sl)[J], uint32_t* pre, uint32_t* lpos,
+                                               uint32_t (&key)[J], uint32_t* pre, uint32_t* lpos,
                                                uint32_t* mw, uint32_t* wsum, uint32_t* bcast) {
     const int tid = threadIdx.x;
     const int nbk = (N + 31) / 32;                     // <= 2048 (N <= 65536)
@@ -79,15 +99,8 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
     for (int j = 0; j < J; ++j) {
         const int k = j * kSelThreads + tid;
         if (k < nc) {
-            int lo = 0, hi = nbk;                          // last block with pre <= k
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if ((int)pre[mid] <= k) lo = mid;
-                else hi = mid;
-            }
-            const int q = k - (int)pre[lo];
-            uint32_t m = mw[lo];
-            for (int i = 0; i < q; ++i) m &= m - 1u;
+            int lo, q;
+            cand_block(k, nbk, pre, lo, q);
             const int c = lo / bpc, r = lo - c * bpc;
             const int head = c * bpc + (r & 3) * q4;
             const int off = (int)(lpos[head + (r >> 2)] - lpos[head]) + q;
@@ -105,7 +118,6 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
                 for (int g = 0; g < G; ++g) S[g] = p[g];
             }
             key[j] = order_key(aggregate<G>(S, z));
-            sl[j] = 32 * lo + __builtin_ctz(m);
         }
         if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
@@ -140,7 +152,6 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
     const bool all = N <= B;
 
     uint32_t key[J];
-    int32_t sl[CAND ? J : 1];
 #pragma unroll
     for (int j = 0; j < J; ++j) key[j] = 0u;
     uint32_t T = 0u;
@@ -152,7 +163,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         if constexpr (G > 0) {
             z = merge_stats<G, kSelThreads>(a.stats + (int64_t)s * a.n_chunks * G, a.n_chunks, a.chunk, N, scratch);
             if constexpr (CAND) {
-                nv = load_candidates<J, G>(a, s, N, z, key, sl, pre, lpos, mw, wsum, bcast);
+                nv = load_candidates<J, G>(a, s, N, z, key, pre, lpos, mw, wsum, bcast);
                 if (nv < B) {                           // overflow (-1) or too few to hold the cut
                     if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1)] = s;
                     return;
@@ -284,7 +295,13 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         const int out = gb + min(eb, need);
         if ((gt || (eq && eb < need)) && out < nk) {
             int slot = n;
-            if constexpr (CAND) slot = all ? n : sl[j];
+            if constexpr (CAND) {
+                if (!all) {                             // candidate n -> its slot
+                    int b, q;
+                    cand_block(n, (N + 31) / 32, pre, b, q);
+                    slot = cand_slot(b, q, mw);
+                }
+            }
             if (a.gather) kept[out] = slot;
             else a.idx_out[(int64_t)s * a.idx_stride + out] = slot;
         }
@@ -310,8 +327,11 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         a.dst.pos[a.dst.row(s, jrow)] = a.src.pos[a.src.row(s, kept[jrow])];
 }
 
+// J <= 16, G <= 4: two workgroups per CU (at most 64 VGPRs and the SGPRs of 8 waves per
+// SIMD), so one workgroup's gather overlaps the other's select phase.
 template <int J, int G, int MODE>
-__global__ __launch_bounds__(kSelThreads) void k_select(SelectArgs a) {
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(J <= 16 && G <= 4 ? 8 : 1))) void k_select(
+    SelectArgs a) {
     select_segment<J, G, MODE>(a, blockIdx.x);
 }
 
