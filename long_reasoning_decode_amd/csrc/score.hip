@@ -593,7 +593,9 @@ constexpr int kCandMul = 3;
 template <int D, int G>
 __global__ __launch_bounds__(kSample) void k_sample(SampleArgs a) {
     constexpr int TS = D / 32, NS = D / 64, NT = (3 * G + 15) / 16;
-    constexpr int TPW = kSample / 4 / 16;    // 16-key tiles per wave
+    constexpr int ROWB = D * 2, CPR = ROWB / 16, NDMA = 32 * CPR / 64;
+    static_assert(kSample == 256, "four waves of two 32-key stages");
+    __shared__ uint4 stage[4][32 * CPR];
     __shared__ float sS[kSample][G];
     __shared__ __align__(16) uint32_t ak[kSample];
     __shared__ float red[kSample / kWave][G];
@@ -608,28 +610,50 @@ __global__ __launch_bounds__(kSample) void k_sample(SampleArgs a) {
         if (tid < G) thr[tid] = -__builtin_inff();
         return;
     }
-    // Sample j = 64 w + 16 u + row sits in stratum j of N/kSample keys, at an
-    // offset that varies with j and the segment.  Its scores come from the same
-    // tile contraction as the scoring pass, so they are the exact fp32 scores.
+    // Sample j = 64 w + 32 h + k (stage h of wave w, stage key k) sits in
+    // stratum j of N/kSample keys, at an offset that varies with j and the
+    // segment.  Its row comes in through LDS like the scoring pass's keys
+    // (whole rows per DMA instruction, the same swizzle), and its scores come
+    // from the same tile contraction, so they are the exact fp32 scores.
     const int stride = N / kSample;           // >= 16 in candidate mode
-    uint4 av[TPW][TS];
+    uint4* region = &stage[w][0];
+    auto issue = [&](int h) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int j = w * (kSample / 4) + 16 * u + row;
-        const int slot = j * stride + (int)(((uint32_t)j * 2654435761u + (uint32_t)s * 40503u) >> 8) % stride;
-        const uint4* rp = reinterpret_cast<const uint4*>(a.kv.k + a.kv.row(s, slot) * (D * 2));
-#pragma unroll
-        for (int st = 0; st < TS; ++st) av[u][st] = rp[4 * st + grp];
-    }
+        for (int i = 0; i < NDMA; ++i) {
+            const int P = 64 * i + lane;
+            const int kl = P / CPR;
+            const int lc = (P % CPR) ^ (kl % CPR);
+            const int j = w * (kSample / 4) + 32 * h + kl;
+            const int slot = j * stride + (int)(((uint32_t)j * 2654435761u + (uint32_t)s * 40503u) >> 8) % stride;
+            const uint8_t* src = a.kv.k + a.kv.row(s, slot) * ROWB + 16 * lc;
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + 64 * i), 16, 0, 0);
+        }
+    };
+    issue(0);
     bf16x8_t bt[TS][NT], bn[NS][NT];
     mfma_coef_fragments<D, G>(a.ctab, a.wtab, a.shape, a.n_q_heads, s, bt, bn);
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        float S4[4];
-        mfma_tile_scores<D, G>(av[u], bt, bn, S4);
-        if (row < G) {
+    for (int h = 0; h < 2; ++h) {
+        uint4 av[2][TS];
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sS[w * (kSample / 4) + 16 * u + 4 * grp + r][row] = S4[r];
+        for (int u = 0; u < 2; ++u) {
+            const int kl = 16 * u + row;
+#pragma unroll
+            for (int st = 0; st < TS; ++st) av[u][st] = region[kl * CPR + ((4 * st + grp) ^ (kl % CPR))];
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+        if (h == 0) issue(1);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float S4[4];
+            mfma_tile_scores<D, G>(av[u], bt, bn, S4);
+            if (row < G) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sS[w * (kSample / 4) + 32 * h + 16 * u + 4 * grp + r][row] = S4[r];
+            }
         }
     }
     __syncthreads();
