@@ -159,7 +159,7 @@ WsPlan plan_workspace(const tri_calib_s* c, const tri_cache_desc* kv) {
     p.stats = p.ctab + align256((size_t)kv->n_layers * kv->n_seq * c->Hq * c->D * sizeof(float));
     p.thr = p.stats + align256((size_t)n_seg * max_chunks * c->G * sizeof(double2));
     p.masks = p.thr + align256((size_t)n_seg * c->G * sizeof(float));
-    p.s_int = p.masks + align256((size_t)n_seg * p.mask_stride * sizeof(uint32_t));
+    p.s_int = p.masks + align256((size_t)n_seg * p.mask_stride * c->G * sizeof(uint32_t));
     p.total = p.s_int + align256((size_t)n_seg * kv->capacity * c->G * sizeof(float));
     return p;
 }

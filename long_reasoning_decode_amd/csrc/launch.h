@@ -90,7 +90,7 @@ struct ScoreArgs {
     float* s_int;           // optional [n_seg][cap][G]; candidate mode: per-wave candidate lists
     double2* stats;         // [n_seg][n_chunks][G]
     const float* thr;       // candidate mode: [n_seg][G] thresholds L_h
-    uint32_t* masks;        // candidate mode: [n_seg][mask_stride], bit i of word b = key 32 b + i
+    uint32_t* masks;        // candidate mode: [n_seg][mask_stride][G], bit i of word (b, h): key 32 b + i passed head h
     int64_t mask_stride;
     const int32_t* fb_list; // fallback mode: segments to redo, and their count
     const int32_t* fb_count;

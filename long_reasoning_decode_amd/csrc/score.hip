@@ -344,13 +344,13 @@ constexpr int kMaxChunkBlocks = 2048 / 32;   // 32-key mask words per chunk
 constexpr int kScoreLds = 40960;
 
 // Scores chunk c of segment s.  CAND = false: every key's G scores go to the
-// interleaved scratch (and/or the head-major output).  CAND = true: only keys
-// with some S_h >= L_h (the segment's thresholds) are kept, as G-float records
-// in a per-wave list in slot order, plus one 32-bit mask word per 32-key block
-// saying which keys those are.  Wave w of a chunk scores blocks w, w+4, w+8,
-// ..., so its list holds at most wave_keys(w, cnt) records; the four lists
-// sit back to back in the scratch rows of the chunk's keys.  The chunk
-// statistics always cover every key.
+// interleaved scratch (and/or the head-major output).  CAND = true: only the
+// (key, head) pairs with S_h >= L_h (the segment's thresholds) are kept: the
+// score S_h, key-major then head-major, in a per-wave list, plus G mask words
+// per 32-key block (word h: which keys of the block passed head h).  Wave w of
+// a chunk scores blocks w, w+4, w+8, ..., so its list holds at most
+// G * wave_keys(w, cnt) floats; the four lists sit back to back in the scratch
+// rows of the chunk's keys.  The chunk statistics always cover every key.
 template <int D, int G, bool CAND>
 __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s, const int c) {
     constexpr int F = D / 2;
@@ -368,20 +368,19 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
     // 128), with the non-temporal hint; chunk lc of stage key k sits at chunk
     // position lc ^ (k mod CPR) so the fragment reads below are conflict-free.
     static_assert(SKEYS == 32, "one stage is one 32-key mask block");
-    // Candidate mode: each wave keeps its records (G floats per candidate, in
-    // slot order) in LDS and writes them out only when the buffer cannot take
-    // another stage, and at the end of the chunk.  Stores share the wait
-    // counter with the staging DMA, so every store in the stream delays the
-    // wave's next stage; the buffer takes whatever LDS four workgroups per CU
-    // leave (118 records per wave for head_dim 128, G = 4).
-    constexpr int FIXED = (int)sizeof(uint4) * 4 * SKEYS * CPR + 4 * G * 3 * 8 + kMaxChunkBlocks * 4;
-    constexpr int CAPR0 = (kScoreLds - FIXED) / (4 * G * 4);
-    constexpr int CAPR = CAND ? (CAPR0 > 64 ? CAPR0 : 64) : 1;   // records per wave buffer
+    // Candidate mode: each wave keeps its kept scores in LDS and writes them
+    // out only when the buffer cannot stage another 32 keys, and at the end of
+    // the chunk; the buffer takes whatever LDS four workgroups per CU leave
+    // (1824 floats per wave for head_dim 128, G = 4).  Every record store
+    // mixed into the key stream slows it on some page placements.
+    constexpr int FIXED = (int)sizeof(uint4) * 4 * SKEYS * CPR + 4 * G * 3 * 8 + kMaxChunkBlocks * G * 4;
+    constexpr int CAPF0 = (kScoreLds - FIXED) / (4 * 4);
+    constexpr int CAPF = CAND ? (CAPF0 > 2 * SKEYS * G ? CAPF0 : 2 * SKEYS * G) : 1;   // floats per wave buffer
     __shared__ uint4 stage[4][SKEYS * CPR];
     __shared__ float tileS[CAND ? 1 : 4][CAND ? 1 : 16 * G];      // one tile's scores, key-major
     __shared__ double part[4][G][3];
-    __shared__ float cbuf[CAND ? 4 : 1][CAND ? CAPR * G : 1];
-    __shared__ uint32_t maskbuf[CAND ? kMaxChunkBlocks : 1];
+    __shared__ float cbuf[CAND ? 4 : 1][CAND ? CAPF : 1];
+    __shared__ uint32_t maskbuf[CAND ? kMaxChunkBlocks * G : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, grp = lane >> 4;
@@ -391,8 +390,7 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
     const int cnt = min(a.chunk, N - start);
 
     float thr[CAND ? G : 1];
-    int nb = 0, nw = 0;            // records staged in LDS / already written (wave-uniform)
-    uint32_t bmask = 0u;
+    int nb = 0, nw = 0;            // floats staged in LDS / already written (wave-uniform)
     float* list = nullptr;
     if constexpr (CAND) {
 #pragma unroll
@@ -423,16 +421,10 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
             __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + 64 * i), 16, 0, 2 /* nt */);
         }
     };
-    // all nb buffered records -> list[nw ..]
+    // all nb buffered floats -> list[nw ..]
     auto flush_records = [&]() {
         if constexpr (CAND) {
-            if constexpr (G % 4 == 0) {
-                for (int i = 4 * lane; i < nb * G; i += 4 * kWave)
-                    *reinterpret_cast<float4*>(list + (int64_t)nw * G + i) =
-                        *reinterpret_cast<const float4*>(&cbuf[wave][i]);
-            } else {
-                for (int i = lane; i < nb * G; i += kWave) list[(int64_t)nw * G + i] = cbuf[wave][i];
-            }
+            for (int i = lane; i < nb; i += kWave) list[nw + i] = cbuf[wave][i];
             nw += nb;
             nb = 0;
             __builtin_amdgcn_wave_barrier();
@@ -453,7 +445,7 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
         __builtin_amdgcn_wave_barrier();
         if (tb + 4 * UT < n_tiles) issue_stage(tb + 4 * UT);       // next stage loads under this compute
         if constexpr (CAND) {
-            if (nb + SKEYS > CAPR) flush_records();                  // no room to stage this stage's scores
+            if (nb + SKEYS * G > CAPF) flush_records();              // no room to stage this stage's scores
         }
 #pragma unroll
         for (int u = 0; u < UT; ++u) {
@@ -466,7 +458,7 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
                 for (int r = 0; r < 4; ++r) {
                     const int key = tile0 + 4 * grp + r;
                     // candidate mode: the stage's 32 keys are staged after the kept records
-                    if constexpr (CAND) cbuf[wave][(nb + 16 * u + 4 * grp + r) * G + row] = S4[r];
+                    if constexpr (CAND) cbuf[wave][nb + (16 * u + 4 * grp + r) * G + row] = S4[r];
                     else tileS[wave][(4 * grp + r) * G + row] = S4[r];
                     if (key < cnt) {
                         if (cntl == 0) shift = S4[r];
@@ -503,28 +495,41 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
             __builtin_amdgcn_wave_barrier();
         }
         if constexpr (CAND) {
-            // lanes 0..31: is staged key tb*16 + lane a candidate (some S_h >= L_h)?
-            // Candidates move down onto the kept records (reads before writes).
+            // lanes 0..31: which heads of staged key tb*16 + lane pass (S_h >= L_h)?
+            // The passing scores move down onto the kept floats (reads before
+            // writes; a key's floats never pass a later key's record).
             const int key0 = tb * 16;
             float rec[G];
-            bool isc = false;
+            uint32_t hb = 0u;
             if (lane < 32) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) rec[g] = cbuf[wave][(nb + lane) * G + g];
+                for (int g = 0; g < G; ++g) rec[g] = cbuf[wave][nb + lane * G + g];
                 if (key0 + lane < cnt) {
 #pragma unroll
-                    for (int g = 0; g < G; ++g) isc |= rec[g] >= thr[g];
+                    for (int g = 0; g < G; ++g) hb |= (rec[g] >= thr[g] ? 1u : 0u) << g;
                 }
             }
-            bmask = (uint32_t)__ballot(isc);
-            __builtin_amdgcn_wave_barrier();
-            if (isc) {
-                const int p = nb + __popc(bmask & ((1u << lane) - 1u));
+            const uint32_t below = (1u << (lane & 31)) - 1u;
+            int off = 0, tot = 0;
+            uint32_t mwd[G];
 #pragma unroll
-                for (int g = 0; g < G; ++g) cbuf[wave][p * G + g] = rec[g];
+            for (int g = 0; g < G; ++g) {
+                mwd[g] = (uint32_t)__ballot((hb >> g) & 1u);
+                off += __popc(mwd[g] & below);
+                tot += __popc(mwd[g]);
             }
-            nb += __popc(bmask);
-            if (lane == 0) maskbuf[tb / UT] = bmask;
+            __builtin_amdgcn_wave_barrier();
+            if (hb) {
+                int p = nb + off;
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    if ((hb >> g) & 1u) cbuf[wave][p++] = rec[g];
+            }
+            nb += tot;
+            if (lane == 0) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) maskbuf[(tb / UT) * G + g] = mwd[g];
+            }
             __builtin_amdgcn_wave_barrier();
         }
     }
@@ -555,7 +560,8 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
         a.stats[((int64_t)s * a.n_chunks + c) * G + tid] = make_double2(tm, tm2);
     }
     if constexpr (CAND) {
-        for (int i = tid; i < (cnt + 31) / 32; i += 256) a.masks[(int64_t)s * a.mask_stride + start / 32 + i] = maskbuf[i];
+        for (int i = tid; i < (cnt + 31) / 32 * G; i += 256)
+            a.masks[((int64_t)s * a.mask_stride + start / 32) * G + i] = maskbuf[i];
     }
 }
 

@@ -55,17 +55,29 @@ __device__ __forceinline__ void cand_block(int k, int nbk, const uint32_t* pre, 
     q = k - (int)pre[lo];
 }
 
-// Slot of the q-th candidate (0-based) of block b.
-__device__ __forceinline__ int cand_slot(int b, int q, const uint32_t* mw) {
-    uint32_t m = mw[b];
+// Position (0..31) of the q-th set bit (0-based) of m.
+__device__ __forceinline__ int nth_bit(uint32_t m, int q) {
     for (int i = 0; i < q; ++i) m &= m - 1u;
-    return 32 * b + __builtin_ctz(m);
+    return __builtin_ctz(m);
 }
 
+// Candidate lists of one segment (written by the scoring pass in candidate
+// mode) -> order keys held in registers, in slot order: entry k sits in
+// register k / 1024 of thread k % 1024.  Returns the number of candidate keys
+// (keys with at least one listed head), or -1 when they do not fit in
+// J * 1024 registers.
+// Block b (keys 32b .. 32b+31) has G mask words (word h: keys whose head h
+// passed) and was scored by wave w = (b mod bpc) mod 4 of chunk c = b / bpc
+// (bpc = chunk / 32), whose list (at wave_list_base in the chunk's scratch
+// rows) holds, block after block and key after key, the passing heads' scores.
+// Two block scans give, per block, the slot-order rank of its first candidate
+// key (pre, from the union of its words) and, in the order of the wave lists,
+// the running float count (lpos) from which its offset inside its list follows.
+// A key's entry is A' = the largest z-score over its listed heads.
 template <int J, int G>
 __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s, const int N, const ZParams<G>& z,
-                                               uint32_t (&key)[J], uint32_t* pre, uint32_t* lpos,
-                                               uint32_t* mw, uint32_t* wsum, uint32_t* bcast) {
+                                               uint32_t (&key)[J], uint32_t* pre, uint32_t* lpos, uint32_t* mw,
+                                               uint32_t* wsum, uint32_t* bcast) {
     const int tid = threadIdx.x;
     const int nbk = (N + 31) / 32;                     // <= 2048 (N <= 65536)
     const int bpc = a.chunk / 32, q4 = bpc / 4;
@@ -73,20 +85,29 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
         const int c = b / bpc, r = b - c * bpc;
         return c * bpc + (r & 3) * q4 + (r >> 2);
     };
-    const uint32_t* mp = a.masks + (int64_t)s * a.mask_stride;
+    const uint32_t* mp = a.masks + (int64_t)s * a.mask_stride * G;
     const int b0 = 2 * tid, b1 = 2 * tid + 1;
-    const uint32_t m0 = b0 < nbk ? mp[b0] : 0u, m1 = b1 < nbk ? mp[b1] : 0u;
-    const uint32_t c0 = __popc(m0), c1 = __popc(m1);
-    mw[b0] = m0;
-    mw[b1] = m1;
+    uint32_t u0 = 0u, u1 = 0u, f0 = 0u, f1 = 0u;       // union word, float count
+    // (blocks 2 tid and 2 tid + 1: 2G consecutive words)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const uint32_t w0 = b0 < nbk ? mp[b0 * G + g] : 0u, w1 = b1 < nbk ? mp[b1 * G + g] : 0u;
+        u0 |= w0;
+        u1 |= w1;
+        f0 += __popc(w0);
+        f1 += __popc(w1);
+    }
+    const uint32_t c0 = __popc(u0), c1 = __popc(u1);
+    mw[b0] = u0;
+    mw[b1] = u1;
     lpos[b0] = 0u;
     lpos[b1] = 0u;
     const uint32_t inc = block_incl_scan(c0 + c1, wsum);     // (synchronises)
     pre[b0] = inc - c0 - c1;
     pre[b1] = inc - c1;
     if (tid == kSelThreads - 1) bcast[0] = inc;
-    if (b0 < nbk) lpos[perm(b0)] = c0;
-    if (b1 < nbk) lpos[perm(b1)] = c1;
+    if (b0 < nbk) lpos[perm(b0)] = f0;
+    if (b1 < nbk) lpos[perm(b1)] = f1;
     __syncthreads();
     const uint32_t t0 = lpos[b0], t1 = lpos[b1];
     const uint32_t inc2 = block_incl_scan(t0 + t1, wsum);
@@ -101,23 +122,36 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
         if (k < nc) {
             int lo, q;
             cand_block(k, nbk, pre, lo, q);
-            const int c = lo / bpc, r = lo - c * bpc;
-            const int head = c * bpc + (r & 3) * q4;
-            const int off = (int)(lpos[head + (r >> 2)] - lpos[head]) + q;
-            const int base = wave_list_base(r & 3, min(a.chunk, N - c * a.chunk));
-            const float* p = a.s_int + ((int64_t)s * a.cap + (int64_t)c * a.chunk + base + off) * G;
-            float S[G];
+            const int kb = nth_bit(mw[lo], q);
+            const uint32_t below = (1u << kb) - 1u;
+            uint32_t hw[G];
             if constexpr (G % 4 == 0) {
 #pragma unroll
                 for (int g = 0; g < G; g += 4) {
-                    const float4 v = *reinterpret_cast<const float4*>(p + g);
-                    S[g] = v.x; S[g + 1] = v.y; S[g + 2] = v.z; S[g + 3] = v.w;
+                    const uint4 v = *reinterpret_cast<const uint4*>(mp + lo * G + g);
+                    hw[g] = v.x; hw[g + 1] = v.y; hw[g + 2] = v.z; hw[g + 3] = v.w;
                 }
             } else {
 #pragma unroll
-                for (int g = 0; g < G; ++g) S[g] = p[g];
+                for (int g = 0; g < G; ++g) hw[g] = mp[lo * G + g];
             }
-            key[j] = order_key(aggregate<G>(S, z));
+            int foff = 0;
+#pragma unroll
+            for (int g = 0; g < G; ++g) foff += __popc(hw[g] & below);
+            const int c = lo / bpc, r = lo - c * bpc;
+            const int head = c * bpc + (r & 3) * q4;
+            const int base = wave_list_base(r & 3, min(a.chunk, N - c * a.chunk));
+            const float* p = a.s_int + ((int64_t)s * a.cap + (int64_t)c * a.chunk + base) * G +
+                             (lpos[head + (r >> 2)] - lpos[head]) + foff;
+            float A = -__builtin_inff();
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if ((hw[g] >> kb) & 1u) {
+                    const float S = *p++;
+                    A = fmaxf(A, ((S - z.mu_hi[g]) - z.mu_lo[g]) * z.inv[g]);
+                }
+            }
+            key[j] = order_key(A);
         }
         if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
@@ -126,12 +160,14 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
 
 // Top-B of segment s.  MODE: SELECT_A reads aggregated scores, SELECT_S the
 // interleaved per-head scores and chunk statistics, SELECT_C the candidate
-// lists.  In mode C the result stands only if every key left out of the list
-// provably ranks below the cut: a key off the list has S_h < L_h for every
-// head, and the aggregate ((S - mu_hi) - mu_lo) * inv, max over heads, is
-// monotone in each S_h in fp32 as well, so its A is at most A(L); the cut T
-// (the B-th largest candidate) must then exceed A(L).  Otherwise the segment
-// goes on the fallback list and nothing is written for it here.
+// lists.  In mode C the result stands only if it provably equals mode S's: an
+// unlisted (key, head) pair has S_h < L_h, and z_h = ((S - mu_hi) - mu_lo) * inv
+// is monotone in S_h in fp32 as well, so its z-score is at most U = max_h z_h(L_h).
+// A key's true A is therefore A' (the max over its listed heads) whenever
+// A' > U, and at most U otherwise (keys with no listed head included).  If the
+// cut T (the B-th largest A') exceeds U, the keys at or above it, their A and
+// their tie order are exactly those of the full computation.  Otherwise the
+// segment goes on the fallback list and nothing is written for it here.
 template <int J, int G, int MODE>
 __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s) {
     constexpr bool CAND = MODE == SELECT_C;
@@ -299,7 +335,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
                 if (!all) {                             // candidate n -> its slot
                     int b, q;
                     cand_block(n, (N + 31) / 32, pre, b, q);
-                    slot = cand_slot(b, q, mw);
+                    slot = 32 * b + nth_bit(mw[b], q);
                 }
             }
             if (a.gather) kept[out] = slot;
