@@ -79,6 +79,20 @@ struct SegShape {
     __device__ __forceinline__ int head(int s) const { return s % n_kv_heads; }
 };
 
+// ---------------------------------------------------------------- matrix cores and LDS DMA
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8): wait until at most n vector-memory operations (LDS-DMA
+// loads included) are outstanding, or for all LDS operations.
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitVm0 = wait_vm(0);
+constexpr int kWaitLgkm0 = 0xC07F;
+
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll

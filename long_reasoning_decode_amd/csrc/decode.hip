@@ -171,10 +171,184 @@ __global__ __launch_bounds__(256) void k_decode_attn(AttnArgs a) {
     }
 }
 
+// bf16 caches.  One 256-thread workgroup per segment; wave w takes the key
+// tiles w, w+4, ... (TK keys each: 32 for head_dim 64, 16 for 128, so a K or V
+// tile is 4 KB).  Tiles come in through LDS DMA, whole rows per instruction,
+// two tiles in flight per wave (double buffer); rows are chunk-swizzled
+// (16-byte chunk lc of tile key k at lc ^ (k mod CPR)).
+//  * logits q.K^T on the matrix cores: A = 16 key rows, B = the G query
+//    vectors as columns (bf16, so the products are exact; fp32 accumulation);
+//  * online softmax per head (base 2) on the fragment layout: lane (grp, row)
+//    holds head `row`'s logits of keys 4 grp + r;
+//  * P.V on the vector units: lane = output dimension, the tile's V rows read
+//    from LDS, probabilities broadcast from LDS.
+// The four waves' (max, sum, partial output) are merged at the end.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
+    constexpr int ROWB = D * 2, CPR = ROWB / 16;
+    constexpr int TK = 2048 / D;               // keys per tile
+    constexpr int NU = TK / 16;                // 16-key MFMA tiles per tile
+    constexpr int TS = D / 32;                 // k-steps
+    constexpr int NDMA = TK * CPR / 64;        // DMA instructions per operand and tile
+    constexpr int DPL = D / kWave;             // output dims per lane
+    constexpr float kLog2e = 1.4426950408889634f;
+    static_assert(G <= 16 && NU >= 1, "one 16-column B fragment holds the group");
+    __shared__ uint4 kt[4][2][TK * CPR];
+    __shared__ uint4 vt[4][2][TK * CPR];
+    __shared__ float pt[4][G][TK];
+    __shared__ float alph[4][G];
+    __shared__ float wm[4][G], wl[4][G];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int row = lane & 15, grp = lane >> 4;
+    const int s = blockIdx.x;
+    const int N = min(max(a.lengths[s], 0), (int)a.kv.capacity);
+    const int l = a.shape.layer(s), b = a.shape.seq(s), h = a.shape.head(s);
+    const uint8_t* qb = a.q + (((int64_t)l * a.shape.n_seq + b) * a.n_q_heads + (int64_t)h * G) * ROWB;
+    const float sl2 = a.scale * kLog2e;
+    const int nt = (N + TK - 1) / TK;
+
+    auto issue = [&](int t, int buf) {
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) {
+            const int P = 64 * i + lane;
+            const int kl = P / CPR;
+            const int lc = (P % CPR) ^ (kl % CPR);
+            const int key = min(t * TK + kl, N - 1);          // tail rows re-read a valid row
+            const int64_t off = a.kv.row(s, key) * ROWB + 16 * lc;
+            __builtin_amdgcn_global_load_lds(a.kv.k + off, (lds_void_t*)(&kt[w][buf][0] + 64 * i), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(a.kv.v + off, (lds_void_t*)(&vt[w][buf][0] + 64 * i), 16, 0, 0);
+        }
+    };
+    if (w < nt) issue(w, 0);
+    if (w + 4 < nt) issue(w + 4, 1);
+
+    // B fragments: column row = head row (zero past G), k-slot (grp, e)
+    bf16x8_t bq[TS];
+#pragma unroll
+    for (int st = 0; st < TS; ++st) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (row < G) v = reinterpret_cast<const uint4*>(qb + (int64_t)row * ROWB)[4 * st + grp];
+        bq[st] = __builtin_bit_cast(bf16x8_t, v);
+    }
+
+    float m = -__builtin_inff(), lsum = 0.0f;              // head `row`'s running max and sum
+    float o[G][DPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) o[g][d] = 0.0f;
+
+    for (int t = w, it = 0; t < nt; t += 4, ++it) {
+        const int buf = it & 1;
+        if (t + 4 < nt) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NDMA));   // the next tile may stay in flight
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_wave_barrier();
+        const uint4* kr = &kt[w][buf][0];
+        float x[NU][4];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int kl = 16 * u + row;
+            f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < TS; ++st) {
+                const uint4 av = kr[kl * CPR + ((4 * st + grp) ^ (kl % CPR))];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), bq[st], acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = t * TK + 16 * u + 4 * grp + r;
+                x[u][r] = key < N ? acc[r] * sl2 : -__builtin_inff();
+            }
+        }
+        // online softmax: head `row` over the tile's keys (4 lanes x NU*4 values);
+        // the tile's first key is valid, so the new maximum is finite
+        float tm = -__builtin_inff();
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tm = fmaxf(tm, x[u][r]);
+        tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
+        tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+        const float mn = fmaxf(m, tm);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        float ts = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(x[u][r] - mn);
+                ts += p;
+                if (row < G) pt[w][row][16 * u + 4 * grp + r] = p;
+            }
+        ts += __shfl_xor(ts, 16, kWave);
+        ts += __shfl_xor(ts, 32, kWave);
+        lsum = lsum * alpha + ts;
+        m = mn;
+        if (row < G && grp == 0) alph[w][row] = alpha;
+        __builtin_amdgcn_wave_barrier();
+        // P.V: lane = output dims lane + 64 dd
+        const uint4* vr = &vt[w][buf][0];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float al = alph[w][g];
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) o[g][d] *= al;
+        }
+#pragma unroll 4
+        for (int k = 0; k < TK; ++k) {
+            float v[DPL];
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) {
+                const int dim = lane + d * kWave;
+                const uint16_t* rp = reinterpret_cast<const uint16_t*>(vr + k * CPR + ((dim >> 3) ^ (k % CPR)));
+                v[d] = bf16_lo((uint32_t)rp[dim & 7]);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float p = pt[w][g][k];
+#pragma unroll
+                for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(p, v[d], o[g][d]);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (t + 8 < nt) issue(t + 8, buf);                 // this buffer is free again
+    }
+
+    // merge the four waves (their tile buffers hold the partial outputs)
+    __syncthreads();
+    float* wo = reinterpret_cast<float*>(&kt[0][0][0]);   // [4][G][D]
+    static_assert(sizeof(kt) >= sizeof(float) * 4 * G * D, "partial outputs fit the K tiles");
+    if (grp == 0 && row < G) {
+        wm[w][row] = m;
+        wl[w][row] = lsum;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) wo[(w * G + g) * D + lane + d * kWave] = o[g][d];
+    __syncthreads();
+    float* out = a.out + (((int64_t)l * a.shape.n_seq + b) * a.n_q_heads + (int64_t)h * G) * D;
+    for (int i = tid; i < G * D; i += 256) {
+        const int g = i / D, d = i - g * D;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, wm[v][g]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float sc = wl[v][g] > 0.0f ? __builtin_amdgcn_exp2f(wm[v][g] - M) : 0.0f;
+            num = fmaf(wo[(v * G + g) * D + d], sc, num);
+            den = fmaf(wl[v][g], sc, den);
+        }
+        out[(int64_t)g * D + d] = den > 0.0f ? num / den : 0.0f;
+    }
+}
+
 template <int D, int G>
 static void attn_dtype(const AttnArgs& a, bool bf16, hipStream_t stream) {
     const dim3 grid((unsigned)a.n_seg), block(256);
-    if (bf16) hipLaunchKernelGGL((k_decode_attn<D, G, true>), grid, block, 0, stream, a);
+    if (bf16) hipLaunchKernelGGL((k_decode_attn_mfma<D, G>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_decode_attn<D, G, false>), grid, block, 0, stream, a);
 }
 

@@ -193,10 +193,6 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
 // load); the coefficient fragments are loop-invariant registers.  |k_f| needs
 // the band's real and imaginary parts, which sit in the same lane and slot of
 // two A fragments (dims f and f + F), so the norm operand is built in registers.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
@@ -227,12 +223,7 @@ __device__ __forceinline__ void chan_merge(double& n, double& m, double& m2, dou
     n = nt;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 
-// s_waitcnt immediates (gfx9 encoding): wait for all vector-memory operations
-// (this includes LDS-DMA loads), or for all LDS operations.
-constexpr int kWaitVm0 = 0x0F70;
-constexpr int kWaitLgkm0 = 0xC07F;
 
 // B fragments of one segment's G query heads for v_mfma_f32_16x16x32_bf16:
 // column 16t + (lane % 16) is (split q, head h) = ((16t + lane%16) / G, % G),
