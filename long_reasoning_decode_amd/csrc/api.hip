@@ -469,10 +469,12 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     double2* stats = reinterpret_cast<double2*>(w + p.stats);
     float* s_int = reinterpret_cast<float*>(w + p.s_int);
     const int chunk = pick_chunk(n_segments(src), src->capacity);
-    // bf16 caches: candidate pass (sample -> score lists -> certified select),
-    // then the full path for any segment whose certificate failed (both
-    // fallback kernels exit at once when none did).  fp32 caches: full path.
-    const bool cand = src->dtype == TRI_DTYPE_BF16;
+    // bf16 caches that can hold a segment long enough for candidate mode:
+    // candidate pass (sample -> score lists -> certified select), then the full
+    // path for any segment whose certificate failed (both fallback kernels exit
+    // at once when none did).  Otherwise (fp32, or capacity below what
+    // candidate mode needs): the full path.
+    const bool cand = src->dtype == TRI_DTYPE_BF16 && candidate_mode(src->capacity, budget);
     if ((rc = run_phase_and_score(calib, src, t, nullptr, s_int, stats, ctab, chunk, st, cand ? &p : nullptr, w,
                                   budget)))
         return rc;

@@ -366,7 +366,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
 // J <= 16, G <= 4: two workgroups per CU (at most 64 VGPRs and the SGPRs of 8 waves per
 // SIMD), so one workgroup's gather overlaps the other's select phase.
 template <int J, int G, int MODE>
-__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(J <= 16 && G <= 4 ? 8 : 1))) void k_select(
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu((J <= 16 && G <= 4) || (J <= 2 && G == 8) ? 8 : 1))) void k_select(
     SelectArgs a) {
     select_segment<J, G, MODE>(a, blockIdx.x);
 }
