@@ -108,12 +108,102 @@ def copy_probe(mib):
                       "copy_GBs_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def bench_decode_loop(args, T, W):
+    """GPT-OSS-shaped decode loop: a step is one 128-token window, i.e. 128 x
+    (append one token to every segment, single-query attention of every query
+    head over its cache) followed by the window's prune back to B.  Tokens are
+    generated before timing and reused window after window."""
+    import math
+
+    import torch
+    cfg = W.CONFIGS["gptoss"]
+    B, win = cfg.budget, cfg.window
+    st = W.decode_start(cfg, "cuda")
+    km = st.pop("key_model")
+    cal = W.calibration(cfg)
+    calib = T.tri_calib_load(cal["mag"], cal["phase"], cal["conc"], cal["offsets"], n_kv_heads=cfg.n_kv_heads,
+                             rope_theta=cfg.theta)
+    cap = st["capacity"]
+    caches = [st, {"k": torch.empty_like(st["k"]), "v": torch.empty_like(st["v"]),
+                   "pos": torch.empty_like(st["pos"]), "lengths": torch.zeros_like(st["lengths"])}]
+    descs = [T.cache_desc(c["k"], c["v"], c["pos"], c["lengths"], n_layers=cfg.n_layers, n_seq=cfg.n_seq,
+                          n_kv_heads=cfg.n_kv_heads) for c in caches]
+    ws = T.workspace(calib, descs[0], B)
+    t0 = cfg.start_pos_range
+    toks = [W.decode_token(cfg, km, j, t0 + j, "cuda") for j in range(win)]
+    out = torch.empty(toks[0][2].shape, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    pos = torch.arange(t0, t0 + (args.warmup + args.steps + 1) * win, dtype=torch.int32,
+                       device="cuda")[:, None].expand(-1, cfg.n_seq).contiguous()      # [token][seq]
+    tvec = torch.empty((cfg.n_seq,), dtype=torch.int32, device="cuda")
+    state = {"cur": 0, "w": 0}
+    stream = torch.cuda.current_stream()
+
+    def window():
+        cur = state["cur"]
+        d = descs[cur]
+        for j in range(win):
+            k_new, v_new, q = toks[j]
+            T.tri_append(d, k_new, v_new, pos[state["w"] * win + j], stream=stream)
+            T.tri_decode_attn(d, cfg.n_q_heads, q, scale, out, stream=stream)
+        tvec.fill_(t0 + (state["w"] + 1) * win)
+        nxt = caches[1 - cur]
+        T.tri_prune_window(calib, d, tvec, B, descs[1 - cur], nxt["lengths"], ws, stream=stream)
+        state["cur"] = 1 - cur
+        state["w"] += 1
+
+    for _ in range(args.warmup):
+        window()
+    torch.cuda.synchronize()
+    T.tri_timing_reset()
+    T.tri_timing_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        window()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    T.tri_timing_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kt = T.tri_timing_read()
+    es = 2
+    # decode attention reads every valid K and V row once per step (lengths B+1 .. B+win over a window)
+    kv_rows = cfg.n_seg * sum(B + j + 1 for j in range(win))
+    attn_bytes = kv_rows * cfg.head_dim * es * 2 + win * (out.numel() * (es + 4))
+    attn_launches, attn_ms = kt["decode_attn"]
+    attn_avg = attn_ms / attn_launches
+    attn_gbs = attn_bytes / win / (attn_avg * 1e-3) / 1e9
+    prune_bytes = cfg.n_seg * ((B + win) * cfg.head_dim * es + B * (4 * cfg.head_dim * es + 8))
+    kernels = {k: {"avg_ms": round(v[1] / v[0], 4), "launches": v[0]} for k, v in kt.items() if v[0]}
+    prune_ms = sum(v["avg_ms"] for k, v in kernels.items() if k not in ("append", "decode_attn"))
+    tokens = win * cfg.n_seq
+    result = {
+        "metric": "decode tokens/sec over the pruned cache (GPT-OSS-shaped loop, prune every 128 tokens)",
+        "value": round(tokens / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": (f"gptoss: {cfg.n_layers} layers x {cfg.n_seq} sequences x {cfg.n_kv_heads} KV heads, "
+                                f"GQA {cfg.group}, head_dim {cfg.head_dim}, bf16, B={B}; a step is one {win}-token "
+                                f"window (append + decode attention per token, then the prune)"),
+                   "tokens_per_step": tokens},
+        "roofline": {"bound": "hbm", "kernel": "decode_attn", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "prune": {"algorithmic_bytes": prune_bytes, "ms": round(prune_ms, 4),
+                  "achieved_GBs": round(prune_bytes / (prune_ms * 1e-3) / 1e9, 1)},
+        "kernels": kernels,
+    }
+    calib.free()
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l"])
+    ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l", "gptoss"],
+                    help="qwen36l (default): the pruning pass; gptoss: decode-loop windows")
     ap.add_argument("--cpu-sample", type=int, default=16, help="oracle segments for the CPU baseline (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
@@ -135,6 +225,9 @@ def main():
 
     T.load()
     torch.cuda.set_device(0)
+    if args.workload == "gptoss":
+        bench_decode_loop(args, T, W)
+        return
     cfg = W.CONFIGS[args.workload]
     B = cfg.budget
     t_gen = time.perf_counter()
