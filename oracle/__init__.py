@@ -57,9 +57,10 @@ def _load():
     lib.orc_gather_rows.argtypes = [P, i64, P, i64, P]
     lib.orc_paged_rows.argtypes = [P, i64, P, i32, i64, P]
     lib.orc_decode_attn.argtypes = [P, i32, P, P, i32, i64, i32, i32, dbl, P]
+    lib.orc_calibrate.argtypes = [P, i32, i64, i32, P, P, P]
     for fn in (lib.orc_score_segment, lib.orc_zscore_max, lib.orc_select_topb,
                lib.orc_select_topb_f32, lib.orc_gather_rows, lib.orc_paged_rows,
-               lib.orc_decode_attn):
+               lib.orc_decode_attn, lib.orc_calibrate):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -172,6 +173,18 @@ def decode_attn(q, K, V, scale):
     _check(lib.orc_decode_attn(_ptr(q), qdt, _ptr(K), _ptr(V), kdt, N, d, G, float(scale),
                                _ptr(out)), "decode_attn")
     return out
+
+
+def calibrate(q):
+    """Centre magnitude, phase and concentration per band of one query head
+    from sampled pre-RoPE rows q [n][d] (fp32 or bf16-as-uint16): fp64 [F] x 3."""
+    qs, dt = _stored(q)
+    n, d = qs.shape
+    M = np.zeros(d // 2)
+    phi = np.zeros(d // 2)
+    R = np.zeros(d // 2)
+    _check(_load().orc_calibrate(_ptr(qs), dt, n, d, _ptr(M), _ptr(phi), _ptr(R)), "orc_calibrate")
+    return M, phi, R
 
 
 def prune_segment(K, V, pos, t, theta, M, phi, R, offsets, B):

@@ -269,3 +269,39 @@ int orc_decode_attn(const void* q, int q_dtype, const void* K, const void* V, in
     free(logit);
     return 0;
 }
+
+/*
+ * Offline calibration of one query head from sampled pre-RoPE queries
+ * ([YY] 主要方法: pre-RoPE queries gather around fixed non-zero centres, and
+ * the concentration of a band is the mean resultant length R, closer to 1
+ * meaning more concentrated directions).  Band f of a sample is the complex
+ * number q[f] + i q[f+F]; over the n samples:
+ *   M[f]   = mean of |q_f|                       (centre magnitude)
+ *   phi[f] = arg of the sum of q_f               (centre phase; 0 when the sum is 0)
+ *   R[f]   = | mean of q_f / |q_f| |             (mean resultant length; a sample
+ *                                                 with q_f = 0 adds a zero vector)
+ * q: [n][d] stored rows; M, phi, R: [F] outputs.  Returns 0, or -1 on bad arguments.
+ */
+int orc_calibrate(const void* q, int dtype, int64_t n, int d, double* M, double* phi, double* R) {
+    if (!q || n <= 0 || d <= 0 || (d & 1) || !M || !phi || !R) return -1;
+    const int F = d / 2;
+    for (int f = 0; f < F; ++f) {
+        double mag = 0.0, sre = 0.0, sim = 0.0, ure = 0.0, uim = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            const double re = stored_value(q, dtype, i * d + f);
+            const double im = stored_value(q, dtype, i * d + f + F);
+            const double r = hypot(re, im);
+            mag += r;
+            sre += re;
+            sim += im;
+            if (r > 0.0) {
+                ure += re / r;
+                uim += im / r;
+            }
+        }
+        M[f] = mag / (double)n;
+        phi[f] = (sre == 0.0 && sim == 0.0) ? 0.0 : atan2(sim, sre);
+        R[f] = hypot(ure, uim) / (double)n;
+    }
+    return 0;
+}

@@ -243,3 +243,80 @@ def test_prune_chain_tiny_shapes_and_budget_cases():
     assert np.all(r["A"][r["idx"]] >= thr)
     r2 = oracle.prune_segment(K, V, pos, t, cfg.theta, M, phi, R, cfg.offsets, 300)
     assert np.array_equal(r2["idx"], np.arange(300)) and np.array_equal(r2["V"], V)
+
+
+# ---------------------------------------------------------------- offline calibration
+# Centre magnitude M = mean |q_f|, phase phi = arg sum q_f, concentration R = mean
+# resultant length | mean q_f / |q_f| | of sampled pre-RoPE queries (band f = q[f] + i q[f+F]).
+
+def _band_rows(z):
+    """Rows [n][2F] (fp32) from complex bands z [n][F] in the half-split layout."""
+    return np.concatenate([z.real, z.imag], axis=1).astype(np.float32)
+
+
+def test_calibrate_identical_samples_are_fully_concentrated():
+    z = np.array([1.5 * np.exp(0.7j), 0.25 * np.exp(-2.0j), 3.0 * np.exp(3.0j)])
+    q = _band_rows(np.tile(z, (9, 1)))
+    M, phi, R = oracle.calibrate(q)
+    zs = q[0, :3].astype(np.float64) + 1j * q[0, 3:].astype(np.float64)
+    assert np.allclose(M, np.abs(zs), rtol=1e-15, atol=0)
+    assert np.allclose(phi, np.angle(zs), rtol=0, atol=1e-15)
+    assert np.allclose(R, 1.0, rtol=0, atol=1e-15)
+
+
+def test_calibrate_antipodal_pairs_have_zero_concentration():
+    z = np.array([[2.0 * np.exp(0.3j), 1.0 * np.exp(1.1j)],
+                  [-0.5 * np.exp(0.3j), -4.0 * np.exp(1.1j)]])
+    M, phi, R = oracle.calibrate(_band_rows(z))
+    assert np.allclose(R, 0.0, atol=1e-7)
+    assert np.allclose(M, [1.25, 2.5], rtol=1e-6)
+    # the sum points along the larger sample: band 0 along +e^{0.3i}, band 1 along -e^{1.1i}
+    assert abs(phi[0] - 0.3) < 1e-6 and abs(abs(phi[1] - 1.1) - np.pi) < 1e-6
+
+
+@pytest.mark.parametrize("a,phi0", [(0.4, 1.0), (1.2, -2.5), (np.pi / 2, 0.1)])
+def test_calibrate_symmetric_spread_gives_cosine_concentration(a, phi0):
+    """Equal-magnitude samples at phi0 +- a: R = cos a exactly, phase phi0."""
+    r = 1.75
+    z = np.array([[r * np.exp(1j * (phi0 + a))], [r * np.exp(1j * (phi0 - a))]] * 3)
+    M, phi, R = oracle.calibrate(_band_rows(z))
+    assert abs(R[0] - np.cos(a)) < 1e-6
+    assert abs(M[0] - r) < 1e-6
+    if np.cos(a) > 1e-3:
+        assert abs(phi[0] - phi0) < 1e-6
+
+
+def test_calibrate_zero_sample_counts_but_adds_no_direction():
+    z = np.array([[0.0 + 0.0j], [2.0 * np.exp(0.5j)]])
+    M, phi, R = oracle.calibrate(_band_rows(z))
+    assert abs(R[0] - 0.5) < 1e-7 and abs(M[0] - 1.0) < 1e-7 and abs(phi[0] - 0.5) < 1e-7
+    Mz, phz, Rz = oracle.calibrate(_band_rows(np.zeros((3, 2))))
+    assert np.all(Mz == 0.0) and np.all(phz == 0.0) and np.all(Rz == 0.0)
+
+
+def test_calibrate_scale_and_rotation():
+    rng = np.random.default_rng(4)
+    z = (1.0 + 0.2 * rng.standard_normal((64, 5))) * np.exp(1j * (0.3 + 0.5 * rng.standard_normal((64, 5))))
+    q = _band_rows(z)
+    M, phi, R = oracle.calibrate(q)
+    M2, phi2, R2 = oracle.calibrate(q * np.float32(2.0))        # exact scaling
+    assert np.array_equal(M2, 2.0 * M) and np.allclose(phi2, phi, atol=1e-15) and np.allclose(R2, R, atol=1e-15)
+    beta = 0.9
+    M3, phi3, R3 = oracle.calibrate(_band_rows(z * np.exp(1j * beta)))
+    assert np.allclose(M3, M, rtol=1e-6) and np.allclose(R3, R, atol=1e-6)
+    assert np.allclose(np.angle(np.exp(1j * (phi3 - phi - beta))), 0.0, atol=1e-6)
+
+
+def test_calibrate_half_split_pairing():
+    """Band f pairs element f with element f + F (not f with f + 1)."""
+    q = np.array([[3.0, 0.0, 0.0, 4.0]], dtype=np.float32)    # band 0 = 3 + 0i, band 1 = 0 + 4i
+    M, phi, R = oracle.calibrate(q)
+    assert np.allclose(M, [3.0, 4.0]) and np.allclose(phi, [0.0, np.pi / 2])
+
+
+def test_calibrate_bf16_matches_fp32_on_representable_values():
+    rng = np.random.default_rng(5)
+    q = (rng.integers(-64, 64, size=(40, 16)) / 16.0).astype(np.float32)   # exact in bf16
+    qb = (q.view(np.uint32) >> 16).astype(np.uint16)
+    for x, y in zip(oracle.calibrate(q), oracle.calibrate(qb)):
+        assert np.array_equal(x, y)
