@@ -197,13 +197,62 @@ def bench_decode_loop(args, T, W):
     print(json.dumps(result), flush=True)
 
 
+def bench_calibrate(args, T, W):
+    """Offline calibration from sampled pre-RoPE queries, Qwen3-8B-shaped: 36
+    layers x 4096 samples x 32 query heads x 128 dims, bf16.  A step is one
+    tri_calibrate over all of them (the samples are resident in HBM)."""
+    import torch
+    cfg = W.CONFIGS["qwen36l"]
+    n = 4096
+    q = W.query_samples(cfg, n, device="cuda")
+    L, _, Hq, d = q.shape
+    mag = torch.empty((L, Hq, d // 2), device="cuda")
+    phase, conc = torch.empty_like(mag), torch.empty_like(mag)
+    import ctypes
+    sz = ctypes.c_size_t(0)
+    T.load().tri_calibrate_workspace_size(L, n, Hq, d, ctypes.byref(sz))
+    ws = torch.empty(sz.value, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        T.tri_calibrate(q, mag, phase, conc, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    T.tri_timing_reset()
+    T.tri_timing_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        T.tri_calibrate(q, mag, phase, conc, ws=ws, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    T.tri_timing_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kt = T.tri_timing_read()
+    kernels = {k: {"avg_ms": round(v[1] / v[0], 4), "launches": v[0]} for k, v in kt.items() if v[0]}
+    alg = q.numel() * q.element_size() + 3 * mag.numel() * 4
+    part = kernels["calibrate"]["avg_ms"]
+    gbs = q.numel() * q.element_size() / (part * 1e-3) / 1e9
+    result = {
+        "metric": "query samples calibrated/sec (offline centre magnitude, phase and concentration)",
+        "value": round(L * n * Hq / (ms * 1e-3) / 1e9, 3), "unit": "G (sample, head) rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"calib: {L} layers x {n} samples x {Hq} query heads x {d} dims, bf16 pre-RoPE queries",
+                   "algorithmic_bytes": alg},
+        "roofline": {"bound": "hbm", "kernel": "calibrate", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "kernels": kernels,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l", "gptoss"],
-                    help="qwen36l (default): the pruning pass; gptoss: decode-loop windows")
+    ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l", "gptoss", "calib"],
+                    help="qwen36l (default): the pruning pass; gptoss: decode-loop windows; "
+                         "calib: offline calibration from query samples")
     ap.add_argument("--cpu-sample", type=int, default=16, help="oracle segments for the CPU baseline (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
@@ -227,6 +276,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "gptoss":
         bench_decode_loop(args, T, W)
+        return
+    if args.workload == "calib":
+        bench_calibrate(args, T, W)
         return
     cfg = W.CONFIGS[args.workload]
     B = cfg.budget

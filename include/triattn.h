@@ -110,6 +110,26 @@ int tri_calib_load(tri_calib_t* out, int n_layers, int n_q_heads, int n_kv_heads
 int tri_calib_free(tri_calib_t calib);
 
 /*
+ * Offline calibration statistics from sampled pre-RoPE queries ([YY] 主要方法:
+ * pre-RoPE queries gather around fixed non-zero centres, and a band's
+ * concentration is the mean resultant length R, closer to 1 meaning more
+ * concentrated).  For every layer, query head and band f (band = q[f] + i q[f+F]):
+ *   mag   = mean of |q_f|,
+ *   phase = arg of the sum of q_f (0 when that sum is 0),
+ *   conc  = | mean of q_f / |q_f| |   (a sample with q_f = 0 adds no direction).
+ *   q     : device [n_layers][n_samples][n_q_heads][head_dim], dtype TRI_DTYPE_*
+ *           (pre-RoPE rows: one per sampled token and query head).
+ *   mag, phase, conc : device fp32 [n_layers][n_q_heads][head_dim/2] outputs,
+ *           the layout tri_calib_load takes (copy them to the host for it).
+ *   ws    : device workspace of tri_calibrate_workspace_size bytes.
+ * Per-sample arithmetic is fp32 and the sums are fp64, added in a fixed order
+ * (results do not depend on scheduling).  head_dim 64 or 128.
+ */
+int tri_calibrate_workspace_size(int n_layers, int n_samples, int n_q_heads, int head_dim, size_t* bytes);
+int tri_calibrate(const void* q, int dtype, int n_layers, int n_samples, int n_q_heads, int head_dim, float* mag,
+                  float* phase, float* conc, void* ws, size_t ws_bytes, tri_stream_t stream);
+
+/*
  * Bytes of device workspace tri_score / tri_select_topb / tri_prune_window
  * need for this cache and budget (host-only; no device call).
  */

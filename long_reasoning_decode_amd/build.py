@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtriattn.so")
-SOURCES = ["api.hip", "score.hip", "select.hip", "decode.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "decode.hip", "calib.hip"]
 ARCH = os.environ.get("TRIATTN_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

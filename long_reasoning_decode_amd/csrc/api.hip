@@ -42,7 +42,7 @@ int64_t g_launches[KID_COUNT] = {};
 double g_ms[KID_COUNT] = {};
 const char* kKernelNames[KID_COUNT] = {"phase",  "score",  "zmax",   "select",         "select_gather",
                                        "gather", "append", "decode_attn", "sample", "score_fallback",
-                                       "select_fallback"};
+                                       "select_fallback", "calibrate", "calibrate_final"};
 
 void drain_timing_locked() {
     for (auto& p : g_pending) {
@@ -570,6 +570,48 @@ int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, floa
     a.n_seg = (int)n_segments(kv);
     return hip_status(launch_decode_attn(a, kv->head_dim, G, kv->dtype == TRI_DTYPE_BF16,
                                          static_cast<hipStream_t>(stream)), "decode attention kernel");
+}
+
+static int check_calib_shape(int n_layers, int n_samples, int n_q_heads, int head_dim) {
+    if (n_layers < 1 || n_samples < 1 || n_q_heads < 1 || head_dim <= 0 || (head_dim & 1)) return TRI_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return TRI_ERR_UNSUPPORTED;
+    return TRI_OK;
+}
+
+static size_t calib_ws_bytes(int n_layers, int n_samples, int n_q_heads, int head_dim) {
+    const int64_t chunks = (n_samples + kCalibChunk - 1) / kCalibChunk;
+    return align256((size_t)n_layers * chunks * n_q_heads * (head_dim / 2) * 5 * sizeof(double));
+}
+
+int tri_calibrate_workspace_size(int n_layers, int n_samples, int n_q_heads, int head_dim, size_t* bytes) {
+    if (!bytes) return TRI_ERR_INVALID_ARG;
+    const int rc = check_calib_shape(n_layers, n_samples, n_q_heads, head_dim);
+    if (rc) return rc;
+    *bytes = calib_ws_bytes(n_layers, n_samples, n_q_heads, head_dim);
+    return TRI_OK;
+}
+
+int tri_calibrate(const void* q, int dtype, int n_layers, int n_samples, int n_q_heads, int head_dim, float* mag,
+                  float* phase, float* conc, void* ws, size_t ws_bytes, tri_stream_t stream) {
+    int rc = check_calib_shape(n_layers, n_samples, n_q_heads, head_dim);
+    if (rc) return rc;
+    if (!q || !mag || !phase || !conc) return TRI_ERR_INVALID_ARG;
+    if (dtype != TRI_DTYPE_F32 && dtype != TRI_DTYPE_BF16) return TRI_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < calib_ws_bytes(n_layers, n_samples, n_q_heads, head_dim)) return TRI_ERR_WORKSPACE;
+    if (!device_present()) return TRI_ERR_NO_DEVICE;
+    CalibArgs a;
+    a.q = static_cast<const uint8_t*>(q);
+    a.part = static_cast<double*>(ws);
+    a.mag = mag;
+    a.phase = phase;
+    a.conc = conc;
+    a.n_layers = n_layers;
+    a.n_samples = n_samples;
+    a.n_q_heads = n_q_heads;
+    a.head_dim = head_dim;
+    a.n_chunks = (n_samples + kCalibChunk - 1) / kCalibChunk;
+    return hip_status(launch_calibrate(a, dtype == TRI_DTYPE_BF16, static_cast<hipStream_t>(stream)),
+                      "calibration kernel");
 }
 
 int tri_timing_enable(int enable) {

@@ -21,6 +21,8 @@ enum KernelId : int {
     KID_SAMPLE,
     KID_SCORE_FALLBACK,
     KID_SELECT_FALLBACK,
+    KID_CALIB,
+    KID_CALIB_FINAL,
     KID_COUNT
 };
 
@@ -183,5 +185,17 @@ struct AttnArgs {
 };
 hipError_t launch_decode_attn(const AttnArgs& a, int head_dim, int group, bool bf16,
                               hipStream_t stream);
+
+// --- offline calibration from sampled pre-RoPE queries
+constexpr int kCalibChunk = 256;           // samples per pass-1 workgroup
+struct CalibArgs {
+    const uint8_t* q;       // [L][n_samples][Hq][d] stored rows
+    double* part;           // [L][n_chunks][Hq][F][5] fp64 partial sums
+    float* mag;             // [L][Hq][F]
+    float* phase;
+    float* conc;
+    int32_t n_layers, n_samples, n_q_heads, head_dim, n_chunks;
+};
+hipError_t launch_calibrate(const CalibArgs& a, bool bf16, hipStream_t stream);
 
 }  // namespace tri

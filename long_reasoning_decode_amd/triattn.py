@@ -30,7 +30,7 @@ EXPORTS = (
     "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
     "tri_compact", "tri_prune_window", "tri_append", "tri_decode_attn", "tri_strerror",
     "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name", "tri_last_error",
-    "tri_prune_fallbacks",
+    "tri_prune_fallbacks", "tri_calibrate_workspace_size", "tri_calibrate",
 )
 
 
@@ -86,6 +86,8 @@ def load():
         "tri_timing_name": [I],
         "tri_last_error": [],
         "tri_prune_fallbacks": [P, SZ, ctypes.POINTER(I32), P],
+        "tri_calibrate_workspace_size": [I, I, I, I, ctypes.POINTER(SZ)],
+        "tri_calibrate": [P, I, I, I, I, I, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -216,6 +218,22 @@ def tri_prune_window(calib, src, t, budget, dst, n_kept, ws, stream=None):
     rc = load().tri_prune_window(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
                                  _p(n_kept), _p(ws), ws.numel(), _stream(stream))
     _check("tri_prune_window", rc)
+
+
+def tri_calibrate(q, mag, phase, conc, ws=None, stream=None):
+    """q: device [L, n_samples, Hq, d] pre-RoPE rows (bf16 or fp32); mag, phase,
+    conc: device fp32 [L, Hq, d/2] outputs.  Allocates the workspace when none is given."""
+    L, n, Hq, d = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    lib = load()
+    need = ctypes.c_size_t(0)
+    _check("tri_calibrate_workspace_size", lib.tri_calibrate_workspace_size(L, n, Hq, d, ctypes.byref(need)))
+    if ws is None:
+        ws = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    rc = lib.tri_calibrate(_p(q), _dtype_code(q.dtype), L, n, Hq, d, _p(mag), _p(phase), _p(conc), _p(ws), ws.numel(),
+                           _stream(stream))
+    _check("tri_calibrate", rc)
 
 
 def tri_prune_fallbacks(ws, stream=None):

@@ -160,3 +160,23 @@ def test_valid_calls_report_no_device():
 
 def test_calib_free_null_is_noop():
     assert T.load().tri_calib_free(None) == 0
+
+
+def test_calibrate_validation():
+    lib = T.load()
+    q = torch.zeros(2, 10, 4, 64)
+    out = torch.zeros(2, 4, 32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    n = ctypes.c_size_t(0)
+    assert lib.tri_calibrate_workspace_size(2, 10, 4, 64, ctypes.byref(n)) == T.TRI_OK and n.value > 0
+    assert lib.tri_calibrate_workspace_size(2, 10, 4, 63, ctypes.byref(n)) == T.TRI_ERR_INVALID_ARG
+    assert lib.tri_calibrate_workspace_size(2, 10, 4, 96, ctypes.byref(n)) == T.TRI_ERR_UNSUPPORTED
+    assert lib.tri_calibrate_workspace_size(0, 10, 4, 64, ctypes.byref(n)) == T.TRI_ERR_INVALID_ARG
+    cal = lambda *, dt=T.TRI_DTYPE_F32, L=2, ns=10, qp=T._p(q), wb=ws.numel(): lib.tri_calibrate(
+        qp, dt, L, ns, 4, 64, T._p(out), T._p(out), T._p(out), T._p(ws), wb, None)
+    assert cal(dt=5) == T.TRI_ERR_INVALID_ARG
+    assert cal(ns=0) == T.TRI_ERR_INVALID_ARG
+    assert cal(qp=None) == T.TRI_ERR_INVALID_ARG
+    assert cal(wb=16) == T.TRI_ERR_WORKSPACE
+    if not torch.cuda.is_available():
+        assert cal() == T.TRI_ERR_NO_DEVICE

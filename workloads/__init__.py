@@ -339,3 +339,18 @@ def synthetic_scores(n_seg: int, capacity: int, seed: int = 0):
         elif kind == 3 and s % 8 == 3:
             A[s] = 1.5
     return A
+
+
+def query_samples(cfg: Config, n_samples: int, device="cpu", sigma: float = 0.3, seed_tag: int = 7000):
+    """Sampled pre-RoPE queries [L][n_samples][Hq][d] in the storage dtype: per
+    band, the calibration centre M e^{i phi} plus complex Gaussian noise of
+    std sigma per component (half-split layout)."""
+    F = cfg.head_dim // 2
+    cal = calibration(cfg)
+    M = cal["mag"].to(device, torch.float64)[:, None]            # [L][1][Hq][F]
+    ph = cal["phase"].to(device, torch.float64)[:, None]
+    g = _gen(device, cfg.seed, seed_tag)
+    shape = (cfg.n_layers, n_samples, cfg.n_q_heads, F)
+    re = M * torch.cos(ph) + sigma * torch.randn(shape, generator=g, device=device, dtype=torch.float64)
+    im = M * torch.sin(ph) + sigma * torch.randn(shape, generator=g, device=device, dtype=torch.float64)
+    return _pack(re, im, cfg.dtype)
