@@ -26,6 +26,11 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32 = 0
 BF16 = 1
+# score variants (orc_score_segment_variant): the ablated components and the R-weighted centre reading
+VAR_TRIG_ONLY = 1
+VAR_NORM_ONLY = 2
+VAR_FIXED_WEIGHT = 4
+VAR_R_WEIGHTED_TRIG = 8
 
 _lib = None
 
@@ -51,6 +56,7 @@ def _load():
     i32 = ctypes.c_int
     dbl = ctypes.c_double
     lib.orc_score_segment.argtypes = [P, i32, P, i64, i32, dbl, i64, P, P, P, i32, P, i32, P, P, P]
+    lib.orc_score_segment_variant.argtypes = [P, i32, P, i64, i32, dbl, i64, P, P, P, i32, P, i32, i32, P, P, P]
     lib.orc_zscore_max.argtypes = [P, i32, i64, P, P, P]
     lib.orc_select_topb.argtypes = [P, i64, i64, P, P]
     lib.orc_select_topb_f32.argtypes = [P, i64, i64, P, P]
@@ -60,7 +66,7 @@ def _load():
     lib.orc_calibrate.argtypes = [P, i32, i64, i32, P, P, P]
     for fn in (lib.orc_score_segment, lib.orc_zscore_max, lib.orc_select_topb,
                lib.orc_select_topb_f32, lib.orc_gather_rows, lib.orc_paged_rows,
-               lib.orc_decode_attn, lib.orc_calibrate):
+               lib.orc_decode_attn, lib.orc_calibrate, lib.orc_score_segment_variant):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -85,8 +91,9 @@ def _check(rc: int, what: str):
         raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
 
 
-def score_segment(K, pos, t, theta, M, phi, R, offsets, parts=False):
-    """S [G][N] (fp64) for one segment.  K: [N][d] stored rows; M, phi, R: [G][F]."""
+def score_segment(K, pos, t, theta, M, phi, R, offsets, parts=False, variant=0):
+    """S [G][N] (fp64) for one segment.  K: [N][d] stored rows; M, phi, R: [G][F];
+    variant: VAR_* flags (0 = the method as read)."""
     lib = _load()
     K, dt = _stored(K)
     N, d = K.shape
@@ -101,9 +108,9 @@ def score_segment(K, pos, t, theta, M, phi, R, offsets, parts=False):
     S = np.empty((G, N), dtype=np.float64)
     trig = np.empty((G, N), dtype=np.float64) if parts else None
     norm = np.empty((G, N), dtype=np.float64) if parts else None
-    rc = lib.orc_score_segment(_ptr(K), dt, _ptr(pos), N, d, float(theta), int(t), _ptr(M),
-                               _ptr(phi), _ptr(R), G, _ptr(offs), len(offs), _ptr(S),
-                               _ptr(trig) if parts else None, _ptr(norm) if parts else None)
+    rc = lib.orc_score_segment_variant(_ptr(K), dt, _ptr(pos), N, d, float(theta), int(t), _ptr(M),
+                                       _ptr(phi), _ptr(R), G, _ptr(offs), len(offs), int(variant), _ptr(S),
+                                       _ptr(trig) if parts else None, _ptr(norm) if parts else None)
     _check(rc, "score_segment")
     return (S, trig, norm) if parts else S
 
@@ -187,9 +194,9 @@ def calibrate(q):
     return M, phi, R
 
 
-def prune_segment(K, V, pos, t, theta, M, phi, R, offsets, B):
+def prune_segment(K, V, pos, t, theta, M, phi, R, offsets, B, variant=0):
     """The whole path for one segment: scores, z/max, top-B, compaction."""
-    S = score_segment(K, pos, t, theta, M, phi, R, offsets)
+    S = score_segment(K, pos, t, theta, M, phi, R, offsets, variant=variant)
     mu, sigma, A = zscore_max(S)
     idx = select_topb(A, B)
     return {

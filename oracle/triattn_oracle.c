@@ -70,11 +70,34 @@ static double stored_value(const void* base, int dtype, int64_t i) {
  * S: [G][N] output.  trig_out / norm_out: optional [G][N] outputs of the two
  * parts.  Returns 0, or -1 on bad arguments.
  */
+/* Score variants (the ablated components the pages name, [YY] 主实验结果: the
+ * trigonometric score, the adaptive weighting and the geometric offsets; plus
+ * the alternative reading of the centre magnitude).  Linear offsets need no
+ * flag: they are a different offset set. */
+#define ORC_VAR_TRIG_ONLY 1        /* drop the norm term                        */
+#define ORC_VAR_NORM_ONLY 2        /* drop the trigonometric term               */
+#define ORC_VAR_FIXED_WEIGHT 4     /* norm weight M instead of (1 - R) M        */
+#define ORC_VAR_R_WEIGHTED_TRIG 8  /* trigonometric term with R M instead of M  */
+
+int orc_score_segment_variant(const void* K, int dtype, const int32_t* pos, int64_t N, int d,
+                              double theta, int64_t t, const float* M, const float* phi,
+                              const float* R, int G, const int64_t* offsets, int n_off, int variant,
+                              double* S, double* trig_out, double* norm_out);
+
 int orc_score_segment(const void* K, int dtype, const int32_t* pos, int64_t N, int d,
                       double theta, int64_t t, const float* M, const float* phi,
                       const float* R, int G, const int64_t* offsets, int n_off,
                       double* S, double* trig_out, double* norm_out) {
+    return orc_score_segment_variant(K, dtype, pos, N, d, theta, t, M, phi, R, G, offsets, n_off, 0, S, trig_out,
+                                     norm_out);
+}
+
+int orc_score_segment_variant(const void* K, int dtype, const int32_t* pos, int64_t N, int d,
+                              double theta, int64_t t, const float* M, const float* phi,
+                              const float* R, int G, const int64_t* offsets, int n_off, int variant,
+                              double* S, double* trig_out, double* norm_out) {
     if (d <= 0 || (d & 1) || G <= 0 || n_off <= 0 || N < 0) return -1;
+    if ((variant & ~15) || ((variant & ORC_VAR_TRIG_ONLY) && (variant & ORC_VAR_NORM_ONLY))) return -1;
     const int F = d / 2;
     double* w = (double*)malloc(sizeof(double) * F);
     double* mag = (double*)malloc(sizeof(double) * F);
@@ -102,13 +125,20 @@ int orc_score_segment(const void* K, int dtype, const int32_t* pos, int64_t N, i
             double trig = 0.0;
             for (int o = 0; o < n_off; ++o) {
                 const double delta = (double)(t + offsets[o]) - p;
-                for (int f = 0; f < F; ++f)
-                    trig += (double)Mh[f] * mag[f] * cos(w[f] * delta + (double)ph[f] - psi[f]);
+                for (int f = 0; f < F; ++f) {
+                    const double c = (variant & ORC_VAR_R_WEIGHTED_TRIG) ? (double)Rh[f] * (double)Mh[f] : (double)Mh[f];
+                    trig += c * mag[f] * cos(w[f] * delta + (double)ph[f] - psi[f]);
+                }
             }
             trig /= (double)n_off;
             /* step 3 */
             double norm = 0.0;
-            for (int f = 0; f < F; ++f) norm += (1.0 - (double)Rh[f]) * (double)Mh[f] * mag[f];
+            for (int f = 0; f < F; ++f) {
+                const double wt = (variant & ORC_VAR_FIXED_WEIGHT) ? 1.0 : 1.0 - (double)Rh[f];
+                norm += wt * (double)Mh[f] * mag[f];
+            }
+            if (variant & ORC_VAR_TRIG_ONLY) norm = 0.0;
+            if (variant & ORC_VAR_NORM_ONLY) trig = 0.0;
             /* step 4 */
             S[(int64_t)h * N + i] = trig + norm;
             if (trig_out) trig_out[(int64_t)h * N + i] = trig;

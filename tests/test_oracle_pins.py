@@ -320,3 +320,62 @@ def test_calibrate_bf16_matches_fp32_on_representable_values():
     qb = (q.view(np.uint32) >> 16).astype(np.uint16)
     for x, y in zip(oracle.calibrate(q), oracle.calibrate(qb)):
         assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------- score variants
+# The ablated components ([YY] 主实验结果: trigonometric score, adaptive weighting,
+# geometric offsets) and the R-weighted centre reading, each pinned to the
+# method as read by an exact relation.
+
+def _variant_case(seed=9, d=64, G=3, N=40):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((N, d)).astype(np.float32)
+    pos = np.sort(rng.choice(5000, N, replace=False)).astype(np.int32)
+    M = rng.uniform(0.5, 2.0, (G, d // 2)).astype(np.float32)
+    phi = rng.uniform(0, 2 * np.pi, (G, d // 2)).astype(np.float32)
+    R = np.array(rng.choice([0.125, 0.5, 0.875], (G, d // 2)), dtype=np.float32)
+    return K, pos, M, phi, R
+
+
+def test_variant_trig_only_plus_norm_only_is_the_method():
+    K, pos, M, phi, R = _variant_case()
+    args = (K, pos, 5100, 1e4, M, phi, R, [1, 2, 4, 8, 16])
+    S, trig, norm = oracle.score_segment(*args, parts=True)
+    St = oracle.score_segment(*args, variant=oracle.VAR_TRIG_ONLY)
+    Sn = oracle.score_segment(*args, variant=oracle.VAR_NORM_ONLY)
+    assert np.array_equal(St, trig) and np.array_equal(Sn, norm)
+    assert np.allclose(St + Sn, S, rtol=1e-14, atol=1e-12)
+
+
+def test_variant_fixed_weight_reduces_to_the_method_at_zero_concentration():
+    K, pos, M, phi, _ = _variant_case(seed=10)
+    R0 = np.zeros_like(M)
+    args = (K, pos, 5100, 1e4, M, phi)
+    assert np.array_equal(oracle.score_segment(*args, R0, [1, 4, 16], variant=oracle.VAR_FIXED_WEIGHT),
+                          oracle.score_segment(*args, R0, [1, 4, 16]))
+    # and its norm term is the plain magnitude-weighted band norm
+    R = _variant_case(seed=10)[4]
+    Sf = oracle.score_segment(*args, R, [1], variant=oracle.VAR_FIXED_WEIGHT | oracle.VAR_NORM_ONLY)
+    F = K.shape[1] // 2
+    bandnorm = np.hypot(K[:, :F].astype(np.float64), K[:, F:].astype(np.float64))
+    assert np.allclose(Sf, M.astype(np.float64) @ bandnorm.T, rtol=1e-13)
+
+
+def test_variant_r_weighted_trig_is_the_method_at_full_concentration_and_scales_with_r():
+    K, pos, M, phi, _ = _variant_case(seed=11)
+    args = (K, pos, 5100, 1e4, M, phi)
+    R1 = np.ones_like(M)
+    assert np.array_equal(oracle.score_segment(*args, R1, [1, 2, 4], variant=oracle.VAR_R_WEIGHTED_TRIG),
+                          oracle.score_segment(*args, R1, [1, 2, 4]))
+    Rh = np.full_like(M, 0.5)
+    Stw = oracle.score_segment(*args, Rh, [1, 2, 4], variant=oracle.VAR_R_WEIGHTED_TRIG | oracle.VAR_TRIG_ONLY)
+    St = oracle.score_segment(*args, Rh, [1, 2, 4], variant=oracle.VAR_TRIG_ONLY)
+    assert np.allclose(Stw, 0.5 * St, rtol=1e-13, atol=1e-12)
+
+
+def test_variant_flags_are_checked():
+    K, pos, M, phi, R = _variant_case()
+    with pytest.raises(ValueError):
+        oracle.score_segment(K, pos, 5100, 1e4, M, phi, R, [1], variant=oracle.VAR_TRIG_ONLY | oracle.VAR_NORM_ONLY)
+    with pytest.raises(ValueError):
+        oracle.score_segment(K, pos, 5100, 1e4, M, phi, R, [1], variant=16)
