@@ -106,6 +106,27 @@ int tri_calib_load(tri_calib_t* out, int n_layers, int n_q_heads, int n_kv_heads
                    double rope_theta, const float* mag, const float* phase, const float* conc,
                    const int32_t* offsets, int n_offsets, tri_stream_t stream);
 
+/*
+ * Score variants ([YY] 主实验结果: the ablations name the trigonometric score,
+ * the adaptive weighting and the geometric offsets as key components), folded
+ * into the handle at load time, so every entry point scores with them:
+ *   TRI_VARIANT_TRIG_ONLY        drop the norm term
+ *   TRI_VARIANT_NORM_ONLY        drop the trigonometric term (not with TRIG_ONLY)
+ *   TRI_VARIANT_FIXED_WEIGHT     norm weight M instead of (1 - R) M
+ *   TRI_VARIANT_R_WEIGHTED_TRIG  trigonometric term with centre magnitude R M
+ *                                (the reading |E q_f| = R mean |q_f|)
+ * Linear instead of geometric offsets need no flag: pass that offset set.
+ * variant 0 is tri_calib_load.  Any other bit, or TRIG_ONLY with NORM_ONLY,
+ * gives TRI_ERR_INVALID_ARG.
+ */
+#define TRI_VARIANT_TRIG_ONLY 1
+#define TRI_VARIANT_NORM_ONLY 2
+#define TRI_VARIANT_FIXED_WEIGHT 4
+#define TRI_VARIANT_R_WEIGHTED_TRIG 8
+int tri_calib_load_ex(tri_calib_t* out, int n_layers, int n_q_heads, int n_kv_heads, int head_dim,
+                      double rope_theta, const float* mag, const float* phase, const float* conc,
+                      const int32_t* offsets, int n_offsets, int variant, tri_stream_t stream);
+
 /* Releases a handle (NULL is a no-op).  Waits for the device to be idle. */
 int tri_calib_free(tri_calib_t calib);
 

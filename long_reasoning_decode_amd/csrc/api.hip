@@ -272,7 +272,18 @@ const char* tri_strerror(int code) {
 int tri_calib_load(tri_calib_t* out, int n_layers, int n_q_heads, int n_kv_heads, int head_dim,
                    double rope_theta, const float* mag, const float* phase, const float* conc,
                    const int32_t* offsets, int n_offsets, tri_stream_t stream) {
+    return tri_calib_load_ex(out, n_layers, n_q_heads, n_kv_heads, head_dim, rope_theta, mag, phase, conc, offsets,
+                             n_offsets, 0, stream);
+}
+
+int tri_calib_load_ex(tri_calib_t* out, int n_layers, int n_q_heads, int n_kv_heads, int head_dim,
+                      double rope_theta, const float* mag, const float* phase, const float* conc,
+                      const int32_t* offsets, int n_offsets, int variant, tri_stream_t stream) {
     if (!out || n_layers < 1 || n_q_heads < 1 || n_kv_heads < 1 || head_dim <= 0 || (head_dim & 1))
+        return TRI_ERR_INVALID_ARG;
+    if ((variant & ~(TRI_VARIANT_TRIG_ONLY | TRI_VARIANT_NORM_ONLY | TRI_VARIANT_FIXED_WEIGHT |
+                     TRI_VARIANT_R_WEIGHTED_TRIG)) ||
+        ((variant & TRI_VARIANT_TRIG_ONLY) && (variant & TRI_VARIANT_NORM_ONLY)))
         return TRI_ERR_INVALID_ARG;
     if (n_q_heads % n_kv_heads) return TRI_ERR_INVALID_ARG;
     if (!(rope_theta > 0.0) || !isfinite(rope_theta)) return TRI_ERR_INVALID_ARG;
@@ -305,10 +316,14 @@ int tri_calib_load(tri_calib_t* out, int n_layers, int n_q_heads, int n_kv_heads
     std::vector<float> wn((size_t)n);
     for (int64_t i = 0; i < n; ++i) {
         const int f = (int)(i % F);
-        const double cr = (double)mag[i] * cos((double)phase[i]);
-        const double ci = (double)mag[i] * sin((double)phase[i]);
+        double m = (double)mag[i];
+        if (variant & TRI_VARIANT_R_WEIGHTED_TRIG) m *= (double)conc[i];
+        if (variant & TRI_VARIANT_NORM_ONLY) m = 0.0;
+        const double cr = m * cos((double)phase[i]);
+        const double ci = m * sin((double)phase[i]);
         P[i] = make_double2(cr * A[f].x - ci * A[f].y, cr * A[f].y + ci * A[f].x);
-        wn[i] = (float)((1.0 - (double)conc[i]) * (double)mag[i]);
+        const double wt = (variant & TRI_VARIANT_FIXED_WEIGHT) ? 1.0 : 1.0 - (double)conc[i];
+        wn[i] = (variant & TRI_VARIANT_TRIG_ONLY) ? 0.0f : (float)(wt * (double)mag[i]);
     }
 
     tri_calib_s* c = new (std::nothrow) tri_calib_s();

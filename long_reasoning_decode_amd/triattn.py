@@ -25,12 +25,16 @@ TRI_DTYPE_F32 = 0
 TRI_DTYPE_BF16 = 1
 TRI_LAYOUT_DENSE = 0
 TRI_LAYOUT_PAGED = 1
+TRI_VARIANT_TRIG_ONLY = 1
+TRI_VARIANT_NORM_ONLY = 2
+TRI_VARIANT_FIXED_WEIGHT = 4
+TRI_VARIANT_R_WEIGHTED_TRIG = 8
 
 EXPORTS = (
     "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
     "tri_compact", "tri_prune_window", "tri_append", "tri_decode_attn", "tri_strerror",
     "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name", "tri_last_error",
-    "tri_prune_fallbacks", "tri_calibrate_workspace_size", "tri_calibrate",
+    "tri_prune_fallbacks", "tri_calibrate_workspace_size", "tri_calibrate", "tri_calib_load_ex",
 )
 
 
@@ -71,6 +75,7 @@ def load():
     DP = ctypes.POINTER(CacheDesc)
     sig = {
         "tri_calib_load": [ctypes.POINTER(P), I, I, I, I, D, P, P, P, P, I, P],
+        "tri_calib_load_ex": [ctypes.POINTER(P), I, I, I, I, D, P, P, P, P, I, I, P],
         "tri_calib_free": [P],
         "tri_workspace_size": [P, DP, I, ctypes.POINTER(SZ)],
         "tri_score": [P, DP, P, P, P, P, P, SZ, P],
@@ -169,8 +174,9 @@ class Calib:
             pass
 
 
-def tri_calib_load(mag, phase, conc, offsets, *, n_kv_heads, rope_theta, stream=None):
-    """mag/phase/conc: host fp32 [L, Hq, F]; offsets: host int32 [n_off]."""
+def tri_calib_load(mag, phase, conc, offsets, *, n_kv_heads, rope_theta, variant=0, stream=None):
+    """mag/phase/conc: host fp32 [L, Hq, F]; offsets: host int32 [n_off];
+    variant: TRI_VARIANT_* flags (tri_calib_load_ex), 0 = the method as read."""
     lib = load()
     mag = mag.detach().to("cpu", torch.float32).contiguous()
     phase = phase.detach().to("cpu", torch.float32).contiguous()
@@ -178,9 +184,9 @@ def tri_calib_load(mag, phase, conc, offsets, *, n_kv_heads, rope_theta, stream=
     offsets = torch.as_tensor(offsets, dtype=torch.int32).contiguous()
     L, Hq, F = mag.shape
     h = ctypes.c_void_p()
-    rc = lib.tri_calib_load(ctypes.byref(h), L, Hq, n_kv_heads, 2 * F, float(rope_theta), _p(mag),
-                            _p(phase), _p(conc), _p(offsets), int(offsets.numel()), _stream(stream))
-    _check("tri_calib_load", rc)
+    rc = lib.tri_calib_load_ex(ctypes.byref(h), L, Hq, n_kv_heads, 2 * F, float(rope_theta), _p(mag),
+                               _p(phase), _p(conc), _p(offsets), int(offsets.numel()), int(variant), _stream(stream))
+    _check("tri_calib_load_ex", rc)
     return Calib(h, L, Hq, n_kv_heads, 2 * F)
 
 

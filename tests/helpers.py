@@ -29,10 +29,10 @@ def log(msg):
     sys.stdout.flush()
 
 
-def calib_for(T, cfg):
+def calib_for(T, cfg, variant=0):
     cal = W.calibration(cfg)
     c = T.tri_calib_load(cal["mag"], cal["phase"], cal["conc"], cal["offsets"],
-                         n_kv_heads=cfg.n_kv_heads, rope_theta=cfg.theta)
+                         n_kv_heads=cfg.n_kv_heads, rope_theta=cfg.theta, variant=variant)
     return c, cal
 
 
@@ -67,10 +67,10 @@ def seg_seq(cfg, s):
     return (s // cfg.n_kv_heads) % cfg.n_seq
 
 
-def oracle_segment(cfg, cal, K, V, pos, t, s, B, layer0=0):
+def oracle_segment(cfg, cal, K, V, pos, t, s, B, layer0=0, variant=0):
     """Oracle prune of one segment from its stored rows (numpy, already CPU)."""
     M, phi, R = seg_calib(cal, cfg, s, layer0)
-    return oracle.prune_segment(K, V, pos, t, cfg.theta, M, phi, R, cfg.offsets, B)
+    return oracle.prune_segment(K, V, pos, t, cfg.theta, M, phi, R, cfg.offsets, B, variant=variant)
 
 
 def check_scores(S_gpu, S_ref, what=""):

@@ -158,6 +158,19 @@ def test_valid_calls_report_no_device():
     assert lib.tri_decode_attn(ctypes.byref(d), 3, T._p(q), 0.125, T._p(out), None) == T.TRI_ERR_INVALID_ARG
 
 
+def test_calib_variant_validation():
+    lib = T.load()
+    m, ph, r, o = _calib_args()
+    h = ctypes.c_void_p()
+    rc = lambda v: lib.tri_calib_load_ex(ctypes.byref(h), 2, 8, 2, 64, 1e4, T._p(m), T._p(ph), T._p(r), T._p(o),
+                                         o.numel(), v, None)
+    assert rc(T.TRI_VARIANT_TRIG_ONLY | T.TRI_VARIANT_NORM_ONLY) == T.TRI_ERR_INVALID_ARG
+    assert rc(16) == T.TRI_ERR_INVALID_ARG
+    assert rc(-1) == T.TRI_ERR_INVALID_ARG
+    if not torch.cuda.is_available():
+        assert rc(T.TRI_VARIANT_FIXED_WEIGHT | T.TRI_VARIANT_R_WEIGHTED_TRIG) == T.TRI_ERR_NO_DEVICE
+
+
 def test_calib_free_null_is_noop():
     assert T.load().tri_calib_free(None) == 0
 

@@ -45,7 +45,7 @@ def _run_unfused(T, cfg, g, calib, B):
                 out2=_to(out2, "cpu"), nk2=nk2.cpu(), fallbacks=fallbacks)
 
 
-def _check_all(cfg, cal, cpu, r, B, lengths, what):
+def _check_all(cfg, cal, cpu, r, B, lengths, what, variant=0):
     """Oracle on every segment of a small dense cache, all steps."""
     n_seg = cpu["k"].shape[0]
     for s in range(n_seg):
@@ -57,7 +57,7 @@ def _check_all(cfg, cal, cpu, r, B, lengths, what):
             continue
         K, V = stored(cpu["k"][s, :N]), stored(cpu["v"][s, :N])
         P = cpu["pos"][s, :N].numpy()
-        ref = oracle_segment(cfg, cal, K, V, P, t, s, B)
+        ref = oracle_segment(cfg, cal, K, V, P, t, s, B, variant=variant)
         check_scores(r["scores"][s, :, :N].numpy(), ref["S"], tag)
         check_mu_sigma(r["ms"][s].numpy(), ref["mu"], ref["sigma"], tag)
         check_agg(r["agg"][s, :N].numpy(), ref["A"], tag)
@@ -340,3 +340,29 @@ def test_candidate_pass_overflow_falls_back(gpu_lib):
     assert r["fallbacks"] == 1
     assert torch.equal(r["out2"]["v"][0], cpu["v"][0, :900])
     _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "candidate overflow")
+
+
+# ---------------------------------------------------------------- score variants
+VARIANTS = {
+    "trig_only": (1, 1), "norm_only": (2, 2), "fixed_weight": (4, 4), "r_weighted_trig": (8, 8),
+    "trig_only_r_weighted": (9, 9),
+}
+
+
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_score_variants_every_step(gpu_lib, name):
+    """Each variant through the unfused chain and the fused pass (candidate mode
+    included: N = 9000 >= 8B) against the oracle with the same flags; the
+    linear-offset ablation is a different offset set."""
+    T = gpu_lib
+    lib_flag, orc_flag = VARIANTS[name]
+    B = 800
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, dtype=torch.bfloat16, theta=1e6, n_kv_heads=2, n_seq=1,
+                                    n_keys=9000, t=9000, budget=B, sigma=None, seed=21,
+                                    offsets=tuple(range(1, 17)) if name == "r_weighted_trig" else W.geometric(16))
+    log(f"case variant {name}")
+    cpu = W.dense_cache(cfg, "cpu")
+    calib, cal = calib_for(T, cfg, variant=lib_flag)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
+    log(f"  fallbacks: {r['fallbacks']}")
+    _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), f"variant {name}", variant=orc_flag)
