@@ -234,7 +234,8 @@ int tri_append(const tri_cache_desc* kv, const void* k_new, const void* v_new,
  * sequence and query head ([ZN] 长推理的内存困境: each decode step re-attends
  * to the whole cache):  out = softmax(scale * q . K^T) V over the segment's
  * valid keys.  q : device [n_layers][n_seq][n_q_heads][head_dim] (cache dtype);
- * out : device fp32, same shape.  Dense caches only; lengths[s] >= 1.
+ * out : device fp32, same shape.  Dense or paged caches (a pruned paged cache
+ * is read in place through its page table); lengths[s] >= 1.
  */
 int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, float scale, float* out,
                     tri_stream_t stream);

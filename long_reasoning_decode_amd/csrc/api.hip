@@ -570,7 +570,6 @@ int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, floa
     int rc = check_cache(kv);
     if (rc) return rc;
     if (!q || !out || n_q_heads < 1 || n_q_heads % kv->n_kv_heads || !isfinite(scale)) return TRI_ERR_INVALID_ARG;
-    if (kv->layout != TRI_LAYOUT_DENSE) return TRI_ERR_UNSUPPORTED;
     const int G = n_q_heads / kv->n_kv_heads;
     if (!supported_group(G)) return TRI_ERR_UNSUPPORTED;
     if (!device_present()) return TRI_ERR_NO_DEVICE;

@@ -166,6 +166,24 @@ def test_ragged_paged_full(gpu_lib):
                          oracle.paged_rows(OVp, opt[s], cfg.page_size, nks), Pd, Pd, tag)
         log(f"  {tag} ok")
 
+    # decode attention reading the pruned pages in place
+    gq = torch.Generator().manual_seed(5)
+    q = torch.randn((1, cfg.n_seq, cfg.n_q_heads, cfg.head_dim), generator=gq).to(cfg.dtype)
+    out = torch.full(q.shape, float("nan"), device="cuda")
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    T.tri_decode_attn(dst, cfg.n_q_heads, q.cuda(), scale, out)
+    torch.cuda.synchronize()
+    for s in sample:
+        nks = min(int(lengths[s]), B)
+        b, h = seg_seq(cfg, s), s % cfg.n_kv_heads
+        hs = slice(h * cfg.group, (h + 1) * cfg.group)
+        ref = oracle.decode_attn(stored(q[0, b, hs]), oracle.paged_rows(OKp, opt[s], cfg.page_size, nks),
+                                 oracle.paged_rows(OVp, opt[s], cfg.page_size, nks), scale)
+        got = out[0, b, hs].cpu().numpy()
+        err = np.abs(got - ref) / np.maximum(np.abs(ref), np.abs(ref).max(axis=1, keepdims=True))
+        assert err.max() <= 1e-4, f"ragged paged attention seg {s}: {err.max():.2e}"
+    log("  paged decode attention over the pruned pages ok")
+
 
 def test_gptoss_decode_loop_full(gpu_lib):
     T = gpu_lib

@@ -366,3 +366,42 @@ def test_score_variants_every_step(gpu_lib, name):
     r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
     log(f"  fallbacks: {r['fallbacks']}")
     _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), f"variant {name}", variant=orc_flag)
+
+
+def test_paged_decode_attention_over_pruned_pages(gpu_lib):
+    """Decode attention reading a pruned paged cache in place (fresh pages with
+    random page tables, per-KV-head kept counts) against the oracle."""
+    import math
+    T = gpu_lib
+    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=4)
+    log("case paged decode attention")
+    pc = W.paged_cache(cfg, "cpu")
+    g = _to(pc, "cuda")
+    calib, cal = calib_for(T, cfg)
+    B = cfg.budget
+    src = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["page_table"], page_size=cfg.page_size,
+                       max_pages=g["max_pages"])
+    nk = torch.zeros((cfg.n_seg,), dtype=torch.int32, device="cuda")
+    dst = T.cache_desc(g["out_k"], g["out_v"], g["out_pos"], nk, n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["out_page_table"], page_size=cfg.page_size,
+                       max_pages=g["out_max_pages"])
+    T.tri_prune_window(calib, src, g["t"], B, dst, nk, T.workspace(calib, src, B))
+    gq = torch.Generator().manual_seed(77)
+    q = torch.randn((1, cfg.n_seq, cfg.n_q_heads, cfg.head_dim), generator=gq).to(cfg.dtype)
+    out = torch.full(q.shape, float("nan"), device="cuda")
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    T.tri_decode_attn(dst, cfg.n_q_heads, q.cuda(), scale, out)
+    torch.cuda.synchronize()
+    OK, OV = stored(g["out_k"].cpu()), stored(g["out_v"].cpu())
+    opt = pc["out_page_table"].numpy()
+    kept = nk.cpu().numpy()
+    for s in range(cfg.n_seg):
+        b, h = seg_seq(cfg, s), s % cfg.n_kv_heads
+        hs = slice(h * cfg.group, (h + 1) * cfg.group)
+        K = oracle.paged_rows(OK, opt[s], cfg.page_size, int(kept[s]))
+        V = oracle.paged_rows(OV, opt[s], cfg.page_size, int(kept[s]))
+        ref = oracle.decode_attn(stored(q[0, b, hs]), K, V, scale)
+        got = out[0, b, hs].cpu().numpy()
+        err = np.abs(got - ref) / np.maximum(np.abs(ref), np.abs(ref).max(axis=1, keepdims=True))
+        assert err.max() <= 1e-4, f"paged attention seg {s} (kept {kept[s]}): {err.max():.2e}"
