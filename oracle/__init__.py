@@ -62,11 +62,13 @@ def _load():
     lib.orc_select_topb_f32.argtypes = [P, i64, i64, P, P]
     lib.orc_gather_rows.argtypes = [P, i64, P, i64, P]
     lib.orc_paged_rows.argtypes = [P, i64, P, i32, i64, P]
+    lib.orc_inplace_layout.argtypes = [P, i64, i64, P]
     lib.orc_decode_attn.argtypes = [P, i32, P, P, i32, i64, i32, i32, dbl, P]
     lib.orc_calibrate.argtypes = [P, i32, i64, i32, P, P, P]
     for fn in (lib.orc_score_segment, lib.orc_zscore_max, lib.orc_select_topb,
                lib.orc_select_topb_f32, lib.orc_gather_rows, lib.orc_paged_rows,
-               lib.orc_decode_attn, lib.orc_calibrate, lib.orc_score_segment_variant):
+               lib.orc_decode_attn, lib.orc_calibrate, lib.orc_score_segment_variant,
+               lib.orc_inplace_layout):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -152,6 +154,16 @@ def gather_rows(src, idx):
     dst = np.empty((len(idx),) + src.shape[1:], dtype=src.dtype)
     _check(lib.orc_gather_rows(_ptr(src), row_bytes, _ptr(idx), len(idx), _ptr(dst)), "gather_rows")
     return dst
+
+
+def inplace_layout(kept, N):
+    """Slot arrangement of a segment pruned in place: entry j is the pre-prune
+    slot of the key now in slot j (kept slots below len(kept) stay put; the
+    kept slots above fill the freed ones in ascending order)."""
+    kept = np.ascontiguousarray(kept, dtype=np.int32)
+    out = np.empty(len(kept), dtype=np.int32)
+    _check(_load().orc_inplace_layout(_ptr(kept), len(kept), int(N), _ptr(out)), "inplace_layout")
+    return out
 
 
 def paged_rows(pool, page_table, page_size, n):

@@ -251,6 +251,35 @@ int orc_gather_rows(const void* src, int64_t row_bytes, const int32_t* idx, int6
     return 0;
 }
 
+/*
+ * Layout of a segment pruned in place.  The pages fix which keys survive a
+ * prune ([YY] 主要方法: keep the top-B keys) but not where they sit afterwards;
+ * attention and later prunes read each key with its stored position, so any
+ * arrangement of the kept rows in slots [0, n_kept) is a valid cache.  Reading
+ * taken for the in-place prune: a kept key already below n_kept stays in its
+ * slot, and the kept keys at or above n_kept fill the freed slots below
+ * n_kept, the lowest such key going to the lowest freed slot, and so on.
+ * kept: the kept slots in ascending order, n of them, all < N.
+ * src_of: [n] output; slot j of the pruned segment holds the key that was in
+ * slot src_of[j] before the prune.
+ */
+int orc_inplace_layout(const int32_t* kept, int64_t n, int64_t N, int32_t* src_of) {
+    if (n < 0 || n > N) return -1;
+    for (int64_t i = 0; i < n; ++i)
+        if (kept[i] < 0 || kept[i] >= N || (i > 0 && kept[i] <= kept[i - 1])) return -1;
+    char* is_kept = (char*)calloc((size_t)(N > 0 ? N : 1), 1);
+    if (!is_kept) return -1;
+    for (int64_t i = 0; i < n; ++i) is_kept[kept[i]] = 1;
+    int64_t next_mover = 0;                       /* first kept entry at or above n */
+    while (next_mover < n && kept[next_mover] < n) ++next_mover;
+    for (int64_t j = 0; j < n; ++j) {
+        if (is_kept[j]) src_of[j] = (int32_t)j;   /* stays where it is */
+        else src_of[j] = kept[next_mover++];      /* freed slot: next key from above */
+    }
+    free(is_kept);
+    return next_mover == n ? 0 : -1;
+}
+
 /* A paged segment read out in slot order: slot i lives in row (i % page_size)
  * of page page_table[i / page_size] of the pool. */
 int orc_paged_rows(const void* pool, int64_t row_bytes, const int32_t* page_table,

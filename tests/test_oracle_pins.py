@@ -11,6 +11,9 @@ never against the oracle itself.
   maps; G = 1.
 * Top-B against a brute-force rank count on tiny inputs with ties.
 * Gather, paged read-out and decode attention against numpy / torch.
+* In-place layout: hand-worked cases (tests/golden/inplace_layout.json), a
+  brute-force search over every arrangement of tiny kept sets for the one
+  that obeys the layout's two rules, and invariants on large kept sets.
 """
 import json
 import math
@@ -379,3 +382,57 @@ def test_variant_flags_are_checked():
         oracle.score_segment(K, pos, 5100, 1e4, M, phi, R, [1], variant=oracle.VAR_TRIG_ONLY | oracle.VAR_NORM_ONLY)
     with pytest.raises(ValueError):
         oracle.score_segment(K, pos, 5100, 1e4, M, phi, R, [1], variant=16)
+
+
+# ---------------------------------------------------------------- in-place layout
+def test_inplace_layout_hand_cases():
+    cases = json.load(open(os.path.join(GOLDEN, "inplace_layout.json")))["cases"]
+    for c in cases:
+        got = oracle.inplace_layout(c["kept"], c["N"])
+        assert got.tolist() == c["src_of"], c["why"]
+
+
+def _brute_inplace(kept, N):
+    """Every arrangement of the kept keys over slots [0, n), filtered by the two
+    rules: a kept key below n keeps its slot, and the keys that move land in
+    freed slots in the same order as their old slots.  Exactly one survives."""
+    import itertools
+    n = len(kept)
+    found = []
+    for perm in itertools.permutations(kept):
+        if any(k < n and perm[k] != k for k in kept):
+            continue
+        moved = [(j, perm[j]) for j in range(n) if perm[j] != j]
+        if all(a[1] < b[1] for a, b in zip(moved, moved[1:])):
+            found.append(list(perm))
+    assert len(found) == 1, f"{kept}, N={N}: {len(found)} arrangements satisfy the rules"
+    return found[0]
+
+
+def test_inplace_layout_brute_force_tiny():
+    import itertools
+    for N in range(1, 8):
+        for n in range(0, N + 1):
+            for kept in itertools.combinations(range(N), n):
+                got = oracle.inplace_layout(list(kept), N).tolist()
+                assert got == _brute_inplace(list(kept), N), (kept, N)
+
+
+def test_inplace_layout_invariants():
+    rng = np.random.default_rng(11)
+    for N, n in [(1152, 1024), (32768, 2048), (5000, 4096), (300, 1)]:
+        kept = np.sort(rng.choice(N, size=n, replace=False)).astype(np.int32)
+        src_of = oracle.inplace_layout(kept, N)
+        assert np.array_equal(np.sort(src_of), kept)             # the same keys, each once
+        stay = kept[kept < n]
+        assert np.array_equal(src_of[stay], stay)                 # kept keys below n do not move
+        moved = np.nonzero(src_of != np.arange(n))[0]
+        assert len(moved) == np.count_nonzero(kept >= n)          # only keys from above move
+        assert np.all(src_of[moved] >= n) and np.all(np.diff(src_of[moved]) > 0)
+
+
+def test_inplace_layout_rejects_bad_lists():
+    with pytest.raises(ValueError):
+        oracle.inplace_layout([3, 1], 5)                          # not ascending
+    with pytest.raises(ValueError):
+        oracle.inplace_layout([0, 5], 5)                          # slot out of range
