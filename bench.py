@@ -112,7 +112,9 @@ def bench_decode_loop(args, T, W):
     """GPT-OSS-shaped decode loop: a step is one 128-token window, i.e. 128 x
     (append one token to every segment, single-query attention of every query
     head over its cache) followed by the window's prune back to B.  Tokens are
-    generated before timing and reused window after window."""
+    generated before timing and reused window after window.  The prune runs in
+    place (only the kept rows above B move) unless --out-of-place is given, in
+    which case it compacts into a second cache and the two alternate."""
     import math
 
     import torch
@@ -138,8 +140,10 @@ def bench_decode_loop(args, T, W):
     tvec = torch.empty((cfg.n_seq,), dtype=torch.int32, device="cuda")
     state = {"cur": 0, "w": 0}
     stream = torch.cuda.current_stream()
+    in_place = not args.out_of_place
+    moved = {}
 
-    def window():
+    def window(count_moves=False):
         cur = state["cur"]
         d = descs[cur]
         for j in range(win):
@@ -147,13 +151,19 @@ def bench_decode_loop(args, T, W):
             T.tri_append(d, k_new, v_new, pos[state["w"] * win + j], stream=stream)
             T.tri_decode_attn(d, cfg.n_q_heads, q, scale, out, stream=stream)
         tvec.fill_(t0 + (state["w"] + 1) * win)
-        nxt = caches[1 - cur]
-        T.tri_prune_window(calib, d, tvec, B, descs[1 - cur], nxt["lengths"], ws, stream=stream)
-        state["cur"] = 1 - cur
+        if in_place:
+            before = caches[cur]["pos"][:, :B].clone() if count_moves else None
+            T.tri_prune_window(calib, d, tvec, B, d, caches[cur]["lengths"], ws, stream=stream)
+            if count_moves:             # rows the prune wrote: slots below B whose key changed
+                moved["rows"] = int((caches[cur]["pos"][:, :B] != before).sum())
+        else:
+            nxt = caches[1 - cur]
+            T.tri_prune_window(calib, d, tvec, B, descs[1 - cur], nxt["lengths"], ws, stream=stream)
+            state["cur"] = 1 - cur
         state["w"] += 1
 
-    for _ in range(args.warmup):
-        window()
+    for i in range(args.warmup):
+        window(count_moves=in_place and i == args.warmup - 1)
     torch.cuda.synchronize()
     T.tri_timing_reset()
     T.tri_timing_enable(True)
@@ -173,7 +183,10 @@ def bench_decode_loop(args, T, W):
     attn_launches, attn_ms = kt["decode_attn"]
     attn_avg = attn_ms / attn_launches
     attn_gbs = attn_bytes / win / (attn_avg * 1e-3) / 1e9
-    prune_bytes = cfg.n_seg * ((B + win) * cfg.head_dim * es + B * (4 * cfg.head_dim * es + 8))
+    # score reads every key; compaction reads and writes K, V and position of each copied row
+    # (all B kept rows out of place; in place, the rows moved, counted on the last warmup window)
+    copied = moved.get("rows", cfg.n_seg * B) if in_place else cfg.n_seg * B
+    prune_bytes = cfg.n_seg * (B + win) * cfg.head_dim * es + copied * (4 * cfg.head_dim * es + 8)
     kernels = {k: {"avg_ms": round(v[1] / v[0], 4), "launches": v[0]} for k, v in kt.items() if v[0]}
     prune_ms = sum(v["avg_ms"] for k, v in kernels.items() if k not in ("append", "decode_attn"))
     tokens = win * cfg.n_seq
@@ -185,12 +198,14 @@ def bench_decode_loop(args, T, W):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": (f"gptoss: {cfg.n_layers} layers x {cfg.n_seq} sequences x {cfg.n_kv_heads} KV heads, "
                                 f"GQA {cfg.group}, head_dim {cfg.head_dim}, bf16, B={B}; a step is one {win}-token "
-                                f"window (append + decode attention per token, then the prune)"),
+                                f"window (append + decode attention per token, then the prune "
+                                f"{'in place' if in_place else 'into a second cache'})"),
                    "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "kernel": "decode_attn", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
         "prune": {"algorithmic_bytes": prune_bytes, "ms": round(prune_ms, 4),
-                  "achieved_GBs": round(prune_bytes / (prune_ms * 1e-3) / 1e9, 1)},
+                  "achieved_GBs": round(prune_bytes / (prune_ms * 1e-3) / 1e9, 1),
+                  "in_place": in_place, "rows_copied": copied},
         "kernels": kernels,
     }
     calib.free()
@@ -326,6 +341,8 @@ def main():
     ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l", "gptoss", "calib", "ragged"],
                     help="qwen36l (default): the pruning pass; gptoss: decode-loop windows; "
                          "calib: offline calibration from query samples; ragged: paged batch prune + attention")
+    ap.add_argument("--out-of-place", action="store_true",
+                    help="gptoss: prune into a second cache instead of in place")
     ap.add_argument("--cpu-sample", type=int, default=16, help="oracle segments for the CPU baseline (0: skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy of this many MiB "

@@ -200,6 +200,16 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
  * aggregate, select and compact in one call, the fused hot path.  Segments
  * with lengths[s] <= budget are copied through unchanged, so dst is always a
  * complete cache; n_kept (device int32 [n_seg]) gets min(lengths[s], budget).
+ *
+ * In place: when dst names src's storage (same k, v, pos, layout, capacity,
+ * layer0 and, if paged, the same page table), the cache is pruned where it
+ * is.  The kept set is the same; the arrangement is not slot order: a kept
+ * key already below n_kept[s] stays in its slot, and the kept keys at or
+ * above it move into the freed slots below, lowest key into lowest freed
+ * slot.  Only those keys are copied (at most lengths[s] - budget rows per
+ * segment); segments with lengths[s] <= budget are not touched.  n_kept may
+ * then be src->lengths itself.  Any other sharing of memory between src and
+ * dst is TRI_ERR_INVALID_ARG.
  */
 int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
                      const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,

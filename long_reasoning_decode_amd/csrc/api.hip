@@ -433,7 +433,18 @@ int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int cap
     return hip_status(launch_select(a, 0, SELECT_A, capacity, static_cast<hipStream_t>(stream)), "select kernel");
 }
 
-static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int budget) {
+// dst names exactly the storage of src (same rows for every slot).
+static bool same_storage(const tri_cache_desc* s, const tri_cache_desc* d) {
+    if (s->k != d->k || s->v != d->v || s->pos != d->pos) return false;
+    if (s->layout != d->layout || s->capacity != d->capacity || s->layer0 != d->layer0) return false;
+    if (s->layout == TRI_LAYOUT_PAGED)
+        return s->page_table == d->page_table && s->page_size == d->page_size && s->max_pages == d->max_pages;
+    return true;
+}
+
+// src -> dst compaction arguments.  With `in_place` non-null, a dst that names
+// src's storage is accepted (and reported); any other sharing is an error.
+static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int budget, bool* in_place = nullptr) {
     int rc = check_cache(src);
     if (rc) return rc;
     if ((rc = check_cache(dst))) return rc;
@@ -442,7 +453,9 @@ static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int 
         return TRI_ERR_INVALID_ARG;
     if (budget < 1) return TRI_ERR_INVALID_ARG;
     if (dst->capacity < budget) return TRI_ERR_INVALID_ARG;
-    if (dst->k == src->k || dst->v == src->v || dst->pos == src->pos || dst->k == src->v || dst->v == src->k)
+    if (in_place) *in_place = same_storage(src, dst);
+    if (!(in_place && *in_place) &&
+        (dst->k == src->k || dst->v == src->v || dst->pos == src->pos || dst->k == src->v || dst->v == src->k))
         return TRI_ERR_INVALID_ARG;
     if (budget > kMaxBudget) return TRI_ERR_UNSUPPORTED;
     return TRI_OK;
@@ -470,7 +483,8 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
 int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
                      const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,
                      tri_stream_t stream) {
-    int rc = check_pair(src, dst, budget);
+    bool in_place = false;
+    int rc = check_pair(src, dst, budget, &in_place);
     if (rc) return rc;
     if ((rc = check_calib_vs_cache(calib, src))) return rc;
     if (!t || !n_kept) return TRI_ERR_INVALID_ARG;
@@ -503,7 +517,7 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     a.lengths = src->lengths;
     a.budget = budget;
     a.n_kept = n_kept;
-    a.gather = 1;
+    a.gather = in_place ? GATHER_IN_PLACE : GATHER_COPY;
     a.src = view_of(src);
     a.dst = out_of(dst);
     a.row_bytes = src->head_dim * elem_size(src->dtype);

@@ -136,12 +136,17 @@ struct SelectArgs {
     int32_t* idx_out;       // optional [n_seg][idx_stride]
     int64_t idx_stride;
     int32_t* n_kept;        // optional [n_seg]
-    int32_t gather;         // 1: copy kept rows src -> dst
+    int32_t gather;         // GatherMode
     CacheView src;
     CacheOut dst;
     int32_t row_bytes;
     int32_t n_seg;
 };
+// GATHER_COPY: kept row j of each segment -> dst slot j (dst is another cache).
+// GATHER_IN_PLACE: dst is src; kept rows below n_kept stay, the kept rows at or
+// above n_kept move into the freed slots below it, in ascending order (reads
+// only from slots >= n_kept, writes only to slots < n_kept: no overlap).
+enum GatherMode : int { GATHER_NONE = 0, GATHER_COPY = 1, GATHER_IN_PLACE = 2 };
 // mode A: select on aggregated scores (group 0); S: on interleaved scores;
 // C: on candidate lists, with the certificate and fallback list; S_FALLBACK:
 // mode S over the segments listed in fb_list.

@@ -11,6 +11,8 @@
 //
 // In gather mode the same workgroup then copies the kept K/V rows and positions
 // (bit-exact, slot order) into the destination cache: the fused pruning pass.
+// In place, only the kept rows at or above the kept count move, into the slots
+// freed below it.
 #include "launch.h"
 #include "stats.h"
 
@@ -342,13 +344,55 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
             else a.idx_out[(int64_t)s * a.idx_stride + out] = slot;
         }
     }
+    __syncthreads();                                    // every wave has read lengths[s] (n_kept may alias it)
     if (a.n_kept && tid == 0) a.n_kept[s] = nk;
     if (!a.gather) return;
-    __syncthreads();
 
-    // ---- compaction of the kept rows (16-byte copies), then positions
     const int cpr = a.row_bytes >> 4;
     const int lg = 31 - __clz(cpr);
+    if (a.gather == GATHER_IN_PLACE) {
+        // kept[0..c) are below nk and stay; kept[c..nk) fill the freed slots
+        // below nk in ascending order.  The r-th freed slot is r + p, where p
+        // counts the kept slots below it, i.e. the entries i < c with
+        // kept[i] - i <= r (kept[i] - i, the freed slots below kept[i], does
+        // not decrease with i).  Freed slots are found in batches of 2048
+        // (the histogram's LDS, no longer needed).
+        int lo = 0, hi = nk;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (kept[mid] < nk) lo = mid + 1;
+            else hi = mid;
+        }
+        const int c = lo, m = nk - c;
+        for (int base = 0; base < m; base += 2048) {
+            const int nb = min(2048, m - base);
+            for (int r = tid; r < nb; r += kSelThreads) {
+                int l2 = 0, h2 = c;
+                while (l2 < h2) {
+                    const int mid = (l2 + h2) >> 1;
+                    if (kept[mid] - mid <= base + r) l2 = mid + 1;
+                    else h2 = mid;
+                }
+                hist[r] = (uint32_t)(base + r + l2);
+            }
+            __syncthreads();
+            for (int u = tid; u < nb * cpr; u += kSelThreads) {
+                const int jr = u >> lg, q = u & (cpr - 1);
+                const int64_t sr = a.src.row(s, kept[c + base + jr]);
+                const int64_t dr = a.dst.row(s, (int)hist[jr]);
+                const uint4 kv = reinterpret_cast<const uint4*>(a.src.k + sr * a.row_bytes)[q];
+                const uint4 vv = reinterpret_cast<const uint4*>(a.src.v + sr * a.row_bytes)[q];
+                reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[q] = kv;
+                reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[q] = vv;
+            }
+            for (int jr = tid; jr < nb; jr += kSelThreads)
+                a.dst.pos[a.dst.row(s, (int)hist[jr])] = a.src.pos[a.src.row(s, kept[c + base + jr])];
+            __syncthreads();                            // hist is refilled by the next batch
+        }
+        return;
+    }
+
+    // ---- compaction of the kept rows (16-byte copies), then positions
     const int total = nk * cpr;
     for (int u = tid; u < total; u += kSelThreads) {
         const int jrow = u >> lg, q = u & (cpr - 1);

@@ -131,3 +131,26 @@ def check_compaction(Ks, Vs, Ps, Kd, Vd, Pd, idx, what=""):
 
 def stored(x):
     return W.to_stored_numpy(x)
+
+
+def check_in_place(cfg, cal, Kb, Vb, Pb, Ka, Va, Pa, N, nk, t, s, B, tag, oop_kept=None):
+    """One segment pruned in place.  b: its rows before the prune (all slots);
+    a: after.  The kept set against the oracle's top-B (and, when given, the
+    out-of-place pass's set), the arrangement against the oracle's in-place
+    layout of that set, rows bit-exact, rows at or above the kept count
+    untouched."""
+    nks = min(N, B)
+    assert nk == nks, f"{tag}: kept count {nk} != {nks}"
+    if N == 0:
+        return
+    K, V, P = Kb[:N], Vb[:N], Pb[:N]
+    ix = kept_slots_from_positions(P, Pa[:nks])
+    kept = np.sort(ix)
+    ref = oracle_segment(cfg, cal, K, V, P, t, s, B)
+    check_selection(kept, ref["A"], B, tag)
+    if oop_kept is not None:
+        assert np.array_equal(kept, oop_kept), f"{tag}: kept set differs from the out-of-place pass"
+    assert np.array_equal(ix, oracle.inplace_layout(kept, N)), f"{tag}: arrangement is not the in-place layout"
+    check_compaction(K, V, P, Ka[:nks], Va[:nks], Pa[:nks], ix, tag)
+    assert np.array_equal(Ka[nks:], Kb[nks:]) and np.array_equal(Va[nks:], Vb[nks:]) and \
+        np.array_equal(Pa[nks:], Pb[nks:]), f"{tag}: rows at or above the kept count were written"

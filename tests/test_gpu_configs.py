@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import (calib_for, check_agg, check_compaction, check_scores, check_selection, dense_desc,
+from helpers import (check_in_place, calib_for, check_agg, check_compaction, check_scores, check_selection, dense_desc,
                      empty_like_dense, kept_slots_from_positions, log, oracle_segment, seg_seq, stored)
 
 pytestmark = pytest.mark.gpu
@@ -185,11 +185,13 @@ def test_ragged_paged_full(gpu_lib):
     log("  paged decode attention over the pruned pages ok")
 
 
-def test_gptoss_decode_loop_full(gpu_lib):
+@pytest.mark.parametrize("in_place", [False, True])
+def test_gptoss_decode_loop_full(gpu_lib, in_place):
     T = gpu_lib
     cfg = W.CONFIGS["gptoss"]
     B = cfg.budget
-    log(f"case gptoss decode loop: {cfg.windows} windows x {cfg.window} steps, {cfg.n_seg} segments")
+    log(f"case gptoss decode loop: {cfg.windows} windows x {cfg.window} steps, {cfg.n_seg} segments, "
+        f"in place {in_place}")
     st = W.decode_start(cfg, "cuda")
     km = st.pop("key_model")
     calib, cal = calib_for(T, cfg)
@@ -221,8 +223,24 @@ def test_gptoss_decode_loop_full(gpu_lib):
                     assert err.max() <= 1e-4, f"attention window {w} step {j} seg {s}: {err.max():.2e}"
             t += 1
         c["t"] = torch.full((cfg.n_seq,), t, dtype=torch.int32, device="cuda")
-        nxt = caches[1 - cur]
         ws = T.workspace(calib, desc, B)
+        if in_place:
+            checked = w in (0, cfg.windows - 1)
+            if checked:
+                before = {k: c[k][sample].cpu() for k in ("k", "v", "pos", "lengths")}
+            T.tri_prune_window(calib, desc, c["t"], B, desc, c["lengths"], ws)
+            torch.cuda.synchronize()
+            assert bool(torch.all(c["lengths"] == B)), f"window {w}: kept counts"
+            if checked:
+                Ka, Va, Pa = (stored(c["k"][sample].cpu()), stored(c["v"][sample].cpu()),
+                              c["pos"][sample].cpu().numpy())
+                Kb, Vb, Pb = stored(before["k"]), stored(before["v"]), before["pos"].numpy()
+                for i, s in enumerate(sample):
+                    check_in_place(cfg, cal, Kb[i], Vb[i], Pb[i], Ka[i], Va[i], Pa[i], int(before["lengths"][i]),
+                                   B, t, s, B, f"gptoss window {w} seg {s} in place")
+                log(f"  window {w} checked")
+            continue
+        nxt = caches[1 - cur]
         T.tri_prune_window(calib, desc, c["t"], B, dense_desc(T, cfg, nxt), nxt["lengths"], ws)
         torch.cuda.synchronize()
         assert bool(torch.all(nxt["lengths"] == B)), f"window {w}: kept counts"

@@ -1,0 +1,140 @@
+"""In-place pruning: tri_prune_window with dst naming src's storage.  Per
+segment, against the oracle:
+* the kept set (oracle top-B under the tie band), and byte for byte the set the
+  out-of-place pass keeps on the same input;
+* the arrangement: the oracle's in-place layout of that kept set, exactly;
+* K/V rows and positions bit-exact, rows at or above the kept count untouched;
+* lengths updated through n_kept aliasing them.
+Dense bf16 and fp32, the candidate pass (including more than 2048 moved rows,
+two batches of freed slots), ragged lengths around the budget, paged pools,
+and the argument checks."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import (calib_for, check_in_place, dense_desc, empty_like_dense, kept_slots_from_positions, log,
+                     seg_seq, stored)
+
+pytestmark = pytest.mark.gpu
+
+
+def _dense_in_place(T, cfg, cpu, B, what):
+    """Out-of-place pass on one copy, in-place pass on another; check both."""
+    calib, cal = calib_for(T, cfg)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in cpu.items()}
+    desc = dense_desc(T, cfg, g)
+    ws = T.workspace(calib, desc, B)
+    out = empty_like_dense(g, B)
+    nk_oop = torch.full_like(g["lengths"], -1)
+    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), nk_oop, ws)
+    torch.cuda.synchronize()
+    fb_oop = T.tri_prune_fallbacks(ws)
+    # in place, n_kept = the cache's own lengths
+    T.tri_prune_window(calib, desc, g["t"], B, desc, g["lengths"], ws)
+    torch.cuda.synchronize()
+    fb = T.tri_prune_fallbacks(ws)
+    log(f"  fallbacks: out of place {fb_oop}, in place {fb}")
+    lengths = cpu["lengths"].numpy()
+    Kb, Vb, Pb = stored(cpu["k"]), stored(cpu["v"]), cpu["pos"].numpy()
+    Ka, Va, Pa = stored(g["k"].cpu()), stored(g["v"].cpu()), g["pos"].cpu().numpy()
+    nk = g["lengths"].cpu().numpy()
+    assert np.array_equal(nk, nk_oop.cpu().numpy())
+    P_oop = out["pos"].cpu().numpy()
+    for s in range(len(lengths)):
+        N = int(lengths[s])
+        nks = min(N, B)
+        oop = kept_slots_from_positions(Pb[s, :N], P_oop[s, :nks]) if N else None
+        check_in_place(cfg, cal, Kb[s], Vb[s], Pb[s], Ka[s], Va[s], Pa[s], N, int(nk[s]),
+                       int(cpu["t"][seg_seq(cfg, s)]), s, B, f"{what} seg {s} N={N}", oop)
+
+
+@pytest.mark.parametrize("d,G,dtype", [(128, 4, torch.bfloat16), (64, 8, torch.bfloat16), (64, 2, torch.float32)])
+def test_in_place_ragged_lengths(gpu_lib, d, G, dtype):
+    """Segments of length 0, 1, B-1, B, B+1, chunk-straddling and full (full-score path)."""
+    B, cap = 200, 2600
+    cfg = W.CONFIGS["tiny"].replace(head_dim=d, group=G, dtype=dtype, theta=1e6, n_kv_heads=3, n_seq=3,
+                                    n_keys=cap, t=cap + 5, budget=B, sigma=None, seed=21)
+    log(f"case in place ragged d={d} G={G} {dtype}")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([0, 1, B - 1, B, B + 1, 513, 1024, 2047, cap], dtype=torch.int32)
+    _dense_in_place(gpu_lib, cfg, cpu, B, f"in place d{d} G{G}")
+
+
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 8)])
+def test_in_place_candidate_pass(gpu_lib, d, G):
+    """Lengths around the candidate-mode boundaries (4096 and 8B)."""
+    B, cap = 600, 12000
+    cfg = W.CONFIGS["tiny"].replace(head_dim=d, group=G, dtype=torch.bfloat16, theta=1e6, n_kv_heads=3, n_seq=3,
+                                    n_keys=cap, t=cap + 3, budget=B, sigma=None, seed=23)
+    log(f"case in place candidate d={d} G={G}")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([cap, 4095, 4096, 8 * B - 1, 8 * B, 8 * B + 1, 9001, B + 1, cap - 17],
+                                  dtype=torch.int32)
+    _dense_in_place(gpu_lib, cfg, cpu, B, f"in place candidate d{d} G{G}")
+
+
+def test_in_place_many_moved_rows(gpu_lib):
+    """More than 2048 kept rows above the kept count: the freed slots are found
+    in two batches.  One candidate-mode segment (N = 65536, B = 4096) and one on
+    the full-score path (N = 12000, B = 4096 < N < 8B)."""
+    B, cap = 4096, 65536
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, group=4, dtype=torch.bfloat16, theta=1e6, n_kv_heads=1, n_seq=2,
+                                    n_keys=cap, t=cap + 1, budget=B, sigma=None, seed=25)
+    log("case in place, many moved rows")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([cap, 12000], dtype=torch.int32)
+    _dense_in_place(gpu_lib, cfg, cpu, B, "in place many moves")
+
+
+def test_in_place_paged(gpu_lib):
+    """A ragged paged pool (random page tables) pruned where it is."""
+    T = gpu_lib
+    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=27)
+    log("case in place paged")
+    pc = W.paged_cache(cfg, "cpu")
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in pc.items()}
+    calib, cal = calib_for(T, cfg)
+    B = cfg.budget
+    src = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["page_table"], page_size=cfg.page_size,
+                       max_pages=g["max_pages"])
+    T.tri_prune_window(calib, src, g["t"], B, src, g["lengths"], T.workspace(calib, src, B))
+    torch.cuda.synchronize()
+    pt = pc["page_table"].numpy()
+    ps = cfg.page_size
+    Kp0, Vp0, Pp0 = stored(pc["k"]), stored(pc["v"]), pc["pos"].numpy()
+    Kp1, Vp1, Pp1 = stored(g["k"].cpu()), stored(g["v"].cpu()), g["pos"].cpu().numpy()
+    nk = g["lengths"].cpu().numpy()
+    for s in range(cfg.n_seg):
+        N = int(pc["lengths"][s])
+        n_rows = (N + ps - 1) // ps * ps                     # the segment's own pages only
+        rows = lambda pool: oracle.paged_rows(pool, pt[s], ps, n_rows)
+        check_in_place(cfg, cal, rows(Kp0), rows(Vp0), rows(Pp0), rows(Kp1), rows(Vp1), rows(Pp1), N,
+                       int(nk[s]), int(pc["t"][seg_seq(cfg, s)]), s, B, f"in place paged seg {s} N={N}")
+
+
+def test_in_place_argument_checks(gpu_lib):
+    """Sharing that is not the same storage is refused before any launch."""
+    T = gpu_lib
+    cfg = W.CONFIGS["tiny"].replace(head_dim=64, group=2, dtype=torch.bfloat16, n_kv_heads=1, n_seq=1,
+                                    n_keys=600, t=600, budget=100)
+    g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in W.dense_cache(cfg, "cpu").items()}
+    calib, _ = calib_for(T, cfg)
+    desc = dense_desc(T, cfg, g)
+    ws = T.workspace(calib, desc, 100)
+    other_v = torch.empty_like(g["v"])
+    half = T.cache_desc(g["k"], other_v, g["pos"], g["lengths"], n_layers=1, n_seq=1, n_kv_heads=1)
+    with pytest.raises(T.TriError) as e:
+        T.tri_prune_window(calib, desc, g["t"], 100, half, g["lengths"], ws)
+    assert e.value.code == T.TRI_ERR_INVALID_ARG
+    shifted = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=1, n_seq=1, n_kv_heads=1, layer0=0)
+    shifted.capacity = desc.capacity - 1
+    with pytest.raises(T.TriError) as e:
+        T.tri_prune_window(calib, desc, g["t"], 100, shifted, g["lengths"], ws)
+    assert e.value.code == T.TRI_ERR_INVALID_ARG
+    with pytest.raises(T.TriError) as e:                      # compaction alone stays out of place
+        idx = torch.zeros((1, 100), dtype=torch.int32, device="cuda")
+        T.tri_compact(desc, idx, g["lengths"], 100, desc)
+    assert e.value.code == T.TRI_ERR_INVALID_ARG

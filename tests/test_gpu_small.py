@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import (calib_for, check_agg, check_compaction, check_mu_sigma, check_scores,
+from helpers import (calib_for, check_agg, check_compaction, check_in_place, check_mu_sigma, check_scores,
                      check_selection, dense_desc, empty_like_dense, kept_slots_from_positions, log,
                      oracle_segment, seg_calib, seg_seq, stored)
 
@@ -198,12 +198,13 @@ def test_paged_small_every_step(gpu_lib):
         check_compaction(K, V, P, Kd, Vd, Pd, ix, tag)
 
 
-def test_decode_loop_small(gpu_lib):
-    """Append + decode attention each step, prune after each window, on a
-    GPT-OSS-shaped but small cache."""
+@pytest.mark.parametrize("in_place", [False, True])
+def test_decode_loop_small(gpu_lib, in_place):
+    """Append + decode attention each step, prune after each window (into the
+    other buffer, or in place), on a GPT-OSS-shaped but small cache."""
     T = gpu_lib
-    cfg = W.CONFIGS["gptoss"].replace(n_layers=2, n_seq=3, budget=64, window=8, windows=2, start_pos_range=512)
-    log("case decode small")
+    cfg = W.CONFIGS["gptoss"].replace(n_layers=2, n_seq=3, budget=64, window=8, windows=3, start_pos_range=512)
+    log(f"case decode small, in place {in_place}")
     st = _to(W.decode_start(cfg, "cpu"), "cuda")
     km = W.key_model(cfg)
     calib, cal = calib_for(T, cfg)
@@ -235,10 +236,20 @@ def test_decode_loop_small(gpu_lib):
             t += 1
         c = caches[cur]
         c["t"] = torch.full((cfg.n_seq,), t, dtype=torch.int32, device="cuda")
-        nxt = caches[1 - cur]
-        nk = nxt["lengths"]
         desc = dense_desc(T, cfg, c)
         ws = T.workspace(calib, desc, cfg.budget)
+        if in_place:
+            before = {k: c[k].cpu() for k in ("k", "v", "pos", "lengths")}
+            T.tri_prune_window(calib, desc, c["t"], cfg.budget, desc, c["lengths"], ws)
+            torch.cuda.synchronize()
+            Ka, Va, Pa = stored(c["k"].cpu()), stored(c["v"].cpu()), c["pos"].cpu().numpy()
+            Kb, Vb, Pb = stored(before["k"]), stored(before["v"]), before["pos"].numpy()
+            for s in range(cfg.n_seg):
+                check_in_place(cfg, cal, Kb[s], Vb[s], Pb[s], Ka[s], Va[s], Pa[s], int(before["lengths"][s]),
+                               int(c["lengths"][s]), t, s, cfg.budget, f"decode window {w} seg {s} in place")
+            continue
+        nxt = caches[1 - cur]
+        nk = nxt["lengths"]
         T.tri_prune_window(calib, desc, c["t"], cfg.budget, dense_desc(T, cfg, nxt), nk, ws)
         torch.cuda.synchronize()
         for s in range(cfg.n_seg):
