@@ -142,7 +142,8 @@ int tri_calib_free(tri_calib_t calib);
  *           (pre-RoPE rows: one per sampled token and query head).
  *   mag, phase, conc : device fp32 [n_layers][n_q_heads][head_dim/2] outputs,
  *           the layout tri_calib_load takes (copy them to the host for it).
- *   ws    : device workspace of tri_calibrate_workspace_size bytes.
+ *   ws    : device workspace of tri_calibrate_workspace_size bytes, 256-byte
+ *           aligned (TRI_ERR_WORKSPACE otherwise).
  * Per-sample arithmetic is fp32 and the sums are fp64, added in a fixed order
  * (results do not depend on scheduling).  head_dim 64 or 128.
  */
@@ -166,7 +167,8 @@ int tri_workspace_size(tri_calib_t calib, const tri_cache_desc* kv, int budget, 
  *              (population statistics over the segment's valid keys; a head
  *              with sigma = 0 contributes 0).  Slots >= lengths[s] untouched.
  *   mu_sigma : optional device fp32 [n_seg][G][2]: (mu_h, sigma_h).
- *   ws       : device workspace of tri_workspace_size bytes.
+ *   ws       : device workspace of tri_workspace_size bytes, 256-byte aligned
+ *              (as every device allocation is; TRI_ERR_WORKSPACE otherwise).
  */
 int tri_score(tri_calib_t calib, const tri_cache_desc* kv, const int32_t* t, float* scores,
               float* agg, float* mu_sigma, void* ws, size_t ws_bytes, tri_stream_t stream);

@@ -68,6 +68,9 @@ int device_present() {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// Workspaces start on a 256-byte boundary (every device allocation does):
+// their regions sit at 256-byte offsets and are read with vector loads.
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255) == 0; }
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
@@ -101,6 +104,15 @@ int check_calib_vs_cache(const tri_calib_s* c, const tri_cache_desc* kv) {
     return TRI_OK;
 }
 
+int page_shift_of(const tri_cache_desc* kv) {
+    if (kv->layout != TRI_LAYOUT_PAGED) return -1;
+    const int ps = kv->page_size;
+    if (ps <= 0 || (ps & (ps - 1))) return -1;
+    int sh = 0;
+    while ((1 << sh) < ps) ++sh;
+    return sh;
+}
+
 CacheView view_of(const tri_cache_desc* kv) {
     CacheView v;
     v.k = static_cast<const uint8_t*>(kv->k);
@@ -109,6 +121,7 @@ CacheView view_of(const tri_cache_desc* kv) {
     v.page_table = kv->layout == TRI_LAYOUT_PAGED ? kv->page_table : nullptr;
     v.capacity = kv->capacity;
     v.page_size = kv->layout == TRI_LAYOUT_PAGED ? kv->page_size : 0;
+    v.page_shift = page_shift_of(kv);
     v.max_pages = kv->layout == TRI_LAYOUT_PAGED ? kv->max_pages : 0;
     v.row_bytes = kv->head_dim * elem_size(kv->dtype);
     return v;
@@ -122,6 +135,7 @@ CacheOut out_of(const tri_cache_desc* kv) {
     o.page_table = kv->layout == TRI_LAYOUT_PAGED ? kv->page_table : nullptr;
     o.capacity = kv->capacity;
     o.page_size = kv->layout == TRI_LAYOUT_PAGED ? kv->page_size : 0;
+    o.page_shift = page_shift_of(kv);
     o.max_pages = kv->layout == TRI_LAYOUT_PAGED ? kv->max_pages : 0;
     return o;
 }
@@ -387,7 +401,7 @@ int tri_score(tri_calib_t calib, const tri_cache_desc* kv, const int32_t* t, flo
     if (!t || !agg) return TRI_ERR_INVALID_ARG;
     if (kv->capacity > kMaxLen) return TRI_ERR_UNSUPPORTED;
     const WsPlan p = plan_workspace(calib, kv);
-    if (!ws || ws_bytes < p.total) return TRI_ERR_WORKSPACE;
+    if (!ws || ws_bytes < p.total || !aligned256(ws)) return TRI_ERR_WORKSPACE;
     if (!device_present()) return TRI_ERR_NO_DEVICE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(ws);
@@ -490,7 +504,7 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     if (!t || !n_kept) return TRI_ERR_INVALID_ARG;
     if (src->capacity > kMaxLen) return TRI_ERR_UNSUPPORTED;
     const WsPlan p = plan_workspace(calib, src);
-    if (!ws || ws_bytes < p.total) return TRI_ERR_WORKSPACE;
+    if (!ws || ws_bytes < p.total || !aligned256(ws)) return TRI_ERR_WORKSPACE;
     if (!device_present()) return TRI_ERR_NO_DEVICE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* w = static_cast<char*>(ws);
@@ -625,7 +639,8 @@ int tri_calibrate(const void* q, int dtype, int n_layers, int n_samples, int n_q
     if (rc) return rc;
     if (!q || !mag || !phase || !conc) return TRI_ERR_INVALID_ARG;
     if (dtype != TRI_DTYPE_F32 && dtype != TRI_DTYPE_BF16) return TRI_ERR_INVALID_ARG;
-    if (!ws || ws_bytes < calib_ws_bytes(n_layers, n_samples, n_q_heads, head_dim)) return TRI_ERR_WORKSPACE;
+    if (!ws || ws_bytes < calib_ws_bytes(n_layers, n_samples, n_q_heads, head_dim) || !aligned256(ws))
+        return TRI_ERR_WORKSPACE;
     if (!device_present()) return TRI_ERR_NO_DEVICE;
     CalibArgs a;
     a.q = static_cast<const uint8_t*>(q);

@@ -40,13 +40,22 @@ struct CacheView {
     const int32_t* page_table;   // paged only
     int64_t capacity;            // dense: rows per segment
     int32_t page_size;           // paged only (>0 means paged)
+    int32_t page_shift;          // log2(page_size) for a power of two, else -1
     int32_t max_pages;
     int32_t row_bytes;           // head_dim * element size
 
+    // Slot n (< 2^31) of a paged segment sits in page-table entry
+    // page_entry(n), row page_within(n) of that page.
+    __device__ __forceinline__ int page_entry(int n) const {
+        return page_shift >= 0 ? n >> page_shift : (int)((uint32_t)n / (uint32_t)page_size);
+    }
+    __device__ __forceinline__ int page_within(int n) const {
+        return page_shift >= 0 ? n & (page_size - 1) : (int)((uint32_t)n % (uint32_t)page_size);
+    }
     __device__ __forceinline__ int64_t row(int64_t s, int64_t n) const {
         if (page_size > 0) {
-            const int64_t page = page_table[s * max_pages + n / page_size];
-            return page * page_size + n % page_size;
+            const int64_t page = page_table[s * max_pages + page_entry((int)n)];
+            return page * page_size + page_within((int)n);
         }
         return s * capacity + n;
     }
@@ -59,12 +68,16 @@ struct CacheOut {
     const int32_t* page_table;
     int64_t capacity;
     int32_t page_size;
+    int32_t page_shift;
     int32_t max_pages;
 
     __device__ __forceinline__ int64_t row(int64_t s, int64_t n) const {
         if (page_size > 0) {
-            const int64_t page = page_table[s * max_pages + n / page_size];
-            return page * page_size + n % page_size;
+            const uint32_t un = (uint32_t)n;
+            const uint32_t e = page_shift >= 0 ? un >> page_shift : un / (uint32_t)page_size;
+            const uint32_t w = page_shift >= 0 ? un & (uint32_t)(page_size - 1) : un - e * (uint32_t)page_size;
+            const int64_t page = page_table[s * max_pages + e];
+            return page * page_size + w;
         }
         return s * capacity + n;
     }

@@ -171,20 +171,25 @@ __global__ __launch_bounds__(256) void k_decode_attn(AttnArgs a) {
     }
 }
 
-// bf16 caches.  One 256-thread workgroup per segment; wave w takes the key
-// tiles w, w+4, ... (TK keys each: 32 for head_dim 64, 16 for 128, so a K or V
-// tile is 4 KB).  Tiles come in through LDS DMA, whole rows per instruction,
-// two tiles in flight per wave (double buffer); rows are chunk-swizzled
-// (16-byte chunk lc of tile key k at lc ^ (k mod CPR)).
+// bf16 caches.  One workgroup of NW waves per segment; wave w takes the key
+// tiles w, w+NW, ... (TK keys each: 32 for head_dim 64, 16 for 128, so a K or
+// V tile is 4 KB).  A tile comes in through LDS DMA, whole rows per
+// instruction, rows chunk-swizzled (16-byte chunk lc of tile key k at
+// lc ^ (k mod CPR)).  Each wave keeps one tile in flight and computes only
+// once it has landed: the compiler makes every LDS read wait for all LDS DMA
+// still in flight, so a per-wave second buffer would not overlap anything;
+// the overlap comes from the waves of the other workgroups on the CU.
 //  * logits q.K^T on the matrix cores: A = 16 key rows, B = the G query
 //    vectors as columns (bf16, so the products are exact; fp32 accumulation);
 //  * online softmax per head (base 2) on the fragment layout: lane (grp, row)
 //    holds head `row`'s logits of keys 4 grp + r;
 //  * P.V on the vector units: lane = output dimension, the tile's V rows read
 //    from LDS, probabilities broadcast from LDS.
-// The four waves' (max, sum, partial output) are merged at the end.
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
+// The waves' (max, sum, partial output) are merged at the end.
+// Paged caches: lane l holds the page of key l of the wave's next tile, read
+// (a plain load into a register) while the current tile is computed.
+template <int D, int G, bool PAGED, int NW>
+__global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
     constexpr int ROWB = D * 2, CPR = ROWB / 16;
     constexpr int TK = 2048 / D;               // keys per tile
     constexpr int NU = TK / 16;                // 16-key MFMA tiles per tile
@@ -193,11 +198,11 @@ __global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
     constexpr int DPL = D / kWave;             // output dims per lane
     constexpr float kLog2e = 1.4426950408889634f;
     static_assert(G <= 16 && NU >= 1, "one 16-column B fragment holds the group");
-    __shared__ uint4 kt[4][2][TK * CPR];
-    __shared__ uint4 vt[4][2][TK * CPR];
-    __shared__ float pt[4][G][TK];
-    __shared__ float alph[4][G];
-    __shared__ float wm[4][G], wl[4][G];
+    __shared__ uint4 kt[NW][TK * CPR];
+    __shared__ uint4 vt[NW][TK * CPR];
+    __shared__ float pt[NW][G][TK];
+    __shared__ float alph[NW][G];
+    __shared__ float wm[NW][G], wl[NW][G];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const int row = lane & 15, grp = lane >> 4;
@@ -208,20 +213,32 @@ __global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
     const float sl2 = a.scale * kLog2e;
     const int nt = (N + TK - 1) / TK;
 
-    auto issue = [&](int t, int buf) {
+    int pg = 0;                                // paged: page of key (lane mod TK) of the next tile
+    auto fetch_pages = [&](int t) {
+        if constexpr (PAGED) {
+            const int key = min(t * TK + lane % TK, N - 1);
+            pg = a.kv.page_table[(int64_t)s * a.kv.max_pages + a.kv.page_entry(key)];
+        }
+    };
+    auto issue = [&](int t) {
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
             const int P = 64 * i + lane;
             const int kl = P / CPR;
             const int lc = (P % CPR) ^ (kl % CPR);
             const int key = min(t * TK + kl, N - 1);          // tail rows re-read a valid row
-            const int64_t off = a.kv.row(s, key) * ROWB + 16 * lc;
-            __builtin_amdgcn_global_load_lds(a.kv.k + off, (lds_void_t*)(&kt[w][buf][0] + 64 * i), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(a.kv.v + off, (lds_void_t*)(&vt[w][buf][0] + 64 * i), 16, 0, 0);
+            int64_t r;
+            if constexpr (PAGED) r = (int64_t)__shfl(pg, kl, kWave) * a.kv.page_size + a.kv.page_within(key);
+            else r = (int64_t)s * a.kv.capacity + key;
+            const int64_t off = r * ROWB + 16 * lc;
+            __builtin_amdgcn_global_load_lds(a.kv.k + off, (lds_void_t*)(&kt[w][0] + 64 * i), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(a.kv.v + off, (lds_void_t*)(&vt[w][0] + 64 * i), 16, 0, 0);
         }
     };
-    if (w < nt) issue(w, 0);
-    if (w + 4 < nt) issue(w + 4, 1);
+    if (w < nt) {
+        fetch_pages(w);
+        issue(w);
+    }
 
     // B fragments: column row = head row (zero past G), k-slot (grp, e)
     bf16x8_t bq[TS];
@@ -239,12 +256,11 @@ __global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int d = 0; d < DPL; ++d) o[g][d] = 0.0f;
 
-    for (int t = w, it = 0; t < nt; t += 4, ++it) {
-        const int buf = it & 1;
-        if (t + 4 < nt) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NDMA));   // the next tile may stay in flight
-        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    for (int t = w; t < nt; t += NW) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);              // this tile has landed
         __builtin_amdgcn_wave_barrier();
-        const uint4* kr = &kt[w][buf][0];
+        if (t + NW < nt) fetch_pages(t + NW);              // completes under this tile's compute
+        const uint4* kr = &kt[w][0];
         float x[NU][4];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
@@ -288,7 +304,7 @@ __global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
         if (row < G && grp == 0) alph[w][row] = alpha;
         __builtin_amdgcn_wave_barrier();
         // P.V: lane = output dims lane + 64 dd
-        const uint4* vr = &vt[w][buf][0];
+        const uint4* vr = &vt[w][0];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float al = alph[w][g];
@@ -311,14 +327,14 @@ __global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
                 for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(p, v[d], o[g][d]);
             }
         }
-        __builtin_amdgcn_wave_barrier();
-        if (t + 8 < nt) issue(t + 8, buf);                 // this buffer is free again
+        __builtin_amdgcn_wave_barrier();                   // the tile buffers are free again
+        if (t + NW < nt) issue(t + NW);
     }
 
-    // merge the four waves (their tile buffers hold the partial outputs)
+    // merge the waves (their tile buffers hold the partial outputs)
     __syncthreads();
-    float* wo = reinterpret_cast<float*>(&kt[0][0][0]);   // [4][G][D]
-    static_assert(sizeof(kt) >= sizeof(float) * 4 * G * D, "partial outputs fit the K tiles");
+    float* wo = reinterpret_cast<float*>(&kt[0][0]);      // [NW][G][D]
+    static_assert(sizeof(kt) >= sizeof(float) * NW * G * D, "partial outputs fit the K tiles");
     if (grp == 0 && row < G) {
         wm[w][row] = m;
         wl[w][row] = lsum;
@@ -329,14 +345,14 @@ __global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
         for (int d = 0; d < DPL; ++d) wo[(w * G + g) * D + lane + d * kWave] = o[g][d];
     __syncthreads();
     float* out = a.out + (((int64_t)l * a.shape.n_seq + b) * a.n_q_heads + (int64_t)h * G) * D;
-    for (int i = tid; i < G * D; i += 256) {
+    for (int i = tid; i < G * D; i += NW * 64) {
         const int g = i / D, d = i - g * D;
         float M = -__builtin_inff();
 #pragma unroll
-        for (int v = 0; v < 4; ++v) M = fmaxf(M, wm[v][g]);
+        for (int v = 0; v < NW; ++v) M = fmaxf(M, wm[v][g]);
         float num = 0.0f, den = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < NW; ++v) {
             const float sc = wl[v][g] > 0.0f ? __builtin_amdgcn_exp2f(wm[v][g] - M) : 0.0f;
             num = fmaf(wo[(v * G + g) * D + d], sc, num);
             den = fmaf(wl[v][g], sc, den);
@@ -345,10 +361,19 @@ __global__ __launch_bounds__(256) void k_decode_attn_mfma(AttnArgs a) {
     }
 }
 
+// Waves per decode-attention workgroup.  Four single-buffered waves (about
+// 37 KB of LDS) let four workgroups share a CU: the same 16 waves per CU as
+// 2 x 8 or 1 x 16, with more tiles per wave to amortise each workgroup's
+// start and a cheaper final merge (measured fastest of 4, 8 and 16).
+constexpr int kAttnWaves = 4;
+
 template <int D, int G>
 static void attn_dtype(const AttnArgs& a, bool bf16, hipStream_t stream) {
     const dim3 grid((unsigned)a.n_seg), block(256);
-    if (bf16) hipLaunchKernelGGL((k_decode_attn_mfma<D, G>), grid, block, 0, stream, a);
+    if (bf16 && a.kv.page_size > 0)
+        hipLaunchKernelGGL((k_decode_attn_mfma<D, G, true, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, stream, a);
+    else if (bf16)
+        hipLaunchKernelGGL((k_decode_attn_mfma<D, G, false, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, stream, a);
     else hipLaunchKernelGGL((k_decode_attn<D, G, false>), grid, block, 0, stream, a);
 }
 

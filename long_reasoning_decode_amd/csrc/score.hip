@@ -200,14 +200,14 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Component q (0: hi, 1: mid, 2: lo) of the three-way bf16 split of x.
+// Component q (0: hi, 1: mid, 2: lo) of the three-way bf16 split of x
+// (all three parts are formed and one is selected: no branch on q).
 __device__ __forceinline__ uint32_t bf16_split3(float x, int q) {
     const uint32_t h = bf16_rne_bits(x);
-    if (q == 0) return h;
     const float r1 = x - __uint_as_float(h << 16);
     const uint32_t m = bf16_rne_bits(r1);
-    if (q == 1) return m;
-    return bf16_rne_bits(r1 - __uint_as_float(m << 16));
+    const uint32_t l = bf16_rne_bits(r1 - __uint_as_float(m << 16));
+    return q == 0 ? h : (q == 1 ? m : l);
 }
 
 // Chan merge of (n, mean, M2) summaries.
@@ -238,35 +238,37 @@ __device__ __forceinline__ void mfma_coef_fragments(const float* ctab, const flo
     const int l = shape.layer(s), b = shape.seq(s), hk = shape.head(s);
     const float* cb = ctab + ((int64_t)(l * shape.n_seq + b) * n_q_heads + hk * G) * D;
     const float* wb = wtab + ((int64_t)l * n_q_heads + hk * G) * F;
+    // All of a column's coefficients are loaded first (8 consecutive floats per
+    // fragment, two 16-byte loads; h < G, so unused columns read valid rows and
+    // are zeroed afterwards), then split: one wait instead of one per element.
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int jg = 16 * t + row;
         const bool used = jg < NCOL;
         const int q = jg / G, h = jg % G;
+        float4 cv[TS][2], wv[NS][2];
 #pragma unroll
-        for (int st = 0; st < TS; ++st) {
+        for (int st = 0; st < TS; ++st)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                cv[st][x] = *reinterpret_cast<const float4*>(cb + h * D + 32 * st + 8 * grp + 4 * x);
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                wv[st][x] = *reinterpret_cast<const float4*>(wb + h * F + 32 * st + 8 * grp + 4 * x);
+        auto pack = [&](const float4 (&v)[2]) {
+            const float e[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
             uint32_t w[4];
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int d0 = 32 * st + 8 * grp + 2 * e2;
-                const uint32_t lo = used ? bf16_split3(cb[h * D + d0], q) : 0u;
-                const uint32_t hi = used ? bf16_split3(cb[h * D + d0 + 1], q) : 0u;
-                w[e2] = lo | (hi << 16);
-            }
-            bt[st][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-        }
+            for (int e2 = 0; e2 < 4; ++e2)
+                w[e2] = used ? (bf16_split3(e[2 * e2], q) | (bf16_split3(e[2 * e2 + 1], q) << 16)) : 0u;
+            return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+        };
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            uint32_t w[4];
+        for (int st = 0; st < TS; ++st) bt[st][t] = pack(cv[st]);
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int f0 = 32 * st + 8 * grp + 2 * e2;
-                const uint32_t lo = used ? bf16_split3(wb[h * F + f0], q) : 0u;
-                const uint32_t hi = used ? bf16_split3(wb[h * F + f0 + 1], q) : 0u;
-                w[e2] = lo | (hi << 16);
-            }
-            bn[st][t] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
-        }
+        for (int st = 0; st < NS; ++st) bn[st][t] = pack(wv[st]);
     }
 }
 
@@ -342,7 +344,7 @@ constexpr int kScoreLds = 40960;
 // a chunk scores blocks w, w+4, w+8, ..., so its list holds at most
 // G * wave_keys(w, cnt) floats; the four lists sit back to back in the scratch
 // rows of the chunk's keys.  The chunk statistics always cover every key.
-template <int D, int G, bool CAND>
+template <int D, int G, bool CAND, bool PAGED>
 __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s, const int c) {
     constexpr int F = D / 2;
     constexpr int TS = D / 32;               // trig k-steps = 16-byte A fragments per key
@@ -389,9 +391,7 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
         list = a.s_int + ((int64_t)s * a.cap + start + wave_list_base(wave, cnt)) * G;
     }
 
-    // loop-invariant B fragments
-    bf16x8_t bt[TS][NT], bn[NS][NT];
-    mfma_coef_fragments<D, G>(a.ctab, a.wtab, a.shape, a.n_q_heads, s, bt, bn);
+    bf16x8_t bt[TS][NT], bn[NS][NT];           // loop-invariant B fragments, loaded below
 
     // per-lane running statistics for head `row` (lanes row < G), shifted by
     // the lane's first score
@@ -399,6 +399,17 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
     int cntl = 0;
     const int n_tiles = (cnt + 15) / 16;
     uint4* region = &stage[wave][0];
+    // Paged caches: lane l holds the page of key l of the next stage to issue
+    // (loaded one stage ahead, so the page-table read completes under the
+    // current stage instead of delaying the next stage's DMA); each DMA lane
+    // takes its row's page from that lane.
+    int pg = 0;
+    auto fetch_pages = [&](int tb) {
+        if constexpr (PAGED) {
+            const int key = min(tb * 16 + (lane & (SKEYS - 1)), cnt - 1);
+            pg = a.kv.page_table[(int64_t)s * a.kv.max_pages + a.kv.page_entry(start + key)];
+        }
+    };
     // DMA of the stage whose first tile is tb: instruction i, lane l fills
     // chunk position P = 64 i + l, i.e. key P / CPR, chunk (P mod CPR) ^ key.
     auto issue_stage = [&](int tb) {
@@ -408,7 +419,10 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
             const int kl = P / CPR;
             const int lc = (P % CPR) ^ (kl % CPR);
             const int key = min(tb * 16 + kl, cnt - 1);            // clamped: tail rows re-read a valid row
-            const uint8_t* src = a.kv.k + a.kv.row(s, start + key) * ROWB + 16 * lc;
+            int64_t r;
+            if constexpr (PAGED) r = (int64_t)__shfl(pg, kl, kWave) * a.kv.page_size + a.kv.page_within(start + key);
+            else r = (int64_t)s * a.kv.capacity + start + key;
+            const uint8_t* src = a.kv.k + r * ROWB + 16 * lc;
             __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + 64 * i), 16, 0, 2 /* nt */);
         }
     };
@@ -421,7 +435,13 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
             __builtin_amdgcn_wave_barrier();
         }
     };
-    if (wave * UT < n_tiles) issue_stage(wave * UT);
+    if (wave * UT < n_tiles) {
+        fetch_pages(wave * UT);
+        issue_stage(wave * UT);
+        fetch_pages(wave * UT + 4 * UT);
+    }
+    // the coefficient loads follow the first stage's DMA, so the two latencies overlap
+    mfma_coef_fragments<D, G>(a.ctab, a.wtab, a.shape, a.n_q_heads, s, bt, bn);
     for (int tb = wave * UT; tb < n_tiles; tb += 4 * UT) {
         uint4 av[UT][TS];
             __builtin_amdgcn_s_waitcnt(kWaitVm0);                      // this stage's DMA has landed
@@ -434,7 +454,10 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                    // fragments are in registers
         __builtin_amdgcn_wave_barrier();
-        if (tb + 4 * UT < n_tiles) issue_stage(tb + 4 * UT);       // next stage loads under this compute
+        if (tb + 4 * UT < n_tiles) {                               // next stage loads under this compute
+            issue_stage(tb + 4 * UT);
+            fetch_pages(tb + 8 * UT);
+        }
         if constexpr (CAND) {
             if (nb + SKEYS * G > CAPF) flush_records();              // no room to stage this stage's scores
         }
@@ -557,21 +580,21 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
 }
 
 // (at most 128 VGPRs for head_dim 128 with G <= 4, so four workgroups share a CU)
-template <int D, int G, bool CAND>
+template <int D, int G, bool CAND, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 1))) void k_score_mfma(ScoreArgs a) {
     const int s = blockIdx.x / a.n_chunks;
-    score_chunk_mfma<D, G, CAND>(a, s, blockIdx.x - s * a.n_chunks);
+    score_chunk_mfma<D, G, CAND, PAGED>(a, s, blockIdx.x - s * a.n_chunks);
 }
 
 // Full scoring of the segments whose candidate pass failed its certificate:
 // work items (listed segment, chunk), grid-strided.
-template <int D, int G>
+template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(256) void k_score_mfma_fallback(ScoreArgs a) {
     const int64_t items = (int64_t)(*a.fb_count) * a.n_chunks;
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         __syncthreads();                      // LDS of the previous item is no longer read
         const int s = a.fb_list[it / a.n_chunks];
-        score_chunk_mfma<D, G, false>(a, s, (int)(it % a.n_chunks));
+        score_chunk_mfma<D, G, false, PAGED>(a, s, (int)(it % a.n_chunks));
     }
 }
 
@@ -745,6 +768,17 @@ static void score_kernel(const ScoreArgs& a, hipStream_t stream) {
                        stream, a);
 }
 
+template <int D, int G, bool PAGED>
+static void score_mfma_launch(const ScoreArgs& a, int mode, int64_t items, hipStream_t stream) {
+    if (mode == SCORE_FULL)
+        hipLaunchKernelGGL((k_score_mfma<D, G, false, PAGED>), dim3((unsigned)items), dim3(256), 0, stream, a);
+    else if (mode == SCORE_CANDIDATES)
+        hipLaunchKernelGGL((k_score_mfma<D, G, true, PAGED>), dim3((unsigned)items), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_score_mfma_fallback<D, G, PAGED>), dim3((unsigned)(items < 2048 ? items : 2048)),
+                           dim3(256), 0, stream, a);
+}
+
 template <int D, int G>
 static bool score_dtype(const ScoreArgs& a, bool bf16, int mode, hipStream_t stream) {
     const int64_t items = (int64_t)a.n_seg * a.n_chunks;
@@ -753,13 +787,8 @@ static bool score_dtype(const ScoreArgs& a, bool bf16, int mode, hipStream_t str
         score_kernel<D, G, false>(a, stream);
         return true;
     }
-    if (mode == SCORE_FULL)
-        hipLaunchKernelGGL((k_score_mfma<D, G, false>), dim3((unsigned)items), dim3(256), 0, stream, a);
-    else if (mode == SCORE_CANDIDATES)
-        hipLaunchKernelGGL((k_score_mfma<D, G, true>), dim3((unsigned)items), dim3(256), 0, stream, a);
-    else
-        hipLaunchKernelGGL((k_score_mfma_fallback<D, G>), dim3((unsigned)(items < 2048 ? items : 2048)), dim3(256), 0,
-                           stream, a);
+    if (a.kv.page_size > 0) score_mfma_launch<D, G, true>(a, mode, items, stream);
+    else score_mfma_launch<D, G, false>(a, mode, items, stream);
     return true;
 }
 

@@ -179,7 +179,9 @@ def test_calibrate_validation():
     lib = T.load()
     q = torch.zeros(2, 10, 4, 64)
     out = torch.zeros(2, 4, 32)
-    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    raw = torch.zeros((1 << 16) + 256, dtype=torch.uint8)
+    skip = (-raw.data_ptr()) % 256
+    ws = raw[skip:skip + (1 << 16)]                           # workspaces start on 256-byte boundaries
     n = ctypes.c_size_t(0)
     assert lib.tri_calibrate_workspace_size(2, 10, 4, 64, ctypes.byref(n)) == T.TRI_OK and n.value > 0
     assert lib.tri_calibrate_workspace_size(2, 10, 4, 63, ctypes.byref(n)) == T.TRI_ERR_INVALID_ARG
@@ -191,5 +193,7 @@ def test_calibrate_validation():
     assert cal(ns=0) == T.TRI_ERR_INVALID_ARG
     assert cal(qp=None) == T.TRI_ERR_INVALID_ARG
     assert cal(wb=16) == T.TRI_ERR_WORKSPACE
+    assert lib.tri_calibrate(T._p(q), T.TRI_DTYPE_F32, 2, 10, 4, 64, T._p(out), T._p(out), T._p(out),
+                             ctypes.c_void_p(ws.data_ptr() + 16), ws.numel() - 16, None) == T.TRI_ERR_WORKSPACE
     if not torch.cuda.is_available():
         assert cal() == T.TRI_ERR_NO_DEVICE
