@@ -188,6 +188,7 @@ def bench_decode_loop(args, T, W):
     copied = moved.get("rows", cfg.n_seg * B) if in_place else cfg.n_seg * B
     prune_bytes = cfg.n_seg * (B + win) * cfg.head_dim * es + copied * (4 * cfg.head_dim * es + 8)
     kernels = {k: {"avg_ms": round(v[1] / v[0], 4), "launches": v[0]} for k, v in kt.items() if v[0]}
+    kernels["decode_attn"]["algorithmic_bytes"] = round(attn_bytes / win)        # per launch, window average
     prune_ms = sum(v["avg_ms"] for k, v in kernels.items() if k not in ("append", "decode_attn"))
     tokens = win * cfg.n_seq
     result = {
@@ -202,7 +203,8 @@ def bench_decode_loop(args, T, W):
                                 f"{'in place' if in_place else 'into a second cache'})"),
                    "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "kernel": "decode_attn", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic("decode_attn", "gptoss")},
         "prune": {"algorithmic_bytes": prune_bytes, "ms": round(prune_ms, 4),
                   "achieved_GBs": round(prune_bytes / (prune_ms * 1e-3) / 1e9, 1),
                   "in_place": in_place, "rows_copied": copied},
@@ -244,6 +246,7 @@ def bench_calibrate(args, T, W):
     kt = T.tri_timing_read()
     kernels = {k: {"avg_ms": round(v[1] / v[0], 4), "launches": v[0]} for k, v in kt.items() if v[0]}
     alg = q.numel() * q.element_size() + 3 * mag.numel() * 4
+    kernels["calibrate"]["algorithmic_bytes"] = q.numel() * q.element_size()
     part = kernels["calibrate"]["avg_ms"]
     gbs = q.numel() * q.element_size() / (part * 1e-3) / 1e9
     result = {
@@ -254,7 +257,8 @@ def bench_calibrate(args, T, W):
         "config": {"workload": f"calib: {L} layers x {n} samples x {Hq} query heads x {d} dims, bf16 pre-RoPE queries",
                    "algorithmic_bytes": alg},
         "roofline": {"bound": "hbm", "kernel": "calibrate", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic("calibrate", "calib")},
         "kernels": kernels,
     }
     print(json.dumps(result), flush=True)
@@ -314,6 +318,8 @@ def bench_ragged(args, T, W):
     prune_ms = sum(v["avg_ms"] for k, v in kernels.items() if k != "decode_attn")
     attn_bytes = int(kept.sum()) * cfg.head_dim * es * 2
     attn_gbs = attn_bytes / (kernels["decode_attn"]["avg_ms"] * 1e-3) / 1e9
+    kernels["decode_attn"]["algorithmic_bytes"] = attn_bytes
+    kernels["score"]["algorithmic_bytes"] = n_keys * cfg.head_dim * es
     result = {
         "metric": "keys scored+pruned/sec on the ragged paged batch (G keys/s)",
         "value": round(n_keys / (prune_ms * 1e-3) / 1e9, 3), "unit": "G keys/s",
@@ -326,7 +332,7 @@ def bench_ragged(args, T, W):
                      "achieved_GBs": round(prune_bytes / (prune_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "kernel": "decode_attn (paged)", "achieved": round(attn_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": read_traffic("decode_attn", "ragged")},
         "kernels": kernels, "fallback_segments": T.tri_prune_fallbacks(ws),
     }
     calib.free()
