@@ -144,8 +144,9 @@ int tri_calib_free(tri_calib_t calib);
  *           the layout tri_calib_load takes (copy them to the host for it).
  *   ws    : device workspace of tri_calibrate_workspace_size bytes, 256-byte
  *           aligned (TRI_ERR_WORKSPACE otherwise).
- * Per-sample arithmetic is fp32 and the sums are fp64, added in a fixed order
- * (results do not depend on scheduling).  head_dim 64 or 128.
+ * Per-sample arithmetic is fp32; each run of at most eight samples is summed
+ * in fp32 and added to fp64 sums, in a fixed order that depends only on the
+ * shape (results do not depend on scheduling).  head_dim 64 or 128.
  */
 int tri_calibrate_workspace_size(int n_layers, int n_samples, int n_q_heads, int head_dim, size_t* bytes);
 int tri_calibrate(const void* q, int dtype, int n_layers, int n_samples, int n_q_heads, int head_dim, float* mag,

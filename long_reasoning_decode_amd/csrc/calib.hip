@@ -6,117 +6,98 @@
 // resultant length).  These are the inputs tri_calib_load folds.
 //
 // Layout: q [L][n_samples][Hq][d] (one row per sample and head); band f of a row
-// is q[f] + i q[f+F].  Pass 1: one-wave workgroup (layer, chunk of kCalibChunk
-// samples, block of 64 (head, 8-band) groups); lane t owns one group and loads
-// 16 bytes of real parts and the matching 16 bytes of imaginary parts per
-// sample (eight bf16 samples in flight), so the wave reads 2 KB of each sample's rows
-// contiguously.  Per sample and band it
-// forms |q_f| and q_f/|q_f| in fp32 and adds the five sums (|q|, Re, Im, unit
-// Re, unit Im) in fp64.  Pass 2 adds the chunks in order (deterministic) and
-// forms M, phi, R.
+// is q[f] + i q[f+F].  Pass 1: one-wave workgroup (layer, chunk of chunk_len
+// samples, block of 64 (head, 4-band) groups); lane t owns one group and loads
+// the 4 real parts and the matching 4 imaginary parts per sample, so the wave
+// reads 1 KB of each sample's rows contiguously (four heads at head_dim 128).
+// Per sample and band it forms |q_f| and q_f/|q_f| in fp32 and adds them to
+// the five sums (|q|, Re, Im, unit Re, unit Im): in fp32 over one batch of at
+// most eight samples (within about eight ulps of the terms' magnitude), each
+// batch then added to fp64 sums, which cuts the fp64-rate work eightfold.
+// Four bands per lane keep the sums to 60 registers, so four waves share a
+// SIMD, each with eight samples' loads in flight.  Pass 2 adds the chunks in order
+// (deterministic) and forms M, phi, R.
 #include "launch.h"
 
 namespace tri {
 
 template <bool BF16>
-__device__ __forceinline__ void load8(const uint8_t* p, float (&x)[8]) {
-    if constexpr (BF16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[2 * e] = bf16_lo(w[e]);
-            x[2 * e + 1] = bf16_hi(w[e]);
-        }
-    } else {
-        const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    }
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(64) void k_calib_partial(CalibArgs a) {
-    constexpr int ES = BF16 ? 2 : 4;
-    const int F = a.head_dim / 2, gpr = F / 8;          // 8-band groups per head
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 1))) void k_calib_partial(CalibArgs a) {
+    constexpr int ES = BF16 ? 2 : 4, NB = kCalibBands;
+    using raw_t = typename std::conditional<BF16, uint2, float4>::type;   // one lane's NB stored values
+    const int F = a.head_dim / 2, gpr = F / NB;          // band groups per head
     const int l = blockIdx.x / a.n_chunks, c = blockIdx.x - l * a.n_chunks;
     const int g = blockIdx.y * 64 + threadIdx.x;         // (head, band group)
     if (g >= a.n_q_heads * gpr) return;
-    const int h = g / gpr, f0 = (g - h * gpr) * 8;
-    const int s0 = c * kCalibChunk, s1 = min(s0 + kCalibChunk, a.n_samples);
+    const int h = g / gpr, f0 = (g - h * gpr) * NB;
+    const int s0 = c * a.chunk_len, s1 = min(s0 + a.chunk_len, a.n_samples);
     const int64_t rowb = (int64_t)a.head_dim * ES;
     const uint8_t* base = a.q + (((int64_t)l * a.n_samples) * a.n_q_heads + h) * rowb;
     const int64_t sstride = (int64_t)a.n_q_heads * rowb;
-    double sm[8], sr[8], si[8], ur[8], ui[8];
+    double sm[NB], sr[NB], si[NB], ur[NB], ui[NB];
+    float bm[NB], br[NB], bi[NB], bu[NB], bv[NB];      // the current batch's sums
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm[e] = sr[e] = si[e] = ur[e] = ui[e] = 0.0;
-    auto add = [&](const float (&re)[8], const float (&im)[8]) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float r2 = fmaf(re[e], re[e], im[e] * im[e]);
-            const float rs = r2 > 0.0f ? __builtin_amdgcn_rsqf(r2) : 0.0f;
-            sm[e] += (double)(r2 * rs);
-            sr[e] += (double)re[e];
-            si[e] += (double)im[e];
-            ur[e] += (double)(re[e] * rs);
-            ui[e] += (double)(im[e] * rs);
+    for (int e = 0; e < NB; ++e) {
+        sm[e] = sr[e] = si[e] = ur[e] = ui[e] = 0.0;
+        bm[e] = br[e] = bi[e] = bu[e] = bv[e] = 0.0f;
+    }
+    auto unpack = [&](const raw_t& v, float (&x)[NB]) {
+        if constexpr (BF16) {
+            x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+        } else {
+            x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
         }
     };
+    auto add = [&](const raw_t& rv, const raw_t& iv) {
+        float re[NB], im[NB];
+        unpack(rv, re);
+        unpack(iv, im);
+#pragma unroll
+        for (int e = 0; e < NB; ++e) {
+            const float r2 = fmaf(re[e], re[e], im[e] * im[e]);
+            const float rs = r2 > 0.0f ? __builtin_amdgcn_rsqf(r2) : 0.0f;
+            bm[e] += r2 * rs;
+            br[e] += re[e];
+            bi[e] += im[e];
+            bu[e] += re[e] * rs;
+            bv[e] += im[e] * rs;
+        }
+    };
+    auto fold = [&]() {                                  // batch sums -> fp64 sums
+#pragma unroll
+        for (int e = 0; e < NB; ++e) {
+            sm[e] += (double)bm[e];
+            sr[e] += (double)br[e];
+            si[e] += (double)bi[e];
+            ur[e] += (double)bu[e];
+            ui[e] += (double)bv[e];
+            bm[e] = br[e] = bi[e] = bu[e] = bv[e] = 0.0f;
+        }
+    };
+    const uint8_t* pr = base + (int64_t)f0 * ES;         // the lane's real parts in sample 0
+    const uint8_t* pi = base + (int64_t)(F + f0) * ES;   // and imaginary parts
     int s = s0;
-    if constexpr (BF16) {
-        // eight samples' raw 16-byte loads in flight, unpacked as they are added
-        constexpr int U = 8;
-        for (; s + U <= s1; s += U) {
-            uint4 rv[U], iv[U];
-            const uint8_t* p0 = base + (int64_t)s * sstride;
+    // eight samples' raw loads in flight, unpacked as they are added
+    constexpr int U = 8;
+    for (; s + U <= s1; s += U) {
+        raw_t rv[U], iv[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                rv[u] = *reinterpret_cast<const uint4*>(p0 + u * sstride + f0 * ES);
-                iv[u] = *reinterpret_cast<const uint4*>(p0 + u * sstride + (F + f0) * ES);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float re[8], im[8];
-                const uint32_t rw[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w}, iw[4] = {iv[u].x, iv[u].y, iv[u].z, iv[u].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    re[2 * e] = bf16_lo(rw[e]);
-                    re[2 * e + 1] = bf16_hi(rw[e]);
-                    im[2 * e] = bf16_lo(iw[e]);
-                    im[2 * e + 1] = bf16_hi(iw[e]);
-                }
-                add(re, im);
-            }
+        for (int u = 0; u < U; ++u) {
+            rv[u] = *reinterpret_cast<const raw_t*>(pr + (int64_t)(s + u) * sstride);
+            iv[u] = *reinterpret_cast<const raw_t*>(pi + (int64_t)(s + u) * sstride);
         }
-    } else {
-        for (; s + 4 <= s1; s += 4) {                    // four samples' loads in flight
-            float re0[8], im0[8], re1[8], im1[8], re2[8], im2[8], re3[8], im3[8];
-            const uint8_t* p0 = base + (int64_t)s * sstride;
-            load8<BF16>(p0 + f0 * ES, re0);
-            load8<BF16>(p0 + (F + f0) * ES, im0);
-            load8<BF16>(p0 + sstride + f0 * ES, re1);
-            load8<BF16>(p0 + sstride + (F + f0) * ES, im1);
-            load8<BF16>(p0 + 2 * sstride + f0 * ES, re2);
-            load8<BF16>(p0 + 2 * sstride + (F + f0) * ES, im2);
-            load8<BF16>(p0 + 3 * sstride + f0 * ES, re3);
-            load8<BF16>(p0 + 3 * sstride + (F + f0) * ES, im3);
-            add(re0, im0);
-            add(re1, im1);
-            add(re2, im2);
-            add(re3, im3);
-        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) add(rv[u], iv[u]);
+        fold();
     }
-    for (; s < s1; ++s) {
-        float re0[8], im0[8];
-        const uint8_t* p0 = base + (int64_t)s * sstride;
-        load8<BF16>(p0 + f0 * ES, re0);
-        load8<BF16>(p0 + (F + f0) * ES, im0);
-        add(re0, im0);
-    }
+    for (; s < s1; ++s)
+        add(*reinterpret_cast<const raw_t*>(pr + (int64_t)s * sstride),
+            *reinterpret_cast<const raw_t*>(pi + (int64_t)s * sstride));
+    fold();
     // partials [L][chunk][Hq][F][5]
     double* out = a.part + ((((int64_t)l * a.n_chunks + c) * a.n_q_heads + h) * F + f0) * 5;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NB; ++e) {
         out[5 * e] = sm[e];
         out[5 * e + 1] = sr[e];
         out[5 * e + 2] = si[e];
@@ -145,7 +126,7 @@ __global__ __launch_bounds__(256) void k_calib_final(CalibArgs a) {
 }
 
 hipError_t launch_calibrate(const CalibArgs& a, bool bf16, hipStream_t stream) {
-    const int groups = a.n_q_heads * (a.head_dim / 16);
+    const int groups = a.n_q_heads * (a.head_dim / 2 / kCalibBands);
     {
         TimedLaunch tl(KID_CALIB, stream);
         const dim3 grid((unsigned)(a.n_layers * a.n_chunks), (unsigned)((groups + 63) / 64));

@@ -192,14 +192,27 @@ hipError_t launch_decode_attn(const AttnArgs& a, int head_dim, int group, bool b
                               hipStream_t stream);
 
 // --- offline calibration from sampled pre-RoPE queries
-constexpr int kCalibChunk = 256;           // samples per pass-1 workgroup
+constexpr int kCalibBands = 4;             // bands per pass-1 lane
+// Samples per pass-1 workgroup (one wave): sized so the grid (layers x chunks
+// x blocks of 64 band groups) is about one round of the one-wave workgroups the
+// chip holds at once (256 CUs x 4 SIMDs x 4 waves); a second, partial round
+// would take as long as the first.  At least 64 samples (the fp64 partials
+// then stay under a sixth of the samples' bytes), a multiple of 8 (one batch).
+constexpr int kCalibResidentWaves = 4096;
+inline int calib_chunk_len(int n_layers, int n_samples, int n_q_heads, int head_dim) {
+    const int64_t blocks = (int64_t)n_layers * ((n_q_heads * (head_dim / 2 / kCalibBands) + 63) / 64);
+    const int64_t chunks = blocks >= kCalibResidentWaves ? 1 : kCalibResidentWaves / blocks;
+    int64_t len = (n_samples + chunks - 1) / chunks;
+    len = len < 64 ? 64 : (len + 7) / 8 * 8;
+    return (int)len;
+}
 struct CalibArgs {
     const uint8_t* q;       // [L][n_samples][Hq][d] stored rows
     double* part;           // [L][n_chunks][Hq][F][5] fp64 partial sums
     float* mag;             // [L][Hq][F]
     float* phase;
     float* conc;
-    int32_t n_layers, n_samples, n_q_heads, head_dim, n_chunks;
+    int32_t n_layers, n_samples, n_q_heads, head_dim, n_chunks, chunk_len;
 };
 hipError_t launch_calibrate(const CalibArgs& a, bool bf16, hipStream_t stream);
 
