@@ -231,8 +231,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
             if constexpr (PAGED) r = (int64_t)__shfl(pg, kl, kWave) * a.kv.page_size + a.kv.page_within(key);
             else r = (int64_t)s * a.kv.capacity + key;
             const int64_t off = r * ROWB + 16 * lc;
-            __builtin_amdgcn_global_load_lds(a.kv.k + off, (lds_void_t*)(&kt[w][0] + 64 * i), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(a.kv.v + off, (lds_void_t*)(&vt[w][0] + 64 * i), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(a.kv.k + off, (lds_void_t*)(&kt[w][0] + 64 * i), 16, 0, 2 /* nt */);
+            __builtin_amdgcn_global_load_lds(a.kv.v + off, (lds_void_t*)(&vt[w][0] + 64 * i), 16, 0, 2 /* nt */);
         }
     };
     if (w < nt) {
