@@ -621,7 +621,8 @@ static int check_calib_shape(int n_layers, int n_samples, int n_q_heads, int hea
 }
 
 static size_t calib_ws_bytes(int n_layers, int n_samples, int n_q_heads, int head_dim) {
-    const int64_t chunks = (n_samples + kCalibChunk - 1) / kCalibChunk;
+    const int len = calib_chunk_len(n_layers, n_samples, n_q_heads, head_dim);
+    const int64_t chunks = (n_samples + len - 1) / len;
     return align256((size_t)n_layers * chunks * n_q_heads * (head_dim / 2) * 5 * sizeof(double));
 }
 
@@ -652,7 +653,8 @@ int tri_calibrate(const void* q, int dtype, int n_layers, int n_samples, int n_q
     a.n_samples = n_samples;
     a.n_q_heads = n_q_heads;
     a.head_dim = head_dim;
-    a.n_chunks = (n_samples + kCalibChunk - 1) / kCalibChunk;
+    a.chunk_len = calib_chunk_len(n_layers, n_samples, n_q_heads, head_dim);
+    a.n_chunks = (n_samples + a.chunk_len - 1) / a.chunk_len;
     return hip_status(launch_calibrate(a, dtype == TRI_DTYPE_BF16, static_cast<hipStream_t>(stream)),
                       "calibration kernel");
 }
