@@ -184,7 +184,8 @@ __global__ __launch_bounds__(256) void k_decode_attn(AttnArgs a) {
 //  * online softmax per head (base 2) on the fragment layout: lane (grp, row)
 //    holds head `row`'s logits of keys 4 grp + r;
 //  * P.V on the vector units: lane = output dimension, the tile's V rows read
-//    from LDS, probabilities broadcast from LDS.
+//    from LDS, probabilities broadcast from LDS (stored key-major, so a key's
+//    G probabilities are one or two 16-byte reads).
 // The waves' (max, sum, partial output) are merged at the end.
 // Paged caches: lane l holds the page of key l of the wave's next tile, read
 // (a plain load into a register) while the current tile is computed.
@@ -198,9 +199,10 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
     constexpr int DPL = D / kWave;             // output dims per lane
     constexpr float kLog2e = 1.4426950408889634f;
     static_assert(G <= 16 && NU >= 1, "one 16-column B fragment holds the group");
+    static_assert(DPL == 1 || DPL == 2, "one or two output dims per lane");
     __shared__ uint4 kt[NW][TK * CPR];
     __shared__ uint4 vt[NW][TK * CPR];
-    __shared__ float pt[NW][G][TK];
+    __shared__ __align__(16) float pt[NW][TK][G];   // probabilities, key-major: one key's G values together
     __shared__ float alph[NW][G];
     __shared__ float wm[NW][G], wl[NW][G];
 
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const float p = __builtin_amdgcn_exp2f(x[u][r] - mn);
                 ts += p;
-                if (row < G) pt[w][row][16 * u + 4 * grp + r] = p;
+                if (row < G) pt[w][16 * u + 4 * grp + r][row] = p;
             }
         ts += __shfl_xor(ts, 16, kWave);
         ts += __shfl_xor(ts, 32, kWave);
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
         m = mn;
         if (row < G && grp == 0) alph[w][row] = alpha;
         __builtin_amdgcn_wave_barrier();
-        // P.V: lane = output dims lane + 64 dd
+        // P.V: lane owns the DPL adjacent output dims DPL * lane + d
         const uint4* vr = &vt[w][0];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -314,18 +316,32 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
 #pragma unroll 4
         for (int k = 0; k < TK; ++k) {
             float v[DPL];
+            {
+                const int dim = DPL * lane;                // the lane's dims share one 16-byte chunk
+                const uint8_t* cp = reinterpret_cast<const uint8_t*>(vr + k * CPR + ((dim >> 3) ^ (k % CPR)));
+                if constexpr (DPL == 2) {
+                    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(cp + 2 * (dim & 7));
+                    v[0] = bf16_lo(w2);
+                    v[1] = bf16_hi(w2);
+                } else {
+                    v[0] = bf16_lo((uint32_t)*reinterpret_cast<const uint16_t*>(cp + 2 * (dim & 7)));
+                }
+            }
+            float pk[G];                                   // key k's probabilities (16-byte broadcast reads)
+            if constexpr (G % 4 == 0) {
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) {
-                const int dim = lane + d * kWave;
-                const uint16_t* rp = reinterpret_cast<const uint16_t*>(vr + k * CPR + ((dim >> 3) ^ (k % CPR)));
-                v[d] = bf16_lo((uint32_t)rp[dim & 7]);
+                for (int g = 0; g < G; g += 4) {
+                    const float4 q4 = *reinterpret_cast<const float4*>(&pt[w][k][g]);
+                    pk[g] = q4.x; pk[g + 1] = q4.y; pk[g + 2] = q4.z; pk[g + 3] = q4.w;
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < G; ++g) pk[g] = pt[w][k][g];
             }
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float p = pt[w][g][k];
+            for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(p, v[d], o[g][d]);
-            }
+                for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(pk[g], v[d], o[g][d]);
         }
         __builtin_amdgcn_wave_barrier();                   // the tile buffers are free again
         if (t + NW < nt) issue(t + NW);
@@ -342,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) wo[(w * G + g) * D + lane + d * kWave] = o[g][d];
+        for (int d = 0; d < DPL; ++d) wo[(w * G + g) * D + DPL * lane + d] = o[g][d];
     __syncthreads();
     float* out = a.out + (((int64_t)l * a.shape.n_seq + b) * a.n_q_heads + (int64_t)h * G) * D;
     for (int i = tid; i < G * D; i += NW * 64) {
