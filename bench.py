@@ -423,18 +423,20 @@ def main():
     es = 2 if cfg.dtype == torch.bfloat16 else 4
     b_score, b_gather = algorithmic_bytes(n_keys, cfg.n_seg, n_kept, cfg.head_dim, es)
     kernels = {}
-    for name, bytes_per_launch in (("score", b_score), ("select_gather", b_gather)):
+    # select_gather: the fused select + compaction; below 256 segments the pass
+    # runs select, then a separate many-workgroup gather, timed as such
+    for name, bytes_per_launch in (("score", b_score), ("select_gather", b_gather), ("gather", b_gather)):
         launches, total = kt.get(name, (0, 0.0))
         if launches:
             avg = total / launches
             kernels[name] = {"avg_ms": round(avg, 4), "launches": launches,
                              "algorithmic_bytes": bytes_per_launch,
                              "achieved_GBs": round(bytes_per_launch / (avg * 1e-3) / 1e9, 1)}
-    for name in ("phase", "sample", "score_fallback", "select_fallback"):
+    for name in ("phase", "sample", "select", "score_fallback", "select_fallback"):
         launches, total = kt.get(name, (0, 0.0))
         if launches:
             kernels[name] = {"avg_ms": round(total / launches, 4), "launches": launches}
-    dom = max(("score", "select_gather"), key=lambda k: kernels.get(k, {}).get("avg_ms", 0.0))
+    dom = max(("score", "select_gather", "gather"), key=lambda k: kernels.get(k, {}).get("avg_ms", 0.0))
     achieved = kernels[dom]["achieved_GBs"]
     traffic = read_traffic(dom, args.workload)
     pass_gbs = (b_score + b_gather) / (ms * 1e-3) / 1e9

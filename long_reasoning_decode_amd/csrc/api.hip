@@ -158,9 +158,17 @@ int pick_chunk(int64_t n_seg, int64_t cap) {
 // Workspace layout.  The fallback counter of the last pruning pass sits at
 // offset 0 so tri_prune_fallbacks can find it without the cache shape.
 struct WsPlan {
-    size_t fb_count, fb_list, ctab, stats, thr, masks, s_int, total;
+    size_t fb_count, fb_list, ctab, stats, thr, masks, s_int, idx, total;
     int64_t mask_stride;
 };
+
+// Fewer segments than CUs: one select+gather workgroup per segment would copy
+// each segment's kept rows with one workgroup while most of the chip idles.
+// The pruning pass then has the select kernels write the kept slots to the
+// workspace, and the unfused gather copies them with B/64 workgroups per
+// segment.
+constexpr int64_t kSplitGatherSegs = 256;
+bool split_gather(const tri_cache_desc* kv) { return n_segments(kv) < kSplitGatherSegs; }
 
 WsPlan plan_workspace(const tri_calib_s* c, const tri_cache_desc* kv) {
     const int64_t n_seg = n_segments(kv);
@@ -174,7 +182,9 @@ WsPlan plan_workspace(const tri_calib_s* c, const tri_cache_desc* kv) {
     p.thr = p.stats + align256((size_t)n_seg * max_chunks * c->G * sizeof(double2));
     p.masks = p.thr + align256((size_t)n_seg * c->G * sizeof(float));
     p.s_int = p.masks + align256((size_t)n_seg * p.mask_stride * c->G * sizeof(uint32_t));
-    p.total = p.s_int + align256((size_t)n_seg * kv->capacity * c->G * sizeof(float));
+    p.idx = p.s_int + align256((size_t)n_seg * kv->capacity * c->G * sizeof(float));
+    const int64_t idx_len = kv->capacity < kMaxBudget ? kv->capacity : kMaxBudget;   // budget <= both
+    p.total = p.idx + (split_gather(kv) ? align256((size_t)n_seg * idx_len * sizeof(int32_t)) : 0);
     return p;
 }
 
@@ -531,12 +541,38 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     a.lengths = src->lengths;
     a.budget = budget;
     a.n_kept = n_kept;
-    a.gather = in_place ? GATHER_IN_PLACE : GATHER_COPY;
+    const bool split = !in_place && split_gather(src);
+    a.gather = in_place ? GATHER_IN_PLACE : split ? GATHER_NONE : GATHER_COPY;
     a.src = view_of(src);
     a.dst = out_of(dst);
     a.row_bytes = src->head_dim * elem_size(src->dtype);
     a.n_seg = (int)n_segments(src);
-    if (!cand) return hip_status(launch_select(a, calib->G, SELECT_S, src->capacity, st), "select+gather kernel");
+    // split: kept-slot rows min(budget, capacity) apart (a segment keeps at most that many)
+    const int64_t idx_stride = budget < src->capacity ? budget : src->capacity;
+    if (split) {
+        a.idx_out = reinterpret_cast<int32_t*>(w + p.idx);
+        a.idx_stride = idx_stride;
+    }
+    // split: every select kernel has written its segments' kept slots; copy them
+    auto gather_split = [&]() -> int {
+        if (!split) return TRI_OK;
+        GatherArgs ga;
+        ga.src = a.src;
+        ga.dst = a.dst;
+        ga.idx = a.idx_out;
+        ga.idx_stride = idx_stride;
+        ga.n_kept = n_kept;
+        ga.row_bytes = a.row_bytes;
+        ga.rows_per_block = 64;
+        ga.blocks_per_seg = (budget + 63) / 64;
+        ga.n_seg = a.n_seg;
+        return hip_status(launch_gather(ga, st), "gather kernel");
+    };
+    if (!cand) {
+        if ((rc = hip_status(launch_select(a, calib->G, SELECT_S, src->capacity, st), "select+gather kernel")))
+            return rc;
+        return gather_split();
+    }
     a.thr = reinterpret_cast<const float*>(w + p.thr);
     a.masks = reinterpret_cast<const uint32_t*>(w + p.masks);
     a.mask_stride = p.mask_stride;
@@ -562,7 +598,9 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     sa.n_seg = a.n_seg;
     if ((rc = hip_status(launch_score(sa, calib->D, calib->G, true, SCORE_FALLBACK, st), "fallback score kernel")))
         return rc;
-    return hip_status(launch_select(a, calib->G, SELECT_S_FALLBACK, src->capacity, st), "fallback select kernel");
+    if ((rc = hip_status(launch_select(a, calib->G, SELECT_S_FALLBACK, src->capacity, st), "fallback select kernel")))
+        return rc;
+    return gather_split();
 }
 
 int tri_prune_fallbacks(const void* ws, size_t ws_bytes, int32_t* count, tri_stream_t stream) {
