@@ -416,3 +416,22 @@ def test_paged_decode_attention_over_pruned_pages(gpu_lib):
         got = out[0, b, hs].cpu().numpy()
         err = np.abs(got - ref) / np.maximum(np.abs(ref), np.abs(ref).max(axis=1, keepdims=True))
         assert err.max() <= 1e-4, f"paged attention seg {s} (kept {kept[s]}): {err.max():.2e}"
+
+
+def test_many_segments_mixed_lengths(gpu_lib):
+    """At least 256 segments, so the fused pass copies inside the select kernel
+    (fewer segments go through the separate gather), with lengths from 0 to the
+    capacity: copy-through below the budget, pruning above it."""
+    T = gpu_lib
+    B, cap = 200, 600
+    cfg = W.CONFIGS["tiny"].replace(head_dim=64, group=4, dtype=torch.bfloat16, theta=1e4, n_kv_heads=8, n_seq=36,
+                                    n_keys=cap, t=cap + 2, budget=B, sigma=None, seed=31)
+    assert cfg.n_seg >= 256
+    log(f"case many segments: {cfg.n_seg} segments, N in [0, {cap}], B={B}")
+    cpu = W.dense_cache(cfg, "cpu")
+    gl = torch.Generator().manual_seed(31)
+    cpu["lengths"] = torch.randint(0, cap + 1, (cfg.n_seg,), generator=gl, dtype=torch.int32)
+    cpu["lengths"][:4] = torch.tensor([0, 1, B, B + 1], dtype=torch.int32)
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
+    _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), "many segments")
