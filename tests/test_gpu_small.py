@@ -435,3 +435,52 @@ def test_many_segments_mixed_lengths(gpu_lib):
     calib, cal = calib_for(T, cfg)
     r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
     _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), "many segments")
+
+
+@pytest.mark.parametrize("d,G,dtype,paged", [
+    (64, 1, torch.bfloat16, False), (64, 8, torch.bfloat16, True), (128, 8, torch.bfloat16, False),
+    (128, 2, torch.bfloat16, True), (64, 2, torch.float32, False), (128, 4, torch.float32, True),
+    (64, 8, torch.float32, False), (128, 1, torch.bfloat16, False)])
+def test_decode_attention_shapes(gpu_lib, d, G, dtype, paged):
+    """Decode attention for every head size, group size and storage type, dense
+    and paged (16-token pages, random page table), at lengths that end inside a
+    tile, against the oracle."""
+    import math
+    T = gpu_lib
+    n_seq, hkv, ps = 2, 3, 16
+    n_seg, hq = n_seq * hkv, hkv * G
+    lengths = [1, 17, 33, 100, 511, 1000]
+    cap = 1008
+    gen = torch.Generator().manual_seed(41 + d + G)
+    K = torch.randn((n_seg, cap, d), generator=gen).to(dtype)
+    V = torch.randn((n_seg, cap, d), generator=gen).to(dtype)
+    q = torch.randn((1, n_seq, hq, d), generator=gen).to(dtype)
+    ln = torch.tensor(lengths, dtype=torch.int32)
+    log(f"case attention d={d} G={G} {dtype} paged={paged}")
+    if paged:
+        mp = cap // ps
+        perm = torch.randperm(n_seg * mp, generator=gen).to(torch.int32).view(n_seg, mp)
+        pool_k = torch.empty((n_seg * mp, ps, d), dtype=dtype)
+        pool_v = torch.empty_like(pool_k)
+        pool_k[perm.reshape(-1).long()] = K.view(n_seg * mp, ps, d)
+        pool_v[perm.reshape(-1).long()] = V.view(n_seg * mp, ps, d)
+        pos = torch.zeros((n_seg * mp, ps), dtype=torch.int32)
+        desc = T.cache_desc(pool_k.cuda(), pool_v.cuda(), pos.cuda(), ln.cuda(), n_layers=1, n_seq=n_seq,
+                            n_kv_heads=hkv, page_table=perm.cuda(), page_size=ps, max_pages=mp)
+        keep = (pool_k, pool_v, pos, perm)
+    else:
+        pos = torch.zeros((n_seg, cap), dtype=torch.int32)
+        desc = T.cache_desc(K.cuda(), V.cuda(), pos.cuda(), ln.cuda(), n_layers=1, n_seq=n_seq, n_kv_heads=hkv)
+        keep = None
+    out = torch.full(q.shape, float("nan"), device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    T.tri_decode_attn(desc, hq, q.cuda(), scale, out)
+    torch.cuda.synchronize()
+    for s in range(n_seg):
+        N = lengths[s]
+        b, h = s // hkv, s % hkv
+        hs = slice(h * G, (h + 1) * G)
+        ref = oracle.decode_attn(stored(q[0, b, hs]), stored(K[s, :N]), stored(V[s, :N]), scale)
+        got = out[0, b, hs].cpu().numpy()
+        err = np.abs(got - ref) / np.maximum(np.abs(ref), np.abs(ref).max(axis=1, keepdims=True))
+        assert err.max() <= 1e-4, f"attention d={d} G={G} {dtype} paged={paged} seg {s} N={N}: {err.max():.2e}"
