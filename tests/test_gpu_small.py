@@ -484,3 +484,43 @@ def test_decode_attention_shapes(gpu_lib, d, G, dtype, paged):
         got = out[0, b, hs].cpu().numpy()
         err = np.abs(got - ref) / np.maximum(np.abs(ref), np.abs(ref).max(axis=1, keepdims=True))
         assert err.max() <= 1e-4, f"attention d={d} G={G} {dtype} paged={paged} seg {s} N={N}: {err.max():.2e}"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_append_rows_and_full_segments(gpu_lib, dtype):
+    """tri_append writes row lengths[s] of each segment (K, V bit-exact, the
+    sequence's position) and grows the length; a full segment is unchanged."""
+    T = gpu_lib
+    n_seq, hkv, d, cap = 2, 3, 64, 40
+    n_seg = n_seq * hkv
+    gen = torch.Generator().manual_seed(43)
+    K = torch.randn((n_seg, cap, d), generator=gen).to(dtype)
+    V = torch.randn((n_seg, cap, d), generator=gen).to(dtype)
+    pos = torch.randint(0, 1000, (n_seg, cap), generator=gen, dtype=torch.int32)
+    ln = torch.tensor([0, 5, cap - 1, cap, 17, 39], dtype=torch.int32)
+    kn = torch.randn((n_seg, d), generator=gen).to(dtype)
+    vn = torch.randn((n_seg, d), generator=gen).to(dtype)
+    pn = torch.tensor([7001, 7002], dtype=torch.int32)
+    g = {"k": K.cuda(), "v": V.cuda(), "pos": pos.cuda(), "lengths": ln.cuda()}
+    desc = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=1, n_seq=n_seq, n_kv_heads=hkv)
+    T.tri_append(desc, kn.cuda(), vn.cuda(), pn.cuda())
+    torch.cuda.synchronize()
+    Ka, Va, Pa, La = g["k"].cpu(), g["v"].cpu(), g["pos"].cpu(), g["lengths"].cpu()
+    for s in range(n_seg):
+        N = int(ln[s])
+        if N >= cap:
+            assert int(La[s]) == cap
+            assert torch.equal(Ka[s], K[s]) and torch.equal(Va[s], V[s]) and torch.equal(Pa[s], pos[s]), f"seg {s}"
+            continue
+        assert int(La[s]) == N + 1, f"seg {s}"
+        assert torch.equal(stored_t(Ka[s, N]), stored_t(kn[s])) and torch.equal(stored_t(Va[s, N]), stored_t(vn[s]))
+        assert int(Pa[s, N]) == int(pn[s // hkv])
+        other = torch.ones(cap, dtype=torch.bool)
+        other[N] = False                                       # every other row untouched
+        assert torch.equal(Ka[s][other], K[s][other]) and torch.equal(Va[s][other], V[s][other])
+        assert torch.equal(Pa[s][other], pos[s][other])
+
+
+def stored_t(x):
+    """Bit pattern of a row (bf16 or fp32) as an integer tensor, for exact compares."""
+    return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
