@@ -87,6 +87,27 @@ def cpu_baseline(W, cfg, g, cal, B, n_sample):
                       f"layers/sequences/heads; {dt:.1f} s wall on {threads} threads"}
 
 
+def copy_bandwidth(mib=4096, reps=5):
+    """Read + write bytes per second of a plain device-to-device copy."""
+    import torch
+    n = mib * 1024 * 1024
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
 def copy_probe(mib):
     """Plain device-to-device copies of a known size, for scaling counters."""
     import torch
@@ -347,6 +368,10 @@ def main():
     ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l", "gptoss", "calib", "ragged"],
                     help="qwen36l (default): the pruning pass; gptoss: decode-loop windows; "
                          "calib: offline calibration from query samples; ragged: paged batch prune + attention")
+    ap.add_argument("--unfused-steps", type=int, default=3,
+                    help="qwen workloads: also time the unfused tri_score -> tri_select_topb -> tri_compact chain")
+    ap.add_argument("--copy-ref", type=int, default=1,
+                    help="qwen workloads: measure a 4 GiB device copy as a reference bandwidth (0: skip)")
     ap.add_argument("--out-of-place", action="store_true",
                     help="gptoss: prune into a second cache instead of in place")
     ap.add_argument("--cpu-sample", type=int, default=16, help="oracle segments for the CPU baseline (0: skip)")
@@ -418,6 +443,35 @@ def main():
     fallbacks = T.tri_prune_fallbacks(ws)
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
+    # the unfused chain on the same cache (tri_score -> tri_select_topb -> tri_compact), after the timed region
+    unfused = None
+    if args.unfused_steps > 0:
+        agg = torch.empty((cfg.n_seg, cfg.n_keys), dtype=torch.float32, device="cuda")
+        idx = torch.empty((cfg.n_seg, B), dtype=torch.int32, device="cuda")
+        nk2 = torch.empty((cfg.n_seg,), dtype=torch.int32, device="cuda")
+
+        def chain():
+            T.tri_score(calib, src, g["t"], agg, ws, stream=stream)
+            T.tri_select_topb(agg, g["lengths"], B, idx, nk2, stream=stream)
+            T.tri_compact(src, idx, nk2, B, dst, stream=stream)
+        chain()
+        torch.cuda.synchronize()
+        T.tri_timing_reset()
+        T.tri_timing_enable(True)
+        u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        u0.record(stream)
+        for _ in range(args.unfused_steps):
+            chain()
+        u1.record(stream)
+        torch.cuda.synchronize()
+        T.tri_timing_enable(False)
+        ukt = T.tri_timing_read()
+        unfused = {"ms_per_step": round(u0.elapsed_time(u1) / args.unfused_steps, 4), "steps": args.unfused_steps,
+                   "kernels": {k: round(v[1] / v[0], 4) for k, v in ukt.items() if v[0]}}
+        del agg, idx, nk2
+        torch.cuda.empty_cache()
+    copy_gbs = copy_bandwidth() if args.copy_ref else None
+
     n_keys = cfg.n_seg * cfg.n_keys
     n_kept = int(out["lengths"].long().sum())
     es = 2 if cfg.dtype == torch.bfloat16 else 4
@@ -460,11 +514,14 @@ def main():
             "kv_dtype": "bf16" if es == 2 else "f32", "keys_per_step": n_keys, "kept_per_step": n_kept,
         },
         "pass_hbm": {"algorithmic_bytes": b_score + b_gather, "achieved_GBs": round(pass_gbs, 1),
-                     "frac_of_peak": round(pass_gbs / HBM_PEAK_GBS, 4)},
+                     "frac_of_peak": round(pass_gbs / HBM_PEAK_GBS, 4),
+                     "device_copy_GBs": round(copy_gbs, 1) if copy_gbs else None,
+                     "frac_of_device_copy": round(pass_gbs / copy_gbs, 4) if copy_gbs else None},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernels": kernels,
         "fallback_segments": fallbacks,
+        "unfused_chain": unfused,
     }
     if args.cpu_sample > 0:
         result["cpu_baseline"] = cpu_baseline(W, cfg, g, cal, B, args.cpu_sample)
