@@ -175,20 +175,21 @@ __global__ __launch_bounds__(256) void k_decode_attn(AttnArgs a) {
 // tiles w, w+NW, ... (TK keys each: 32 for head_dim 64, 16 for 128, so a K or
 // V tile is 4 KB).  A tile comes in through LDS DMA, whole rows per
 // instruction, rows chunk-swizzled (16-byte chunk lc of tile key k at
-// lc ^ (k mod CPR)).  Each wave keeps one tile in flight and computes only
-// once it has landed: the compiler makes every LDS read wait for all LDS DMA
-// still in flight, so a per-wave second buffer would not overlap anything;
-// the overlap comes from the waves of the other workgroups on the CU.
+// lc ^ (k mod CPR)).  The compiler makes every LDS access wait for all LDS
+// DMA in flight, so a wave reads its whole tile into registers as soon as it
+// lands, refills the buffer with its next tile, and then computes from
+// registers only: one tile in flight per wave during all of its compute.
 //  * logits q.K^T on the matrix cores: A = 16 key rows, B = the G query
 //    vectors as columns (bf16, so the products are exact; fp32 accumulation);
 //  * online softmax per head (base 2) on the fragment layout: lane (grp, row)
 //    holds head `row`'s logits of keys 4 grp + r;
-//  * P.V on the vector units: lane = output dimension, the tile's V rows read
-//    from LDS, probabilities broadcast from LDS (stored key-major, so a key's
-//    G probabilities are one or two 16-byte reads).
+//  * P.V on the vector units: lane = output dimension(s); the lane's V values
+//    are copied from LDS to registers right after the tile lands, and each
+//    key's probabilities are broadcast from the lanes that computed them
+//    (readlane), so the compute touches no LDS while the next tile loads.
 // The waves' (max, sum, partial output) are merged at the end.
-// Paged caches: lane l holds the page of key l of the wave's next tile, read
-// (a plain load into a register) while the current tile is computed.
+// Paged caches: lane l holds the page of key l of the tile the wave issues
+// next, loaded (a plain load into a register) one compute phase ahead.
 template <int D, int G, bool PAGED, int NW>
 __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
     constexpr int ROWB = D * 2, CPR = ROWB / 16;
@@ -202,9 +203,6 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
     static_assert(DPL == 1 || DPL == 2, "one or two output dims per lane");
     __shared__ uint4 kt[NW][TK * CPR];
     __shared__ uint4 vt[NW][TK * CPR];
-    __shared__ __align__(16) float pt[NW][TK][G];   // probabilities, key-major: one key's G values together
-    __shared__ float alph[NW][G];
-    __shared__ float wm[NW][G], wl[NW][G];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
     const int row = lane & 15, grp = lane >> 4;
@@ -240,6 +238,7 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
     if (w < nt) {
         fetch_pages(w);
         issue(w);
+        if (w + NW < nt) fetch_pages(w + NW);              // arrives while tile w is awaited and computed
     }
 
     // B fragments: column row = head row (zero past G), k-slot (grp, e)
@@ -258,21 +257,51 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int d = 0; d < DPL; ++d) o[g][d] = 0.0f;
 
+    constexpr int VW = TK * DPL / 2;                       // 32-bit words of the lane's V values per tile
     for (int t = w; t < nt; t += NW) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);              // this tile has landed
         __builtin_amdgcn_wave_barrier();
-        if (t + NW < nt) fetch_pages(t + NW);              // completes under this tile's compute
+        // Everything the tile needs from LDS goes to registers first: the K
+        // fragments and this lane's V values (key pairs packed at head_dim 64,
+        // a dim pair per key at 128).  The buffers are then refilled with the
+        // next tile while this one is computed, and the compute touches no LDS
+        // (the probabilities and rescale factors are broadcast with readlane).
         const uint4* kr = &kt[w][0];
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(&vt[w][0]);
+        uint4 af[NU][TS];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int st = 0; st < TS; ++st) {
+                const int kl = 16 * u + row;
+                af[u][st] = kr[kl * CPR + ((4 * st + grp) ^ (kl % CPR))];
+            }
+        uint32_t vw[VW];
+        {
+            const int dim = DPL * lane;                    // the lane's dims share one 16-byte chunk
+#pragma unroll
+            for (int k = 0; k < TK; ++k) {
+                const uint8_t* cp = vb + 16 * (k * CPR + ((dim >> 3) ^ (k % CPR))) + 2 * (dim & 7);
+                if constexpr (DPL == 2) {
+                    vw[k] = *reinterpret_cast<const uint32_t*>(cp);
+                } else {
+                    const uint32_t h = *reinterpret_cast<const uint16_t*>(cp);
+                    if (k & 1) vw[k >> 1] |= h << 16;
+                    else vw[k >> 1] = h;
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);            // the reads are done: the buffers may be refilled
+        __builtin_amdgcn_wave_barrier();
+        if (t + NW < nt) issue(t + NW);
+        if (t + 2 * NW < nt) fetch_pages(t + 2 * NW);      // the tile after next: arrives under this compute
         float x[NU][4];
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int kl = 16 * u + row;
             f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int st = 0; st < TS; ++st) {
-                const uint4 av = kr[kl * CPR + ((4 * st + grp) ^ (kl % CPR))];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), bq[st], acc, 0, 0, 0);
-            }
+            for (int st = 0; st < TS; ++st)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[u][st]), bq[st], acc, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = t * TK + 16 * u + 4 * grp + r;
@@ -295,61 +324,50 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
         for (int u = 0; u < NU; ++u)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = __builtin_amdgcn_exp2f(x[u][r] - mn);
-                ts += p;
-                if (row < G) pt[w][16 * u + 4 * grp + r][row] = p;
+                x[u][r] = __builtin_amdgcn_exp2f(x[u][r] - mn);   // probability, head `row`, key 16u + 4grp + r
+                ts += x[u][r];
             }
         ts += __shfl_xor(ts, 16, kWave);
         ts += __shfl_xor(ts, 32, kWave);
         lsum = lsum * alpha + ts;
         m = mn;
-        if (row < G && grp == 0) alph[w][row] = alpha;
-        __builtin_amdgcn_wave_barrier();
-        // P.V: lane owns the DPL adjacent output dims DPL * lane + d
-        const uint4* vr = &vt[w][0];
+        // P.V: lane owns the DPL adjacent output dims DPL * lane + d; head g's
+        // probability of key 16u + 4q + r sits in lane 16q + g, register x[u][r]
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float al = alph[w][g];
+            const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), g));
 #pragma unroll
             for (int d = 0; d < DPL; ++d) o[g][d] *= al;
         }
-#pragma unroll 4
-        for (int k = 0; k < TK; ++k) {
-            float v[DPL];
-            {
-                const int dim = DPL * lane;                // the lane's dims share one 16-byte chunk
-                const uint8_t* cp = reinterpret_cast<const uint8_t*>(vr + k * CPR + ((dim >> 3) ^ (k % CPR)));
-                if constexpr (DPL == 2) {
-                    const uint32_t w2 = *reinterpret_cast<const uint32_t*>(cp + 2 * (dim & 7));
-                    v[0] = bf16_lo(w2);
-                    v[1] = bf16_hi(w2);
-                } else {
-                    v[0] = bf16_lo((uint32_t)*reinterpret_cast<const uint16_t*>(cp + 2 * (dim & 7)));
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int k = 16 * u + 4 * q + r;
+                    float v[DPL];
+                    if constexpr (DPL == 2) {
+                        v[0] = bf16_lo(vw[k]);
+                        v[1] = bf16_hi(vw[k]);
+                    } else {
+                        v[0] = (k & 1) ? bf16_hi(vw[k >> 1]) : bf16_lo(vw[k >> 1]);
+                    }
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[u][r]), 16 * q + g));
+#pragma unroll
+                        for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(p, v[d], o[g][d]);
+                    }
                 }
-            }
-            float pk[G];                                   // key k's probabilities (16-byte broadcast reads)
-            if constexpr (G % 4 == 0) {
-#pragma unroll
-                for (int g = 0; g < G; g += 4) {
-                    const float4 q4 = *reinterpret_cast<const float4*>(&pt[w][k][g]);
-                    pk[g] = q4.x; pk[g + 1] = q4.y; pk[g + 2] = q4.z; pk[g + 3] = q4.w;
-                }
-            } else {
-#pragma unroll
-                for (int g = 0; g < G; ++g) pk[g] = pt[w][k][g];
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(pk[g], v[d], o[g][d]);
-        }
-        __builtin_amdgcn_wave_barrier();                   // the tile buffers are free again
-        if (t + NW < nt) issue(t + NW);
     }
 
-    // merge the waves (their tile buffers hold the partial outputs)
+    // merge the waves (their tile buffers hold the partial outputs, maxima and sums)
     __syncthreads();
     float* wo = reinterpret_cast<float*>(&kt[0][0]);      // [NW][G][D]
+    float (*wm)[G] = reinterpret_cast<float (*)[G]>(&vt[0][0]);
+    float (*wl)[G] = wm + NW;
+    static_assert(sizeof(vt) >= sizeof(float) * 2 * NW * G, "maxima and sums fit the V tiles");
     static_assert(sizeof(kt) >= sizeof(float) * NW * G * D, "partial outputs fit the K tiles");
     if (grp == 0 && row < G) {
         wm[w][row] = m;
