@@ -365,7 +365,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l", "gptoss", "calib", "ragged"],
+    ap.add_argument("--workload", default="qwen36l", choices=["qwen36l", "qwen1l", "tiny", "gptoss", "calib", "ragged"],
                     help="qwen36l (default): the pruning pass; gptoss: decode-loop windows; "
                          "calib: offline calibration from query samples; ragged: paged batch prune + attention")
     ap.add_argument("--unfused-steps", type=int, default=3,

@@ -206,8 +206,10 @@ int hip_status(hipError_t e, const char* step = "launch") {
 // and the score kernel writes candidate lists and masks instead of every score.
 int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const int32_t* t, float* s_raw,
                         float* s_int, double2* stats, float* ctab, int chunk, hipStream_t st,
-                        const WsPlan* cand = nullptr, char* ws = nullptr, int budget = 0) {
+                        const WsPlan* cand = nullptr, char* ws = nullptr, int budget = 0,
+                        int32_t* fb_reset = nullptr) {
     PhaseArgs pa;
+    pa.fb_reset = fb_reset;
     pa.P = c->P;
     pa.omega = c->omega;
     pa.t = t;
@@ -532,8 +534,9 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     // at once when none did).  Otherwise (fp32, or capacity below what
     // candidate mode needs): the full path.
     const bool cand = src->dtype == TRI_DTYPE_BF16 && candidate_mode(src->capacity, budget);
+    // (without candidate mode nothing falls back: the phase kernel zeroes the count tri_prune_fallbacks reads)
     if ((rc = run_phase_and_score(calib, src, t, nullptr, s_int, stats, ctab, chunk, st, cand ? &p : nullptr, w,
-                                  budget)))
+                                  budget, cand ? nullptr : reinterpret_cast<int32_t*>(w + p.fb_count))))
         return rc;
     SelectArgs a;
     memset(&a, 0, sizeof a);

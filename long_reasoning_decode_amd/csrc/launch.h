@@ -63,6 +63,7 @@ struct PhaseArgs {
     const double* omega;    // [F]
     const int32_t* t;       // [n_seq]
     float* ctab;            // [n_layers][n_seq][Hq][D]
+    int32_t* fb_reset;      // optional: a pruning pass without candidate mode zeroes its fallback count
     int32_t layer0, n_layers, n_seq, n_q_heads, head_dim;
 };
 hipError_t launch_phase(const PhaseArgs& a, hipStream_t stream);

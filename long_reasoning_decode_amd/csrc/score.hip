@@ -21,6 +21,7 @@ __global__ __launch_bounds__(256) void k_phase(PhaseArgs a) {
     const int F = a.head_dim / 2;
     const int64_t total = (int64_t)a.n_layers * a.n_seq * F;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0 && a.fb_reset) *a.fb_reset = 0;
     if (i >= total) return;
     const int f = (int)(i % F);
     const int b = (int)((i / F) % a.n_seq);

@@ -524,3 +524,19 @@ def test_append_rows_and_full_segments(gpu_lib, dtype):
 def stored_t(x):
     """Bit pattern of a row (bf16 or fp32) as an integer tensor, for exact compares."""
     return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+
+
+def test_fallback_count_zero_without_candidate_mode(gpu_lib):
+    """A pass that never enters candidate mode (fp32 here) reports zero
+    fallbacks even on a workspace holding stale bytes."""
+    T = gpu_lib
+    cfg = W.CONFIGS["tiny"]
+    g = _to(W.dense_cache(cfg, "cpu"), "cuda")
+    calib, _ = calib_for(T, cfg)
+    desc = dense_desc(T, cfg, g)
+    out = empty_like_dense(g, cfg.budget)
+    nk = torch.zeros_like(g["lengths"])
+    ws = T.workspace(calib, desc, cfg.budget)
+    ws.fill_(0x5A)
+    T.tri_prune_window(calib, desc, g["t"], cfg.budget, dense_desc(T, cfg, out), nk, ws)
+    assert T.tri_prune_fallbacks(ws) == 0
