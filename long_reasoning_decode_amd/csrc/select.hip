@@ -75,46 +75,80 @@ __device__ __forceinline__ int nth_bit(uint32_t m, int q) {
 // Two block scans give, per block, the slot-order rank of its first candidate
 // key (pre, from the union of its words) and, in the order of the wave lists,
 // the running float count (lpos) from which its offset inside its list follows.
+// The mask words are staged in LDS (hwl) as they are read, so each candidate
+// then needs one global load (its scores), not two.
 // A key's entry is A' = the largest z-score over its listed heads.
-template <int J, int G>
+// NB: the blocks the per-block LDS arrays hold (>= nbk; a multiple of 64, so a
+// chunk's wave-list positions stay inside them).
+template <int J, int G, int NB>
 __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s, const int N, const ZParams<G>& z,
                                                uint32_t (&key)[J], uint32_t* pre, uint32_t* lpos, uint32_t* mw,
-                                               uint32_t* wsum, uint32_t* bcast) {
+                                               uint32_t* hwl, uint32_t* wsum, uint32_t* bcast) {
+    constexpr int BPT = NB >= kSelThreads ? NB / kSelThreads : 1;   // blocks per thread: tid * BPT + i
     const int tid = threadIdx.x;
-    const int nbk = (N + 31) / 32;                     // <= 2048 (N <= 65536)
+    const int nbk = (N + 31) / 32;                     // <= NB
     const int bpc = a.chunk / 32, q4 = bpc / 4;
     auto perm = [&](int b) {                           // block -> position in wave-list order
         const int c = b / bpc, r = b - c * bpc;
         return c * bpc + (r & 3) * q4 + (r >> 2);
     };
     const uint32_t* mp = a.masks + (int64_t)s * a.mask_stride * G;
-    const int b0 = 2 * tid, b1 = 2 * tid + 1;
-    uint32_t u0 = 0u, u1 = 0u, f0 = 0u, f1 = 0u;       // union word, float count
-    // (blocks 2 tid and 2 tid + 1: 2G consecutive words)
+    uint32_t cu[BPT], cf[BPT], ct = 0u;                // per block: candidate keys, listed floats
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const uint32_t w0 = b0 < nbk ? mp[b0 * G + g] : 0u, w1 = b1 < nbk ? mp[b1 * G + g] : 0u;
-        u0 |= w0;
-        u1 |= w1;
-        f0 += __popc(w0);
-        f1 += __popc(w1);
+    for (int i = 0; i < BPT; ++i) {
+        const int b = tid * BPT + i;
+        uint32_t u = 0u, f = 0u;
+        if (b < nbk) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const uint32_t wd = mp[b * G + g];
+                hwl[b * G + g] = wd;
+                u |= wd;
+                f += __popc(wd);
+            }
+        }
+        if (b < NB) {
+            mw[b] = u;
+            lpos[b] = 0u;
+        }
+        cu[i] = __popc(u);
+        cf[i] = f;
+        ct += cu[i];
     }
-    const uint32_t c0 = __popc(u0), c1 = __popc(u1);
-    mw[b0] = u0;
-    mw[b1] = u1;
-    lpos[b0] = 0u;
-    lpos[b1] = 0u;
-    const uint32_t inc = block_incl_scan(c0 + c1, wsum);     // (synchronises)
-    pre[b0] = inc - c0 - c1;
-    pre[b1] = inc - c1;
+    const uint32_t inc = block_incl_scan(ct, wsum);     // (synchronises)
+    {
+        uint32_t run = inc - ct;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            const int b = tid * BPT + i;
+            if (b < NB) pre[b] = run;
+            run += cu[i];
+        }
+    }
     if (tid == kSelThreads - 1) bcast[0] = inc;
-    if (b0 < nbk) lpos[perm(b0)] = f0;
-    if (b1 < nbk) lpos[perm(b1)] = f1;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const int b = tid * BPT + i;
+        if (b < nbk) lpos[perm(b)] = cf[i];
+    }
     __syncthreads();
-    const uint32_t t0 = lpos[b0], t1 = lpos[b1];
-    const uint32_t inc2 = block_incl_scan(t0 + t1, wsum);
-    lpos[b0] = inc2 - t0 - t1;
-    lpos[b1] = inc2 - t1;
+    uint32_t tv[BPT], tt = 0u;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+        const int b = tid * BPT + i;
+        tv[i] = b < NB ? lpos[b] : 0u;
+        tt += tv[i];
+    }
+    const uint32_t inc2 = block_incl_scan(tt, wsum);
+    {
+        uint32_t run = inc2 - tt;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            const int b = tid * BPT + i;
+            if (b < NB) lpos[b] = run;
+            run += tv[i];
+        }
+    }
     __syncthreads();
     const int nc = (int)bcast[0];
     if (nc > J * kSelThreads) return -1;
@@ -130,12 +164,12 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
             if constexpr (G % 4 == 0) {
 #pragma unroll
                 for (int g = 0; g < G; g += 4) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(mp + lo * G + g);
+                    const uint4 v = *reinterpret_cast<const uint4*>(hwl + lo * G + g);
                     hw[g] = v.x; hw[g + 1] = v.y; hw[g + 2] = v.z; hw[g + 3] = v.w;
                 }
             } else {
 #pragma unroll
-                for (int g = 0; g < G; ++g) hw[g] = mp[lo * G + g];
+                for (int g = 0; g < G; ++g) hw[g] = hwl[lo * G + g];
             }
             int foff = 0;
 #pragma unroll
@@ -173,7 +207,9 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
 template <int J, int G, int MODE>
 __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s) {
     constexpr bool CAND = MODE == SELECT_C;
-    constexpr int NB = CAND ? 2048 : 1;
+    // mode C holds at most J*1024 >= N/2 candidates (launch_select), so a segment
+    // has at most 64 J blocks of 32 keys (and at most 2048, N <= 65536)
+    constexpr int NB = CAND ? (64 * J < 2048 ? 64 * J : 2048) : 1;
     constexpr int GZ = G > 0 ? G : 1;
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t wsum[kSelWaves];
@@ -182,6 +218,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
     __shared__ int32_t kept[kMaxBudget];
     __shared__ double scratch[(kSelWaves + 1) * GZ];
     __shared__ uint32_t pre[NB], lpos[NB], mw[NB];
+    __shared__ __align__(16) uint32_t hwl[CAND ? NB * GZ : 1];      // mode C: the segment's mask words
     __shared__ uint32_t bcast[1];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
@@ -201,7 +238,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         if constexpr (G > 0) {
             z = merge_stats<G, kSelThreads>(a.stats + (int64_t)s * a.n_chunks * G, a.n_chunks, a.chunk, N, scratch);
             if constexpr (CAND) {
-                nv = load_candidates<J, G>(a, s, N, z, key, pre, lpos, mw, wsum, bcast);
+                nv = load_candidates<J, G, NB>(a, s, N, z, key, pre, lpos, mw, hwl, wsum, bcast);
                 if (nv < B) {                           // overflow (-1) or too few to hold the cut
                     if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1)] = s;
                     return;
