@@ -540,3 +540,44 @@ def test_fallback_count_zero_without_candidate_mode(gpu_lib):
     ws.fill_(0x5A)
     T.tri_prune_window(calib, desc, g["t"], cfg.budget, dense_desc(T, cfg, out), nk, ws)
     assert T.tri_prune_fallbacks(ws) == 0
+
+
+def test_cache_at_a_later_calibration_layer(gpu_lib):
+    """A two-layer cache whose layer 0 is calibration layer 1 of three
+    (layer0 = 1): every step of the pass, candidate mode included, must use
+    layers 1 and 2 of the calibration."""
+    T = gpu_lib
+    B, cap = 600, 12000
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, group=4, dtype=torch.bfloat16, theta=1e6, n_layers=2, n_kv_heads=2,
+                                    n_seq=2, n_keys=cap, t=cap + 3, budget=B, sigma=None, seed=47)
+    log(f"case layer0 = 1: {cfg.n_seg} segments over calibration layers 1-2")
+    cal = W.calibration(cfg.replace(n_layers=3))
+    calib = T.tri_calib_load(cal["mag"], cal["phase"], cal["conc"], cal["offsets"], n_kv_heads=cfg.n_kv_heads,
+                             rope_theta=cfg.theta)
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([cap, 9001, 4095, 700, cap, 5000, B, 8000], dtype=torch.int32)
+    g = _to(cpu, "cuda")
+    desc = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=2, n_seq=cfg.n_seq,
+                        n_kv_heads=cfg.n_kv_heads, layer0=1)
+    out = empty_like_dense(g, B)
+    nk = torch.full_like(g["lengths"], -1)
+    odesc = T.cache_desc(out["k"], out["v"], out["pos"], out["lengths"], n_layers=2, n_seq=cfg.n_seq,
+                         n_kv_heads=cfg.n_kv_heads, layer0=1)
+    ws = T.workspace(calib, desc, B)
+    T.tri_prune_window(calib, desc, g["t"], B, odesc, nk, ws)
+    agg = torch.full((cfg.n_seg, cap), float("nan"), device="cuda")
+    T.tri_score(calib, desc, g["t"], agg, ws)
+    torch.cuda.synchronize()
+    A = agg.cpu()
+    for s in range(cfg.n_seg):
+        N = int(cpu["lengths"][s])
+        tag = f"layer0=1 seg {s} N={N}"
+        K, V, P = stored(cpu["k"][s, :N]), stored(cpu["v"][s, :N]), cpu["pos"][s, :N].numpy()
+        ref = oracle_segment(cfg, cal, K, V, P, int(cpu["t"][seg_seq(cfg, s)]), s, B, layer0=1)
+        check_agg(A[s, :N].numpy(), ref["A"], tag)
+        nks = int(nk[s])
+        assert nks == min(N, B), tag
+        Pd = out["pos"][s, :nks].cpu().numpy()
+        ix = kept_slots_from_positions(P, Pd)
+        check_selection(ix, ref["A"], B, tag)
+        check_compaction(K, V, P, stored(out["k"][s, :nks].cpu()), stored(out["v"][s, :nks].cpu()), Pd, ix, tag)
