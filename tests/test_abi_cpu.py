@@ -197,3 +197,17 @@ def test_calibrate_validation():
                              ctypes.c_void_p(ws.data_ptr() + 16), ws.numel() - 16, None) == T.TRI_ERR_WORKSPACE
     if not torch.cuda.is_available():
         assert cal() == T.TRI_ERR_NO_DEVICE
+
+
+def test_append_refuses_paged_caches():
+    lib = T.load()
+    k = torch.zeros(8, 16, 64, dtype=torch.bfloat16)          # pool of 8 pages x 16 rows
+    pos = torch.zeros(8, 16, dtype=torch.int32)
+    ln = torch.zeros(4, dtype=torch.int32)
+    pt = torch.zeros(4, 2, dtype=torch.int32)
+    d = T.cache_desc(k, k.clone(), pos, ln, n_layers=1, n_seq=2, n_kv_heads=2, page_table=pt, page_size=16,
+                     max_pages=2)
+    kn = torch.zeros(4, 64, dtype=torch.bfloat16)
+    p = torch.zeros(2, dtype=torch.int32)
+    assert lib.tri_append(ctypes.byref(d), T._p(kn), T._p(kn), T._p(p), None) == T.TRI_ERR_UNSUPPORTED
+    assert lib.tri_append(ctypes.byref(d), None, T._p(kn), T._p(p), None) == T.TRI_ERR_INVALID_ARG
