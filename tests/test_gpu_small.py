@@ -437,19 +437,20 @@ def test_many_segments_mixed_lengths(gpu_lib):
     _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), "many segments")
 
 
-@pytest.mark.parametrize("d,G,dtype,paged", [
-    (64, 1, torch.bfloat16, False), (64, 8, torch.bfloat16, True), (128, 8, torch.bfloat16, False),
-    (128, 2, torch.bfloat16, True), (64, 2, torch.float32, False), (128, 4, torch.float32, True),
-    (64, 8, torch.float32, False), (128, 1, torch.bfloat16, False)])
-def test_decode_attention_shapes(gpu_lib, d, G, dtype, paged):
+@pytest.mark.parametrize("d,G,dtype,paged,n_seq", [
+    (64, 1, torch.bfloat16, False, 2), (64, 8, torch.bfloat16, True, 2), (128, 8, torch.bfloat16, False, 2),
+    (128, 2, torch.bfloat16, True, 2), (64, 2, torch.float32, False, 2), (128, 4, torch.float32, True, 2),
+    (64, 8, torch.float32, False, 2), (128, 1, torch.bfloat16, False, 2),
+    (64, 8, torch.bfloat16, False, 1), (128, 2, torch.bfloat16, True, 1)])
+def test_decode_attention_shapes(gpu_lib, d, G, dtype, paged, n_seq):
     """Decode attention for every head size, group size and storage type, dense
     and paged (16-token pages, random page table), at lengths that end inside a
-    tile, against the oracle."""
+    tile, against the oracle; n_seq = 1 gives an odd segment count."""
     import math
     T = gpu_lib
-    n_seq, hkv, ps = 2, 3, 16
+    hkv, ps = 3, 16
     n_seg, hq = n_seq * hkv, hkv * G
-    lengths = [1, 17, 33, 100, 511, 1000]
+    lengths = [1, 17, 33, 100, 511, 1000] if n_seq == 2 else [1000, 1, 511]
     cap = 1008
     gen = torch.Generator().manual_seed(41 + d + G)
     K = torch.randn((n_seg, cap, d), generator=gen).to(dtype)
