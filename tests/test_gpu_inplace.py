@@ -88,6 +88,19 @@ def test_in_place_many_moved_rows(gpu_lib):
     _dense_in_place(gpu_lib, cfg, cpu, B, "in place many moves")
 
 
+def test_in_place_maximum_sizes(gpu_lib):
+    """The largest segment and budget: 65536 keys, B = 8192 (candidate pass, up
+    to four batches of freed slots), and a 30000-key segment on the full-score
+    path."""
+    B, cap = 8192, 65536
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, group=4, dtype=torch.bfloat16, theta=1e6, n_kv_heads=1, n_seq=2,
+                                    n_keys=cap, t=cap + 1, budget=B, sigma=None, seed=33)
+    log("case in place, maximum sizes")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([cap, 30000], dtype=torch.int32)
+    _dense_in_place(gpu_lib, cfg, cpu, B, "in place maximum")
+
+
 def test_in_place_paged(gpu_lib):
     """A ragged paged pool (random page tables) pruned where it is."""
     T = gpu_lib

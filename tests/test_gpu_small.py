@@ -437,6 +437,24 @@ def test_many_segments_mixed_lengths(gpu_lib):
     _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), "many segments")
 
 
+@pytest.mark.parametrize("d,G,dtype,lengths", [
+    (128, 4, torch.bfloat16, [65536, 65535, 8193]), (64, 8, torch.float32, [65536, 8192])])
+def test_maximum_sizes(gpu_lib, d, G, dtype, lengths):
+    """The largest segment (65536 keys) and budget (8192) the library takes,
+    every step against the oracle.  bf16 at N = 8 B runs the candidate pass,
+    one key fewer the full-score path."""
+    T = gpu_lib
+    B, cap = 8192, 65536
+    cfg = W.CONFIGS["tiny"].replace(head_dim=d, group=G, dtype=dtype, theta=1e6, n_kv_heads=1, n_seq=len(lengths),
+                                    n_keys=cap, t=cap + 1, budget=B, sigma=None, seed=29)
+    log(f"case maximum sizes d={d} G={G} {dtype} lengths={lengths}")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor(lengths, dtype=torch.int32)
+    calib, cal = calib_for(T, cfg)
+    r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, B)
+    _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), f"maximum d{d}")
+
+
 @pytest.mark.parametrize("d,G,dtype,paged,n_seq", [
     (64, 1, torch.bfloat16, False, 2), (64, 8, torch.bfloat16, True, 2), (128, 8, torch.bfloat16, False, 2),
     (128, 2, torch.bfloat16, True, 2), (64, 2, torch.float32, False, 2), (128, 4, torch.float32, True, 2),
