@@ -204,7 +204,8 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
     __shared__ uint4 kt[NW][TK * CPR];
     __shared__ uint4 vt[NW][TK * CPR];
 
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform: the tile loop runs on scalar registers
     const int row = lane & 15, grp = lane >> 4;
     const int s = blockIdx.x;
     const int N = min(max(a.lengths[s], 0), (int)a.kv.capacity);

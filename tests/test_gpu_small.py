@@ -505,6 +505,38 @@ def test_decode_attention_shapes(gpu_lib, d, G, dtype, paged, n_seq):
         assert err.max() <= 1e-4, f"attention d={d} G={G} {dtype} paged={paged} seg {s} N={N}: {err.max():.2e}"
 
 
+@pytest.mark.parametrize("d,G", [(64, 8), (128, 4), (64, 2)])
+def test_decode_attention_more_segments_than_workgroups(gpu_lib, d, G):
+    """Dense bf16 caches with more segments (2560) than the GPU holds
+    workgroups at once, at ragged lengths; every segment against the oracle."""
+    T = gpu_lib
+    n_seq, hkv, cap = 320, 8, 160
+    n_seg, hq = n_seq * hkv, hkv * G
+    gen = torch.Generator().manual_seed(47 + d + G)
+    K = torch.randn((n_seg, cap, d), generator=gen).to(torch.bfloat16)
+    V = torch.randn((n_seg, cap, d), generator=gen).to(torch.bfloat16)
+    q = torch.randn((1, n_seq, hq, d), generator=gen).to(torch.bfloat16)
+    ln = torch.randint(1, cap + 1, (n_seg,), generator=gen, dtype=torch.int32)
+    ln[:6] = torch.tensor([1, cap, 2, cap - 1, 17, 64], dtype=torch.int32)
+    log(f"case attention, {n_seg} segments, d={d} G={G}")
+    pos = torch.zeros((n_seg, cap), dtype=torch.int32)
+    desc = T.cache_desc(K.cuda(), V.cuda(), pos.cuda(), ln.cuda(), n_layers=1, n_seq=n_seq, n_kv_heads=hkv)
+    out = torch.full(q.shape, float("nan"), device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    T.tri_decode_attn(desc, hq, q.cuda(), scale, out)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    qs, Ks, Vs = stored(q), stored(K), stored(V)
+    for s in range(n_seg):
+        N = int(ln[s])
+        b, h = s // hkv, s % hkv
+        hs = slice(h * G, (h + 1) * G)
+        ref = oracle.decode_attn(qs[0, b, hs], Ks[s, :N], Vs[s, :N], scale)
+        got = out[0, b, hs]
+        err = np.abs(got - ref) / np.maximum(np.abs(ref), np.abs(ref).max(axis=1, keepdims=True))
+        assert err.max() <= 1e-4, f"attention d={d} G={G} seg {s} N={N}: {err.max():.2e}"
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_append_rows_and_full_segments(gpu_lib, dtype):
     """tri_append writes row lengths[s] of each segment (K, V bit-exact, the
