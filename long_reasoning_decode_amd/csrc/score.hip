@@ -581,10 +581,19 @@ __device__ __forceinline__ void score_chunk_mfma(const ScoreArgs& a, const int s
 }
 
 // (at most 128 VGPRs for head_dim 128 with G <= 4, so four workgroups share a CU)
+// Paged pools are sized for the longest segment, so many of a ragged batch's
+// (segment, chunk) workgroups have no keys.  There the grid runs chunk-major
+// (chunk 0 of every segment first): the workgroups with keys are dispatched
+// first and the empty ones, which return at once, come last.
 template <int D, int G, bool CAND, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 1))) void k_score_mfma(ScoreArgs a) {
-    const int s = blockIdx.x / a.n_chunks;
-    score_chunk_mfma<D, G, CAND, PAGED>(a, s, blockIdx.x - s * a.n_chunks);
+    if constexpr (PAGED) {
+        const int c = blockIdx.x / a.n_seg;
+        score_chunk_mfma<D, G, CAND, PAGED>(a, blockIdx.x - c * a.n_seg, c);
+    } else {
+        const int s = blockIdx.x / a.n_chunks;
+        score_chunk_mfma<D, G, CAND, PAGED>(a, s, blockIdx.x - s * a.n_chunks);
+    }
 }
 
 // Full scoring of the segments whose candidate pass failed its certificate:
