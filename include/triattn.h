@@ -218,18 +218,34 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
                      const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,
                      tri_stream_t stream);
 /*
- * How the pass runs (the result does not depend on it): for bf16 caches,
- * segments with N >= 4096 and N >= 8 B first get per-head score thresholds
- * from a 256-key sample, and only keys reaching a threshold in some head
- * keep their scores for the select step.  The select step proves, with the
- * exact per-head statistics, that every other key ranks below the cut;
- * segments where that proof fails are scored and selected again over all of
- * their keys within the same call.  The kept set is always the one the
- * full-score path gives.
+ * How the pass runs (the result does not depend on it).  The full-score path
+ * keeps every key's G scores for the select step.  The candidate pass, for
+ * bf16 caches, first gives segments with N >= 4096 and N >= 8 B per-head
+ * score thresholds from a 256-key sample, and only keys reaching a threshold
+ * in some head keep their scores.  The select step proves, with the exact
+ * per-head statistics, that every other key ranks below the cut; segments
+ * where that proof fails are scored and selected again over all of their
+ * keys within the same call.  The kept set is always the one the full-score
+ * path gives.
+ *
+ * tri_prune_window takes TRI_PATH_AUTO: the candidate pass when the cache is
+ * bf16, its capacity allows candidate mode (>= 4096 and >= 8 B) and it has at
+ * least 256 segments.  Fewer segments cannot fill the GPU: there the sample
+ * and fallback launches cost more than the score writes the pass saves.
+ * tri_prune_window_ex takes the path as an argument: TRI_PATH_FULL, or
+ * TRI_PATH_CANDIDATES (the candidate pass whenever the cache allows it,
+ * whatever its segment count).  Any other value is TRI_ERR_INVALID_ARG.
  *
  * tri_prune_fallbacks: number of segments the last tri_prune_window on this
- * workspace had to redo in full (host int32 *count).  Synchronises `stream`.
+ * workspace had to redo in full (host int32 *count; 0 after a full-score
+ * pass).  Synchronises `stream`.
  */
+#define TRI_PATH_AUTO 0
+#define TRI_PATH_FULL 1
+#define TRI_PATH_CANDIDATES 2
+int tri_prune_window_ex(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
+                        const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes, int path,
+                        tri_stream_t stream);
 int tri_prune_fallbacks(const void* ws, size_t ws_bytes, int32_t* count, tri_stream_t stream);
 
 /*

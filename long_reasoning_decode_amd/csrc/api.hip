@@ -510,9 +510,16 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
     return hip_status(launch_gather(a, static_cast<hipStream_t>(stream)), "gather kernel");
 }
 
-int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
-                     const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,
-                     tri_stream_t stream) {
+// Segments below which the automatic path scores every key: they cannot fill
+// the GPU, and the candidate pass's sample and fallback launches then cost
+// more than the score writes it saves (one 32K-key layer, 8 segments: 0.17 ms
+// with the candidate pass, 0.13 ms without).
+constexpr int64_t kCandidateMinSegs = 256;
+
+static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
+                        const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes, int path,
+                        tri_stream_t stream) {
+    if (path != TRI_PATH_AUTO && path != TRI_PATH_FULL && path != TRI_PATH_CANDIDATES) return TRI_ERR_INVALID_ARG;
     bool in_place = false;
     int rc = check_pair(src, dst, budget, &in_place);
     if (rc) return rc;
@@ -531,9 +538,11 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     // bf16 caches that can hold a segment long enough for candidate mode:
     // candidate pass (sample -> score lists -> certified select), then the full
     // path for any segment whose certificate failed (both fallback kernels exit
-    // at once when none did).  Otherwise (fp32, or capacity below what
-    // candidate mode needs): the full path.
-    const bool cand = src->dtype == TRI_DTYPE_BF16 && candidate_mode(src->capacity, budget);
+    // at once when none did); the automatic choice also wants enough segments
+    // to fill the GPU.  Otherwise (fp32, capacity below what candidate mode
+    // needs, or the full path asked for): the full path.
+    const bool cand = src->dtype == TRI_DTYPE_BF16 && candidate_mode(src->capacity, budget) &&
+                      (path == TRI_PATH_CANDIDATES || (path == TRI_PATH_AUTO && n_segments(src) >= kCandidateMinSegs));
     // (without candidate mode nothing falls back: the phase kernel zeroes the count tri_prune_fallbacks reads)
     if ((rc = run_phase_and_score(calib, src, t, nullptr, s_int, stats, ctab, chunk, st, cand ? &p : nullptr, w,
                                   budget, cand ? nullptr : reinterpret_cast<int32_t*>(w + p.fb_count))))
@@ -608,6 +617,18 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
     if ((rc = hip_status(launch_select(a, calib->G, SELECT_S_FALLBACK, src->capacity, st), "fallback select kernel")))
         return rc;
     return gather_split();
+}
+
+int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
+                     const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,
+                     tri_stream_t stream) {
+    return prune_window(calib, src, t, budget, dst, n_kept, ws, ws_bytes, TRI_PATH_AUTO, stream);
+}
+
+int tri_prune_window_ex(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
+                        const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes, int path,
+                        tri_stream_t stream) {
+    return prune_window(calib, src, t, budget, dst, n_kept, ws, ws_bytes, path, stream);
 }
 
 int tri_prune_fallbacks(const void* ws, size_t ws_bytes, int32_t* count, tri_stream_t stream) {

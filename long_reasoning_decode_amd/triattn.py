@@ -29,12 +29,16 @@ TRI_VARIANT_TRIG_ONLY = 1
 TRI_VARIANT_NORM_ONLY = 2
 TRI_VARIANT_FIXED_WEIGHT = 4
 TRI_VARIANT_R_WEIGHTED_TRIG = 8
+TRI_PATH_AUTO = 0
+TRI_PATH_FULL = 1
+TRI_PATH_CANDIDATES = 2
 
 EXPORTS = (
     "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
     "tri_compact", "tri_prune_window", "tri_append", "tri_decode_attn", "tri_strerror",
     "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name", "tri_last_error",
     "tri_prune_fallbacks", "tri_calibrate_workspace_size", "tri_calibrate", "tri_calib_load_ex",
+    "tri_prune_window_ex",
 )
 
 
@@ -82,6 +86,7 @@ def load():
         "tri_select_topb": [P, P, I, I, I, P, P, P, SZ, P],
         "tri_compact": [DP, P, P, I, DP, P],
         "tri_prune_window": [P, DP, P, I, DP, P, P, SZ, P],
+        "tri_prune_window_ex": [P, DP, P, I, DP, P, P, SZ, I, P],
         "tri_append": [DP, P, P, P, P],
         "tri_decode_attn": [DP, I, P, F, P, P],
         "tri_strerror": [I],
@@ -220,10 +225,17 @@ def tri_compact(src, idx, n_kept, budget, dst, stream=None):
     _check("tri_compact", rc)
 
 
-def tri_prune_window(calib, src, t, budget, dst, n_kept, ws, stream=None):
-    rc = load().tri_prune_window(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
-                                 _p(n_kept), _p(ws), ws.numel(), _stream(stream))
-    _check("tri_prune_window", rc)
+def tri_prune_window(calib, src, t, budget, dst, n_kept, ws, stream=None, path=None):
+    """path None: tri_prune_window (the automatic path); else tri_prune_window_ex
+    with TRI_PATH_AUTO / TRI_PATH_FULL / TRI_PATH_CANDIDATES."""
+    if path is None:
+        rc = load().tri_prune_window(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
+                                     _p(n_kept), _p(ws), ws.numel(), _stream(stream))
+        _check("tri_prune_window", rc)
+    else:
+        rc = load().tri_prune_window_ex(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
+                                        _p(n_kept), _p(ws), ws.numel(), int(path), _stream(stream))
+        _check("tri_prune_window_ex", rc)
 
 
 def tri_calibrate(q, mag, phase, conc, ws=None, stream=None):

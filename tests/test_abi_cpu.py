@@ -29,6 +29,14 @@ def test_header_declares_the_boundary():
     assert set(names) == set(T.EXPORTS)
 
 
+def test_path_constants_match_the_header():
+    """The binding's TRI_PATH_* values are the header's."""
+    hdr = open(HEADER).read()
+    vals = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (TRI_PATH_\w+) (\d+)", hdr)}
+    assert vals == {"TRI_PATH_AUTO": T.TRI_PATH_AUTO, "TRI_PATH_FULL": T.TRI_PATH_FULL,
+                    "TRI_PATH_CANDIDATES": T.TRI_PATH_CANDIDATES}
+
+
 def test_library_exports_every_declared_symbol():
     lib = T.load()
     missing = [n for n in _declared() if not hasattr(lib, n)]

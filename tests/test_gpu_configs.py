@@ -20,12 +20,12 @@ from helpers import (check_in_place, calib_for, check_agg, check_compaction, che
 pytestmark = pytest.mark.gpu
 
 
-def _dense_prune(T, cfg, g, calib, B):
+def _dense_prune(T, cfg, g, calib, B, path=None):
     desc = dense_desc(T, cfg, g)
     ws = T.workspace(calib, desc, B)
     out = empty_like_dense(g, B)
     nk = out["lengths"]
-    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), nk, ws)
+    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), nk, ws, path=path)
     return desc, ws, out
 
 
@@ -55,7 +55,15 @@ def test_qwen_single_layer_full(gpu_lib):
     log(f"case qwen1l full: 8 segments x {cfg.n_keys}")
     g = W.dense_cache(cfg, "cuda")
     calib, cal = calib_for(T, cfg)
-    desc, ws, out = _dense_prune(T, cfg, g, calib, B)
+    desc, ws, out = _dense_prune(T, cfg, g, calib, B)          # 8 segments: the full-score path
+    # the candidate pass, asked for, keeps the same rows in the same order
+    _, ws_c, out_c = _dense_prune(T, cfg, g, calib, B, path=T.TRI_PATH_CANDIDATES)
+    fb = T.tri_prune_fallbacks(ws_c)
+    log(f"  candidate pass: {fb} fallbacks")
+    for key in ("k", "v", "pos", "lengths"):
+        assert torch.equal(out_c[key], out[key]), f"qwen1l: candidate pass {key} differs from the full path"
+    assert T.tri_prune_fallbacks(ws) == 0
+    del out_c, ws_c
     n_seg, cap, G = cfg.n_seg, g["capacity"], cfg.group
     scores = torch.empty((n_seg, G, cap), device="cuda")
     agg = torch.empty((n_seg, cap), device="cuda")

@@ -28,11 +28,13 @@ def _dense_in_place(T, cfg, cpu, B, what):
     ws = T.workspace(calib, desc, B)
     out = empty_like_dense(g, B)
     nk_oop = torch.full_like(g["lengths"], -1)
-    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), nk_oop, ws)
+    # (the candidate pass wherever the cache allows it: these batches are too
+    # small for the automatic path to take it)
+    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), nk_oop, ws, path=T.TRI_PATH_CANDIDATES)
     torch.cuda.synchronize()
     fb_oop = T.tri_prune_fallbacks(ws)
     # in place, n_kept = the cache's own lengths
-    T.tri_prune_window(calib, desc, g["t"], B, desc, g["lengths"], ws)
+    T.tri_prune_window(calib, desc, g["t"], B, desc, g["lengths"], ws, path=T.TRI_PATH_CANDIDATES)
     torch.cuda.synchronize()
     fb = T.tri_prune_fallbacks(ws)
     log(f"  fallbacks: out of place {fb_oop}, in place {fb}")
@@ -147,6 +149,11 @@ def test_in_place_argument_checks(gpu_lib):
     with pytest.raises(T.TriError) as e:
         T.tri_prune_window(calib, desc, g["t"], 100, shifted, g["lengths"], ws)
     assert e.value.code == T.TRI_ERR_INVALID_ARG
+    out = empty_like_dense(g, 100)
+    for path in (3, -1):                                      # no such path
+        with pytest.raises(T.TriError) as e:
+            T.tri_prune_window(calib, desc, g["t"], 100, dense_desc(T, cfg, out), out["lengths"], ws, path=path)
+        assert e.value.code == T.TRI_ERR_INVALID_ARG
     with pytest.raises(T.TriError) as e:                      # compaction alone stays out of place
         idx = torch.zeros((1, 100), dtype=torch.int32, device="cuda")
         T.tri_compact(desc, idx, g["lengths"], 100, desc)

@@ -21,7 +21,12 @@ def _to(cache, device):
     return {k: (v.to(device) if torch.is_tensor(v) else v) for k, v in cache.items()}
 
 
-def _run_unfused(T, cfg, g, calib, B):
+def _run_unfused(T, cfg, g, calib, B, path=None):
+    """The unfused chain, then the fused pass on the same cache.  These batches
+    are too small for the automatic path to take the candidate pass, so the
+    fused pass asks for it (it applies wherever the cache allows it) unless a
+    path is given."""
+    path = T.TRI_PATH_CANDIDATES if path is None else path
     desc = dense_desc(T, cfg, g)
     ws = T.workspace(calib, desc, B)
     n_seg, cap = g["k"].shape[0], g["k"].shape[1]
@@ -38,7 +43,7 @@ def _run_unfused(T, cfg, g, calib, B):
     # the same cache through the fused entry point
     out2 = empty_like_dense(g, B)
     nk2 = torch.full((n_seg,), -1, dtype=torch.int32, device="cuda")
-    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out2), nk2, ws)
+    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out2), nk2, ws, path=path)
     fallbacks = T.tri_prune_fallbacks(ws)
     torch.cuda.synchronize()
     return dict(scores=scores.cpu(), agg=agg.cpu(), ms=ms.cpu(), idx=idx.cpu(), nk=nk.cpu(), out=_to(out, "cpu"),
@@ -577,6 +582,39 @@ def stored_t(x):
     return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
 
 
+def test_prune_paths_give_the_same_cache(gpu_lib):
+    """On a bf16 batch whose capacity allows the candidate pass, the three
+    paths of tri_prune_window_ex (automatic: the full path for 9 segments;
+    full; candidates) write byte-identical caches and kept counts, out of
+    place and in place.  Neither the automatic nor the full path falls back."""
+    T = gpu_lib
+    B, cap = 600, 12000
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, group=4, dtype=torch.bfloat16, theta=1e6, n_kv_heads=3, n_seq=3,
+                                    n_keys=cap, t=cap + 3, budget=B, sigma=None, seed=53)
+    log("case prune paths")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([cap, 4095, 4096, 8 * B - 1, 8 * B, 8 * B + 1, 9001, B + 1, 0], dtype=torch.int32)
+    calib, _ = calib_for(T, cfg)
+    outs, fbs = {}, {}
+    for path in (T.TRI_PATH_AUTO, T.TRI_PATH_FULL, T.TRI_PATH_CANDIDATES):
+        g = _to(cpu, "cuda")
+        desc = dense_desc(T, cfg, g)
+        ws = T.workspace(calib, desc, B)
+        out = empty_like_dense(g, B)
+        T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), out["lengths"], ws, path=path)
+        fbs[path] = T.tri_prune_fallbacks(ws)
+        T.tri_prune_window(calib, desc, g["t"], B, desc, g["lengths"], ws, path=path)      # in place
+        torch.cuda.synchronize()
+        outs[path] = (_to(out, "cpu"), _to(g, "cpu"))
+    log(f"  fallbacks per path: {fbs}")
+    assert fbs[T.TRI_PATH_AUTO] == 0 and fbs[T.TRI_PATH_FULL] == 0
+    ref_out, ref_in = outs[T.TRI_PATH_FULL]
+    for path, (out, inp) in outs.items():
+        for key in ("k", "v", "pos", "lengths"):
+            assert torch.equal(out[key], ref_out[key]), f"path {path}: out of place {key} differs"
+            assert torch.equal(inp[key], ref_in[key]), f"path {path}: in place {key} differs"
+
+
 def test_fallback_count_zero_without_candidate_mode(gpu_lib):
     """A pass that never enters candidate mode (fp32 here) reports zero
     fallbacks even on a workspace holding stale bytes."""
@@ -615,7 +653,7 @@ def test_cache_at_a_later_calibration_layer(gpu_lib):
     odesc = T.cache_desc(out["k"], out["v"], out["pos"], out["lengths"], n_layers=2, n_seq=cfg.n_seq,
                          n_kv_heads=cfg.n_kv_heads, layer0=1)
     ws = T.workspace(calib, desc, B)
-    T.tri_prune_window(calib, desc, g["t"], B, odesc, nk, ws)
+    T.tri_prune_window(calib, desc, g["t"], B, odesc, nk, ws, path=T.TRI_PATH_CANDIDATES)
     agg = torch.full((cfg.n_seg, cap), float("nan"), device="cuda")
     T.tri_score(calib, desc, g["t"], agg, ws)
     torch.cuda.synchronize()
