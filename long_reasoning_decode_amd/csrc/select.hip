@@ -463,28 +463,33 @@ __global__ __launch_bounds__(kSelThreads) void k_select_fallback(SelectArgs a) {
 }
 
 template <int J, int G>
-static void select_launch(const SelectArgs& a, int mode, hipStream_t stream) {
+static bool select_launch(const SelectArgs& a, int mode, hipStream_t stream) {
     const dim3 block(kSelThreads);
     if (mode == SELECT_S_FALLBACK) {
         if constexpr (G > 0)
             hipLaunchKernelGGL((k_select_fallback<J, G>), dim3((unsigned)(a.n_seg < 512 ? a.n_seg : 512)), block, 0, stream, a);
-        return;
+        return G > 0;
     }
     const dim3 grid((unsigned)a.n_seg);
-    if constexpr (G == 0) hipLaunchKernelGGL((k_select<J, 0, SELECT_A>), grid, block, 0, stream, a);
-    else if (mode == SELECT_C) hipLaunchKernelGGL((k_select<J, G, SELECT_C>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_select<J, G, SELECT_S>), grid, block, 0, stream, a);
+    if constexpr (G == 0) {
+        hipLaunchKernelGGL((k_select<J, 0, SELECT_A>), grid, block, 0, stream, a);
+    } else if (mode == SELECT_C) {
+        hipLaunchKernelGGL((k_select<J, G, SELECT_C>), grid, block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((k_select<J, G, SELECT_S>), grid, block, 0, stream, a);
+    }
+    return true;
 }
 
 template <int J>
 static bool select_group(const SelectArgs& a, int group, int mode, hipStream_t stream) {
     if ((group == 0) != (mode == SELECT_A)) return false;
     switch (group) {
-        case 0: select_launch<J, 0>(a, mode, stream); return true;
-        case 1: select_launch<J, 1>(a, mode, stream); return true;
-        case 2: select_launch<J, 2>(a, mode, stream); return true;
-        case 4: select_launch<J, 4>(a, mode, stream); return true;
-        case 8: select_launch<J, 8>(a, mode, stream); return true;
+        case 0: return select_launch<J, 0>(a, mode, stream);
+        case 1: return select_launch<J, 1>(a, mode, stream);
+        case 2: return select_launch<J, 2>(a, mode, stream);
+        case 4: return select_launch<J, 4>(a, mode, stream);
+        case 8: return select_launch<J, 8>(a, mode, stream);
         default: return false;
     }
 }
@@ -509,6 +514,8 @@ hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_l
     else if (held <= 8 * kSelThreads) ok = select_group<8>(a, group, mode, stream);
     else if (mode == SELECT_C && held <= 16 * kSelThreads) ok = select_group<16>(a, group, mode, stream);
     else if (held <= 32 * kSelThreads) ok = select_group<32>(a, group, mode, stream);
+    // a 32K-key cache plus a window of up to 4K appended keys
+    else if (held <= 36 * kSelThreads) ok = select_group<36>(a, group, mode, stream);
     else ok = select_group<64>(a, group, mode, stream);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();

@@ -122,7 +122,7 @@ def test_equal_scores_keep_lowest_slots(gpu_lib):
     _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "equal")
 
 
-@pytest.mark.parametrize("cap", [2048, 8192, 32768, 40000, 65536])
+@pytest.mark.parametrize("cap", [2048, 8192, 32768, 32896, 40000, 65536])
 def test_select_kernel_bit_exact(gpu_lib, cap):
     """tri_select_topb on seeded score arrays (ties, signed zeros, all-equal)
     equals the oracle's selection exactly."""
