@@ -236,34 +236,57 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
     if (!all) {
         ZParams<GZ> z;
         if constexpr (G > 0) {
-            z = merge_stats<G, kSelThreads>(a.stats + (int64_t)s * a.n_chunks * G, a.n_chunks, a.chunk, N, scratch);
+            // the segment's mean and spread per head: each wave merges the chunk
+            // statistics by itself when a wave holds them all (no barrier)
+            const double2* st = a.stats + (int64_t)s * a.n_chunks * G;
+            auto merge = [&]() {
+                return a.n_chunks <= kWave ? merge_stats_wave<G>(st, a.n_chunks, a.chunk, N)
+                                           : merge_stats<G, kSelThreads>(st, a.n_chunks, a.chunk, N, scratch);
+            };
             if constexpr (CAND) {
+                z = merge();
                 nv = load_candidates<J, G, NB>(a, s, N, z, key, pre, lpos, mw, hwl, wsum, bcast);
                 if (nv < B) {                           // overflow (-1) or too few to hold the cut
                     if (tid == 0) a.fb_list[atomicAdd(a.fb_count, 1)] = s;
                     return;
                 }
             } else {
+                // Key j's G scores; loaded LB keys at a time (the scheduler would
+                // otherwise hoist every key's loads at once).  Where one block
+                // per CU leaves the registers (J >= 32), batches are 16 keys and
+                // the first is requested before the merge, which does not need it.
+                constexpr bool WIDE = J >= 32 && G <= 4;
+                constexpr int LB = WIDE ? 16 : 8;
+                constexpr int L0 = WIDE ? LB : 0;                  // keys loaded before the merge
+                auto load_scores = [&](int j, float (&S)[G]) {
+                    const float* p = a.s_int + ((int64_t)s * a.cap + j * kSelThreads + tid) * G;
+                    if constexpr (G % 4 == 0) {
 #pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    const int n = j * kSelThreads + tid;
-                    if (n < N) {
-                        const float* p = a.s_int + ((int64_t)s * a.cap + n) * G;
-                        float S[G];
-                        if constexpr (G % 4 == 0) {
-#pragma unroll
-                            for (int g = 0; g < G; g += 4) {
-                                const float4 v = *reinterpret_cast<const float4*>(p + g);
-                                S[g] = v.x; S[g + 1] = v.y; S[g + 2] = v.z; S[g + 3] = v.w;
-                            }
-                        } else {
-#pragma unroll
-                            for (int g = 0; g < G; ++g) S[g] = p[g];
+                        for (int g = 0; g < G; g += 4) {
+                            const float4 v = *reinterpret_cast<const float4*>(p + g);
+                            S[g] = v.x; S[g + 1] = v.y; S[g + 2] = v.z; S[g + 3] = v.w;
                         }
+                    } else {
+#pragma unroll
+                        for (int g = 0; g < G; ++g) S[g] = p[g];
+                    }
+                };
+                float S0[L0 > 0 ? L0 : 1][G];
+#pragma unroll
+                for (int j = 0; j < L0; ++j)
+                    if (j * kSelThreads + tid < N) load_scores(j, S0[j]);
+                z = merge();
+#pragma unroll
+                for (int j = 0; j < L0; ++j)
+                    if (j * kSelThreads + tid < N) key[j] = order_key(aggregate<G>(S0[j], z));
+#pragma unroll
+                for (int j = L0; j < J; ++j) {
+                    if (j * kSelThreads + tid < N) {
+                        float S[G];
+                        load_scores(j, S);
                         key[j] = order_key(aggregate<G>(S, z));
                     }
-                    // keep the scheduler from hoisting every key's loads at once
-                    if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+                    if (j % LB == LB - 1) __builtin_amdgcn_sched_barrier(0);
                 }
             }
         } else {

@@ -90,6 +90,36 @@ __device__ __forceinline__ ZParams<G> merge_stats(const double2* st, int n_chunk
     return z;
 }
 
+// The same merge by one wave, for at most 64 chunks (lane c holds chunk c):
+// no barrier and no LDS, so each wave of a block can run it by itself.  Its
+// sums are exactly those of merge_stats: there, too, every chunk sits in wave
+// 0 (thread c), the butterfly is the same, and the other waves add zeros.
+template <int G>
+__device__ __forceinline__ ZParams<G> merge_stats_wave(const double2* st, int n_chunks, int chunk, int N) {
+    const int c = threadIdx.x & (kWave - 1);
+    const int nc = c < n_chunks ? min(max(N - c * chunk, 0), chunk) : 0;
+    ZParams<G> z;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {                 // one head at a time: few registers live
+        const double2 v = nc > 0 ? st[c * G + g] : make_double2(0.0, 0.0);
+        double acc = 0.0;
+        if (nc > 0) acc += (double)nc * v.x;
+        acc = wave_sum(acc);
+        const double mean = N > 0 ? acc / (double)N : 0.0;
+        acc = 0.0;
+        if (nc > 0) {
+            const double dm = v.x - mean;
+            acc += v.y + (double)nc * dm * dm;
+        }
+        acc = wave_sum(acc);
+        const double sig = N > 0 ? sqrt(acc / (double)N) : 0.0;
+        z.mu_hi[g] = (float)mean;
+        z.mu_lo[g] = (float)(mean - (double)z.mu_hi[g]);
+        z.inv[g] = sig > 0.0 ? (float)(1.0 / sig) : 0.0f;
+    }
+    return z;
+}
+
 // A = max over the G query heads of their z-scores.
 template <int G>
 __device__ __forceinline__ float aggregate(const float (&S)[G], const ZParams<G>& z) {
