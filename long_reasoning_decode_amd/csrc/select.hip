@@ -523,8 +523,9 @@ hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_l
     int64_t held = max_len;                             // entries one thread block holds in registers
     if (mode == SELECT_C) {
         // every key of a segment outside candidate mode (N < max(4096, 8B)), or
-        // half of the longest segment's keys (the expected candidates are 2.5 B/N
-        // of them, at most 5/16); a longer list falls back to mode S
+        // half of the longest segment's keys (the sampled threshold admits about
+        // 3 B/N of them, at most 3/8 since N >= 8 B); a longer list sends its
+        // segment to the fallback (full rescoring, mode S)
         const int64_t small = 8 * (int64_t)a.budget > 4096 ? 8 * (int64_t)a.budget : 4096;
         const int64_t half = (max_len + 1) / 2 > small ? (max_len + 1) / 2 : small;
         held = half < max_len ? half : max_len;
