@@ -103,6 +103,19 @@ def test_in_place_maximum_sizes(gpu_lib):
     _dense_in_place(gpu_lib, cfg, cpu, B, "in place maximum")
 
 
+def test_candidate_select_36_keys_per_thread(gpu_lib):
+    """B = 4500: segments below 8 B = 36000 keys list every key, so the
+    candidate select holds up to 36000 entries (36 per thread).  Candidate and
+    full-score segments, in place and out of place, against the oracle."""
+    B, cap = 4500, 40000
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, group=4, dtype=torch.bfloat16, theta=1e6, n_kv_heads=1, n_seq=5,
+                                    n_keys=cap, t=cap + 1, budget=B, sigma=None, seed=37)
+    log("case candidate select, 36 keys per thread")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([cap, 36000, 35999, 20000, B + 1], dtype=torch.int32)
+    _dense_in_place(gpu_lib, cfg, cpu, B, "in place J36")
+
+
 def test_in_place_paged(gpu_lib):
     """A ragged paged pool (random page tables) pruned where it is."""
     T = gpu_lib
