@@ -385,7 +385,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus} GPUs, WORLD_SIZE={world}); the pruning "
-              "path has no cross-GPU step and this build runs on a single MI355X", file=sys.stderr)
+              "path has no cross-GPU step: each GPU would run the same kernels on its own share of the segments",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
