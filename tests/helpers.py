@@ -2,7 +2,8 @@
 HIP path through the C ABI, running the oracle on the same bytes, and the
 tolerance checks.
 
-Tolerances (derived in the design doc from the arithmetic):
+Tolerances (from the arithmetic: fp32 accumulation of exact bf16 products and
+an fp32 aggregate, against the oracle's fp64):
   scores S_h : |gpu - ref| <= 1e-4 * max(|ref|, rms of the head's ref scores)
   mu, sigma  : |gpu - ref| <= 1e-4 * max(|ref mu|, ref sigma)
   A          : |gpu - ref| <= 1e-4 * max(|ref|, 1)
