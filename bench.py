@@ -87,6 +87,37 @@ def cpu_baseline(W, cfg, g, cal, B, n_sample):
                       f"layers/sequences/heads; {dt:.1f} s wall on {threads} threads"}
 
 
+def kernel_breakdown(T, step, steps):
+    """{kernel: (launches, total ms)} over `steps` steps with every kernel
+    bracketed by events (untimed: each event record costs GPU time)."""
+    import torch
+    T.tri_timing_reset()
+    T.tri_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    T.tri_timing_enable(False)
+    return T.tri_timing_read()
+
+
+def timed_steps(T, step, steps, stream, kernels):
+    """The timed region: `steps` steps between two events, with only the named
+    kernels' launches bracketed by library events.  Returns (ms per step,
+    {kernel: (launches, total ms)})."""
+    import torch
+    T.tri_timing_reset()
+    T.tri_timing_enable(True, only=kernels)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    T.tri_timing_enable(False)
+    return ev0.elapsed_time(ev1) / steps, T.tri_timing_read()
+
+
 def copy_bandwidth(mib=4096, reps=5):
     """Read + write bytes per second of a plain device-to-device copy."""
     import torch
@@ -156,7 +187,8 @@ def bench_decode_loop(args, T, W):
     toks = [W.decode_token(cfg, km, j, t0 + j, "cuda") for j in range(win)]
     out = torch.empty(toks[0][2].shape, dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(cfg.head_dim)
-    pos = torch.arange(t0, t0 + (args.warmup + args.steps + 1) * win, dtype=torch.int32,
+    # positions of every window run: warmup, the per-kernel breakdown and the timed steps
+    pos = torch.arange(t0, t0 + (args.warmup + 2 * args.steps + 1) * win, dtype=torch.int32,
                        device="cuda")[:, None].expand(-1, cfg.n_seq).contiguous()      # [token][seq]
     tvec = torch.empty((cfg.n_seq,), dtype=torch.int32, device="cuda")
     state = {"cur": 0, "w": 0}
@@ -164,13 +196,21 @@ def bench_decode_loop(args, T, W):
     in_place = not args.out_of_place
     moved = {}
 
+    # timed region: events around every 8th decode-attention launch of a window only
+    sampled = list(range(0, win, 8))
+    state["sample"] = False
+
     def window(count_moves=False):
         cur = state["cur"]
         d = descs[cur]
         for j in range(win):
             k_new, v_new, q = toks[j]
             T.tri_append(d, k_new, v_new, pos[state["w"] * win + j], stream=stream)
+            if state["sample"]:
+                T.tri_timing_enable(j % 8 == 0, only=["decode_attn"])
             T.tri_decode_attn(d, cfg.n_q_heads, q, scale, out, stream=stream)
+        if state["sample"]:
+            T.tri_timing_enable(False)
         tvec.fill_(t0 + (state["w"] + 1) * win)
         if in_place:
             before = caches[cur]["pos"][:, :B].clone() if count_moves else None
@@ -186,30 +226,27 @@ def bench_decode_loop(args, T, W):
     for i in range(args.warmup):
         window(count_moves=in_place and i == args.warmup - 1)
     torch.cuda.synchronize()
-    T.tri_timing_reset()
-    T.tri_timing_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        window()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    T.tri_timing_enable(False)
-    ms = ev0.elapsed_time(ev1) / args.steps
-    kt = T.tri_timing_read()
+    kt = kernel_breakdown(T, window, args.steps)          # every kernel, untimed
+    state["sample"] = True
+    ms, kt_timed = timed_steps(T, window, args.steps, stream, ["decode_attn"])
+    state["sample"] = False
     es = 2
-    # decode attention reads every valid K and V row once per step (lengths B+1 .. B+win over a window)
-    kv_rows = cfg.n_seg * sum(B + j + 1 for j in range(win))
-    attn_bytes = kv_rows * cfg.head_dim * es * 2 + win * (out.numel() * (es + 4))
-    attn_launches, attn_ms = kt["decode_attn"]
+    # decode attention reads every valid K and V row once per step (lengths B+1 .. B+win over a
+    # window); the timed region brackets the launches j = 0, 8, ..., so their bytes are counted
+    attn_bytes = (cfg.n_seg * sum(B + j + 1 for j in range(win)) * cfg.head_dim * es * 2
+                  + win * (out.numel() * (es + 4)))
+    sampled_bytes = (cfg.n_seg * sum(B + j + 1 for j in sampled) * cfg.head_dim * es * 2
+                     + len(sampled) * (out.numel() * (es + 4)))
+    attn_launches, attn_ms = kt_timed["decode_attn"]
     attn_avg = attn_ms / attn_launches
-    attn_gbs = attn_bytes / win / (attn_avg * 1e-3) / 1e9
+    attn_gbs = sampled_bytes / len(sampled) / (attn_avg * 1e-3) / 1e9
     # score reads every key; compaction reads and writes K, V and position of each copied row
     # (all B kept rows out of place; in place, the rows moved, counted on the last warmup window)
     copied = moved.get("rows", cfg.n_seg * B) if in_place else cfg.n_seg * B
     prune_bytes = cfg.n_seg * (B + win) * cfg.head_dim * es + copied * (4 * cfg.head_dim * es + 8)
     kernels = {k: {"avg_ms": round(v[1] / v[0], 4), "launches": v[0]} for k, v in kt.items() if v[0]}
     kernels["decode_attn"]["algorithmic_bytes"] = round(attn_bytes / win)        # per launch, window average
+    kernels["decode_attn"]["timed_region_avg_ms"] = round(attn_avg, 4)           # the sampled launches
     prune_ms = sum(v["avg_ms"] for k, v in kernels.items() if k not in ("append", "decode_attn"))
     tokens = win * cfg.n_seq
     result = {
@@ -251,24 +288,18 @@ def bench_calibrate(args, T, W):
     T.load().tri_calibrate_workspace_size(L, n, Hq, d, ctypes.byref(sz))
     ws = torch.empty(sz.value, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    def step():
+        T.tri_calibrate(q, mag, phase, conc, ws=ws, stream=stream)
+
     for _ in range(args.warmup):
-        T.tri_calibrate(q, mag, phase, conc, ws=ws, stream=stream)
+        step()
     torch.cuda.synchronize()
-    T.tri_timing_reset()
-    T.tri_timing_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        T.tri_calibrate(q, mag, phase, conc, ws=ws, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    T.tri_timing_enable(False)
-    ms = ev0.elapsed_time(ev1) / args.steps
-    kt = T.tri_timing_read()
+    kt = kernel_breakdown(T, step, args.steps)
+    ms, kt_timed = timed_steps(T, step, args.steps, stream, ["calibrate"])
     kernels = {k: {"avg_ms": round(v[1] / v[0], 4), "launches": v[0]} for k, v in kt.items() if v[0]}
     alg = q.numel() * q.element_size() + 3 * mag.numel() * 4
     kernels["calibrate"]["algorithmic_bytes"] = q.numel() * q.element_size()
-    part = kernels["calibrate"]["avg_ms"]
+    part = kt_timed["calibrate"][1] / kt_timed["calibrate"][0]
     gbs = q.numel() * q.element_size() / (part * 1e-3) / 1e9
     result = {
         "metric": "query samples calibrated/sec (offline centre magnitude, phase and concentration)",
@@ -319,17 +350,8 @@ def bench_ragged(args, T, W):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    T.tri_timing_reset()
-    T.tri_timing_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    T.tri_timing_enable(False)
-    ms = ev0.elapsed_time(ev1) / args.steps
-    kt = T.tri_timing_read()
+    kt = kernel_breakdown(T, step, args.steps)
+    ms, kt_timed = timed_steps(T, step, args.steps, stream, ["decode_attn"])
     kernels = {k: {"avg_ms": round(v[1] / v[0], 4), "launches": v[0]} for k, v in kt.items() if v[0]}
     lens = pc["lengths"].long()
     kept = torch.clamp(lens, max=B)
@@ -338,7 +360,8 @@ def bench_ragged(args, T, W):
     prune_bytes = n_keys * cfg.head_dim * es + int(kept.sum()) * (4 * cfg.head_dim * es + 8)
     prune_ms = sum(v["avg_ms"] for k, v in kernels.items() if k != "decode_attn")
     attn_bytes = int(kept.sum()) * cfg.head_dim * es * 2
-    attn_gbs = attn_bytes / (kernels["decode_attn"]["avg_ms"] * 1e-3) / 1e9
+    attn_avg = kt_timed["decode_attn"][1] / kt_timed["decode_attn"][0]
+    attn_gbs = attn_bytes / (attn_avg * 1e-3) / 1e9
     kernels["decode_attn"]["algorithmic_bytes"] = attn_bytes
     kernels["score"]["algorithmic_bytes"] = n_keys * cfg.head_dim * es
     result = {
@@ -426,21 +449,19 @@ def main():
     print(f"# inputs ready in {t_gen:.1f} s: {cfg.n_seg} segments x {cfg.n_keys} keys", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+
+    def step():
+        T.tri_prune_window(calib, src, g["t"], B, dst, out["lengths"], ws, stream=stream)
+
     for _ in range(args.warmup):
-        T.tri_prune_window(calib, src, g["t"], B, dst, out["lengths"], ws, stream=stream)
+        step()
     torch.cuda.synchronize()
-    T.tri_timing_reset()
-    T.tri_timing_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        T.tri_prune_window(calib, src, g["t"], B, dst, out["lengths"], ws, stream=stream)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    T.tri_timing_enable(False)
-    ms = ev0.elapsed_time(ev1) / args.steps
-    kt = T.tri_timing_read()
+    # every kernel's duration (untimed steps), then the timed region with only
+    # the dominant HBM-bound kernel bracketed by events
+    kt = kernel_breakdown(T, step, args.steps)
+    heavy = ("score", "select_gather", "gather")
+    dom = max(heavy, key=lambda k: kt.get(k, (0, 0.0))[1] / max(kt.get(k, (0, 0.0))[0], 1))
+    ms, kt_timed = timed_steps(T, step, args.steps, stream, [dom])
     fallbacks = T.tri_prune_fallbacks(ws)
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
@@ -491,8 +512,10 @@ def main():
         launches, total = kt.get(name, (0, 0.0))
         if launches:
             kernels[name] = {"avg_ms": round(total / launches, 4), "launches": launches}
-    dom = max(("score", "select_gather", "gather"), key=lambda k: kernels.get(k, {}).get("avg_ms", 0.0))
-    achieved = kernels[dom]["achieved_GBs"]
+    dom_bytes = {"score": b_score, "select_gather": b_gather, "gather": b_gather}[dom]
+    dom_avg = kt_timed[dom][1] / kt_timed[dom][0]
+    achieved = round(dom_bytes / (dom_avg * 1e-3) / 1e9, 1)
+    kernels[dom]["timed_region_avg_ms"] = round(dom_avg, 4)
     traffic = read_traffic(dom, args.workload)
     pass_gbs = (b_score + b_gather) / (ms * 1e-3) / 1e9
     result = {

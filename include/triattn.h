@@ -278,12 +278,17 @@ const char* tri_last_error(void);
 
 /*
  * Kernel timing (instrumentation).  When enabled, every kernel launched by
- * the library is bracketed by HIP events on its stream; tri_timing_read
- * synchronises those events and returns, for kernel id `which` (0-based, see
- * tri_timing_name), the number of launches and their summed duration in ms
- * since the last reset.  Returns TRI_ERR_INVALID_ARG past the last id.
+ * the library whose id is in the mask (bit i = kernel id i; all kernels
+ * until tri_timing_mask says otherwise) is bracketed by HIP events on its
+ * stream; each event record costs a few microseconds of GPU time, so a
+ * caller timing a short pass can restrict the mask to the kernels it needs.
+ * tri_timing_read synchronises those events and returns, for kernel id
+ * `which` (0-based, see tri_timing_name), the number of launches and their
+ * summed duration in ms since the last reset.  Returns TRI_ERR_INVALID_ARG
+ * past the last id.
  */
 int tri_timing_enable(int enable);
+int tri_timing_mask(uint32_t mask);
 int tri_timing_reset(void);
 int tri_timing_read(int which, int64_t* launches, double* total_ms);
 const char* tri_timing_name(int which);

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -32,12 +33,27 @@ constexpr int kMinChunk = 512;
 
 // ---------------------------------------------------------------- timing
 struct PendingTiming {
-    int id;
+    int id, device;
     hipEvent_t start, stop;
 };
 std::mutex g_tmu;
 bool g_timing = false;
+uint32_t g_timing_mask = ~0u;                   // kernel ids timed when enabled
 std::vector<PendingTiming> g_pending;
+// Timing events are reused (per device): creating two events for every launch
+// cost the host more than a small pass's kernels take.
+std::map<int, std::vector<hipEvent_t>> g_free_events;
+
+hipEvent_t take_event_locked(int device) {
+    auto& f = g_free_events[device];
+    if (!f.empty()) {
+        hipEvent_t e = f.back();
+        f.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
 int64_t g_launches[KID_COUNT] = {};
 double g_ms[KID_COUNT] = {};
 const char* kKernelNames[KID_COUNT] = {"phase",  "score",  "zmax",   "select",         "select_gather",
@@ -51,8 +67,8 @@ void drain_timing_locked() {
             g_ms[p.id] += ms;
             g_launches[p.id] += 1;
         }
-        (void)hipEventDestroy(p.start);
-        (void)hipEventDestroy(p.stop);
+        g_free_events[p.device].push_back(p.start);
+        g_free_events[p.device].push_back(p.stop);
     }
     g_pending.clear();
 }
@@ -270,8 +286,12 @@ int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const in
 namespace tri {
 TimedLaunch::TimedLaunch(int id_, hipStream_t s) : id(id_), stream(s) {
     std::lock_guard<std::mutex> lk(g_tmu);
-    if (!g_timing) return;
-    if (hipEventCreate(&start) != hipSuccess || hipEventCreate(&stop) != hipSuccess) {
+    if (!g_timing || !((g_timing_mask >> id) & 1u) || hipGetDevice(&device) != hipSuccess) return;
+    start = take_event_locked(device);
+    stop = take_event_locked(device);
+    if (!start || !stop) {
+        if (start) g_free_events[device].push_back(start);
+        if (stop) g_free_events[device].push_back(stop);
         start = stop = nullptr;
         return;
     }
@@ -281,7 +301,7 @@ TimedLaunch::~TimedLaunch() {
     if (!start) return;
     std::lock_guard<std::mutex> lk(g_tmu);
     (void)hipEventRecord(stop, stream);
-    g_pending.push_back({id, start, stop});
+    g_pending.push_back({id, device, start, stop});
 }
 }  // namespace tri
 
@@ -728,6 +748,12 @@ int tri_calibrate(const void* q, int dtype, int n_layers, int n_samples, int n_q
 int tri_timing_enable(int enable) {
     std::lock_guard<std::mutex> lk(g_tmu);
     g_timing = enable != 0;
+    return TRI_OK;
+}
+
+int tri_timing_mask(uint32_t mask) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing_mask = mask;
     return TRI_OK;
 }
 

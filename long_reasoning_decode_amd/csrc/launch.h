@@ -53,6 +53,7 @@ struct TimedLaunch {
     ~TimedLaunch();
     int id;
     hipStream_t stream;
+    int device = 0;
     hipEvent_t start = nullptr, stop = nullptr;
 };
 

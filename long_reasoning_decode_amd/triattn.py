@@ -37,6 +37,7 @@ EXPORTS = (
     "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
     "tri_compact", "tri_prune_window", "tri_append", "tri_decode_attn", "tri_strerror",
     "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name", "tri_last_error",
+    "tri_timing_mask",
     "tri_prune_fallbacks", "tri_calibrate_workspace_size", "tri_calibrate", "tri_calib_load_ex",
     "tri_prune_window_ex",
 )
@@ -91,6 +92,7 @@ def load():
         "tri_decode_attn": [DP, I, P, F, P, P],
         "tri_strerror": [I],
         "tri_timing_enable": [I],
+        "tri_timing_mask": [ctypes.c_uint32],
         "tri_timing_reset": [],
         "tri_timing_read": [I, ctypes.POINTER(I64), ctypes.POINTER(D)],
         "tri_timing_name": [I],
@@ -280,8 +282,23 @@ def tri_last_error():
     return load().tri_last_error().decode()
 
 
-def tri_timing_enable(on=True):
-    _check("tri_timing_enable", load().tri_timing_enable(1 if on else 0))
+def tri_timing_enable(on=True, only=None):
+    """Time every kernel, or only the kernels named in `only` (each timed
+    launch costs two event records of GPU time)."""
+    lib = load()
+    mask = 0xFFFFFFFF
+    if only is not None:
+        names = []
+        i = 0
+        while lib.tri_timing_name(i) is not None:
+            names.append(lib.tri_timing_name(i).decode())
+            i += 1
+        unknown = set(only) - set(names)
+        if unknown:
+            raise ValueError(f"unknown kernel names {sorted(unknown)}")
+        mask = sum(1 << names.index(n) for n in set(only))
+    _check("tri_timing_mask", lib.tri_timing_mask(mask))
+    _check("tri_timing_enable", lib.tri_timing_enable(1 if on else 0))
 
 
 def tri_timing_reset():

@@ -37,6 +37,16 @@ def test_path_constants_match_the_header():
                     "TRI_PATH_CANDIDATES": T.TRI_PATH_CANDIDATES}
 
 
+def test_timing_mask_is_host_only():
+    """Restricting the timed kernels needs no GPU; unknown names are refused."""
+    T.tri_timing_enable(True, only=["score", "decode_attn"])
+    T.tri_timing_enable(False)
+    assert T.load().tri_timing_mask(0xFFFFFFFF) == T.TRI_OK
+    with pytest.raises(ValueError):
+        T.tri_timing_enable(True, only=["no_such_kernel"])
+    T.tri_timing_enable(False)
+
+
 def test_library_exports_every_declared_symbol():
     lib = T.load()
     missing = [n for n in _declared() if not hasattr(lib, n)]
