@@ -300,6 +300,7 @@ def bench_calibrate(args, T, W):
     alg = q.numel() * q.element_size() + 3 * mag.numel() * 4
     kernels["calibrate"]["algorithmic_bytes"] = q.numel() * q.element_size()
     part = kt_timed["calibrate"][1] / kt_timed["calibrate"][0]
+    kernels["calibrate"]["timed_region_avg_ms"] = round(part, 4)
     gbs = q.numel() * q.element_size() / (part * 1e-3) / 1e9
     result = {
         "metric": "query samples calibrated/sec (offline centre magnitude, phase and concentration)",
@@ -362,6 +363,7 @@ def bench_ragged(args, T, W):
     attn_bytes = int(kept.sum()) * cfg.head_dim * es * 2
     attn_avg = kt_timed["decode_attn"][1] / kt_timed["decode_attn"][0]
     attn_gbs = attn_bytes / (attn_avg * 1e-3) / 1e9
+    kernels["decode_attn"]["timed_region_avg_ms"] = round(attn_avg, 4)
     kernels["decode_attn"]["algorithmic_bytes"] = attn_bytes
     kernels["score"]["algorithmic_bytes"] = n_keys * cfg.head_dim * es
     result = {
