@@ -64,7 +64,7 @@ def test_in_place_ragged_lengths(gpu_lib, d, G, dtype):
     _dense_in_place(gpu_lib, cfg, cpu, B, f"in place d{d} G{G}")
 
 
-@pytest.mark.parametrize("d,G", [(128, 4), (64, 8)])
+@pytest.mark.parametrize("d,G", [(128, 4), (64, 8), (128, 1), (64, 2), (128, 2), (64, 4)])
 def test_in_place_candidate_pass(gpu_lib, d, G):
     """Lengths around the candidate-mode boundaries (4096 and 8B)."""
     B, cap = 600, 12000
