@@ -396,20 +396,46 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
     }
 }
 
-// Waves per decode-attention workgroup.  Four single-buffered waves (about
-// 37 KB of LDS) let four workgroups share a CU: the same 16 waves per CU as
-// 2 x 8 or 1 x 16, with more tiles per wave to amortise each workgroup's
-// start and a cheaper final merge (measured fastest of 4, 8 and 16).
+// Waves per decode-attention workgroup.  Four single-buffered waves (32 KB of
+// LDS) let four or five workgroups share a CU, with more tiles per wave to
+// amortise each workgroup's start and a cheaper final merge than 2 x 8 or
+// 1 x 16 (measured fastest of 4, 8 and 16 on a batch that fills the GPU many
+// times over, and no slower from 288 segments up).  A batch with fewer
+// segments than CUs leaves most SIMDs without waves at four per segment: it
+// takes 8 waves per segment (25-75% faster at 192 segments, head_dim 64 and
+// 128), and 16 when at most half the CUs have a segment.
 constexpr int kAttnWaves = 4;
+
+static int attn_waves(int64_t n_seg) {
+    static int cus = -1;
+    if (cus < 0) {
+        int dev = 0, n = 0;
+        cus = hipGetDevice(&dev) == hipSuccess &&
+                      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0
+                  ? n
+                  : 256;
+    }
+    if (n_seg >= cus) return kAttnWaves;
+    return 2 * n_seg > cus ? 8 : 16;
+}
+
+template <int D, int G, bool PAGED>
+static void attn_mfma(const AttnArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_seg);
+    switch (attn_waves(a.n_seg)) {
+        case kAttnWaves:
+            hipLaunchKernelGGL((k_decode_attn_mfma<D, G, PAGED, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, stream, a);
+            break;
+        case 8: hipLaunchKernelGGL((k_decode_attn_mfma<D, G, PAGED, 8>), grid, dim3(8 * 64), 0, stream, a); break;
+        default: hipLaunchKernelGGL((k_decode_attn_mfma<D, G, PAGED, 16>), grid, dim3(16 * 64), 0, stream, a); break;
+    }
+}
 
 template <int D, int G>
 static void attn_dtype(const AttnArgs& a, bool bf16, hipStream_t stream) {
-    const dim3 grid((unsigned)a.n_seg), block(256);
-    if (bf16 && a.kv.page_size > 0)
-        hipLaunchKernelGGL((k_decode_attn_mfma<D, G, true, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, stream, a);
-    else if (bf16)
-        hipLaunchKernelGGL((k_decode_attn_mfma<D, G, false, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, stream, a);
-    else hipLaunchKernelGGL((k_decode_attn<D, G, false>), grid, block, 0, stream, a);
+    if (bf16 && a.kv.page_size > 0) attn_mfma<D, G, true>(a, stream);
+    else if (bf16) attn_mfma<D, G, false>(a, stream);
+    else hipLaunchKernelGGL((k_decode_attn<D, G, false>), dim3((unsigned)a.n_seg), dim3(256), 0, stream, a);
 }
 
 template <int D>

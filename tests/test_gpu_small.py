@@ -510,12 +510,14 @@ def test_decode_attention_shapes(gpu_lib, d, G, dtype, paged, n_seq):
         assert err.max() <= 1e-4, f"attention d={d} G={G} {dtype} paged={paged} seg {s} N={N}: {err.max():.2e}"
 
 
-@pytest.mark.parametrize("d,G", [(64, 8), (128, 4), (64, 2)])
-def test_decode_attention_more_segments_than_workgroups(gpu_lib, d, G):
-    """Dense bf16 caches with more segments (2560) than the GPU holds
-    workgroups at once, at ragged lengths; every segment against the oracle."""
+@pytest.mark.parametrize("d,G,n_seq", [(64, 8, 320), (128, 4, 320), (64, 2, 320), (128, 4, 20), (64, 8, 20),
+                                       (128, 2, 10)])
+def test_decode_attention_batch_sizes(gpu_lib, d, G, n_seq):
+    """Dense bf16 caches at ragged lengths, every segment against the oracle:
+    more segments (2560) than the GPU holds workgroups at once, and batches
+    of 160 and 80 segments (fewer than CUs: 8 and 16 waves per segment)."""
     T = gpu_lib
-    n_seq, hkv, cap = 320, 8, 160
+    hkv, cap = 8, 160
     n_seg, hq = n_seq * hkv, hkv * G
     gen = torch.Generator().manual_seed(47 + d + G)
     K = torch.randn((n_seg, cap, d), generator=gen).to(torch.bfloat16)
