@@ -617,6 +617,42 @@ def test_prune_paths_give_the_same_cache(gpu_lib):
             assert torch.equal(inp[key], ref_in[key]), f"path {path}: in place {key} differs"
 
 
+@pytest.mark.parametrize("n_seq,n_keys", [(3, 12000), (1, 3000)])
+def test_prune_with_exactly_the_reported_workspace(gpu_lib, n_seq, n_keys):
+    """tri_prune_window runs in exactly tri_workspace_size bytes (candidate
+    pass and full path; the candidate-capable cache and a small one), and
+    refuses one byte less or a start off the 256-byte grid, before any launch
+    (the destination stays untouched)."""
+    T = gpu_lib
+    B = 600
+    cfg = W.CONFIGS["tiny"].replace(head_dim=128, group=4, dtype=torch.bfloat16, theta=1e6, n_kv_heads=3, n_seq=n_seq,
+                                    n_keys=n_keys, t=n_keys + 1, budget=B, sigma=None, seed=59)
+    log(f"case exact workspace: {cfg.n_seg} segments x {n_keys} keys")
+    g = _to(W.dense_cache(cfg, "cpu"), "cuda")
+    calib, _ = calib_for(T, cfg)
+    desc = dense_desc(T, cfg, g)
+    need = T.tri_workspace_size(calib, desc, B)
+    assert need > 0
+    buf = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    off = (-buf.data_ptr()) % 256
+    ws = buf[off:off + need]
+    outs = []
+    for path in (T.TRI_PATH_FULL, T.TRI_PATH_CANDIDATES):
+        out = empty_like_dense(g, B)
+        T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), out["lengths"], ws, path=path)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for key in ("k", "v", "pos", "lengths"):
+        assert torch.equal(outs[0][key], outs[1][key]), f"exact workspace: {key} differs between paths"
+    untouched = empty_like_dense(g, B)
+    for bad in (buf[off:off + need - 1], buf[off + 1:off + 1 + need]):
+        with pytest.raises(T.TriError) as e:
+            T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, untouched), untouched["lengths"], bad)
+        assert e.value.code == T.TRI_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert int(untouched["lengths"].abs().sum()) == 0 and int((untouched["pos"] != -1).sum()) == 0
+
+
 def test_fallback_count_zero_without_candidate_mode(gpu_lib):
     """A pass that never enters candidate mode (fp32 here) reports zero
     fallbacks even on a workspace holding stale bytes."""
