@@ -174,6 +174,12 @@ def test_valid_calls_report_no_device():
     out = torch.zeros(1, 2, 4, 64)
     assert lib.tri_decode_attn(ctypes.byref(d), 4, T._p(q), 0.125, T._p(out), None) == T.TRI_ERR_NO_DEVICE
     assert lib.tri_decode_attn(ctypes.byref(d), 3, T._p(q), 0.125, T._p(out), None) == T.TRI_ERR_INVALID_ARG
+    assert lib.tri_decode_attn(ctypes.byref(d), 4, None, 0.125, T._p(out), None) == T.TRI_ERR_INVALID_ARG
+    assert lib.tri_decode_attn(ctypes.byref(d), 4, T._p(q), 0.125, None, None) == T.TRI_ERR_INVALID_ARG
+    assert lib.tri_decode_attn(ctypes.byref(d), 4, T._p(q), float("nan"), T._p(out), None) == T.TRI_ERR_INVALID_ARG
+    assert lib.tri_decode_attn(ctypes.byref(d), 4, T._p(q), float("inf"), T._p(out), None) == T.TRI_ERR_INVALID_ARG
+    # two KV heads x 16 query heads each: a group the kernels do not build
+    assert lib.tri_decode_attn(ctypes.byref(d), 32, T._p(q), 0.125, T._p(out), None) == T.TRI_ERR_UNSUPPORTED
 
 
 def test_calib_variant_validation():
