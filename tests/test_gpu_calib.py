@@ -40,7 +40,8 @@ def _run(T, q):
     return mag.cpu(), phase.cpu(), conc.cpu()
 
 
-@pytest.mark.parametrize("d,dtype,n", [(64, torch.float32, 300), (128, torch.bfloat16, 513), (64, torch.bfloat16, 7)])
+@pytest.mark.parametrize("d,dtype,n", [(64, torch.float32, 300), (128, torch.bfloat16, 513), (64, torch.bfloat16, 7),
+                                       (128, torch.float32, 1), (128, torch.float32, 64)])
 def test_calibrate_small_every_head(gpu_lib, d, dtype, n):
     """Every (layer, head); sample counts spanning chunk tails; a head with a
     zero band, a head of identical samples, a head of antipodal pairs."""
@@ -48,7 +49,7 @@ def test_calibrate_small_every_head(gpu_lib, d, dtype, n):
     cfg = W.CONFIGS["tiny"].replace(n_layers=2, n_kv_heads=2, group=4, head_dim=d, dtype=dtype, seed=3)
     log(f"case calibrate small d={d} {dtype} n={n}")
     q = W.query_samples(cfg, n)
-    q[0, :, 1] = q[0, 0, 1]                        # identical samples: R = 1
+    q[0, :, 1] = q[0, 0, 1].clone()                # identical samples: R = 1
     q[1, :, 2, 0] = 0.0                            # band 0 real part zero ...
     q[1, :, 2, d // 2] = 0.0                       # ... and imaginary part: a zero band
     half = (n // 2) * 2
