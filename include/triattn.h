@@ -212,7 +212,9 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
  * slot.  Only those keys are copied (at most lengths[s] - budget rows per
  * segment); segments with lengths[s] <= budget are not touched.  n_kept may
  * then be src->lengths itself.  Any other sharing of memory between src and
- * dst is TRI_ERR_INVALID_ARG.
+ * dst is TRI_ERR_INVALID_ARG.  dst must hold min(budget, src->capacity) rows
+ * per segment (else TRI_ERR_INVALID_ARG); a cache whose capacity is below
+ * the budget is copied through, or left as it is in place.
  */
 int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
                      const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,

@@ -494,7 +494,12 @@ static bool same_storage(const tri_cache_desc* s, const tri_cache_desc* d) {
 
 // src -> dst compaction arguments.  With `in_place` non-null, a dst that names
 // src's storage is accepted (and reported); any other sharing is an error.
-static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int budget, bool* in_place = nullptr) {
+// dst must hold `budget` rows per segment for tri_compact (its kept counts
+// come from the caller), and min(budget, src capacity) for a pruning pass,
+// which keeps at most that many (a cache smaller than the budget is copied
+// through, or left as it is in place).
+static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int budget, bool* in_place = nullptr,
+                      bool pruning = false) {
     int rc = check_cache(src);
     if (rc) return rc;
     if ((rc = check_cache(dst))) return rc;
@@ -502,7 +507,8 @@ static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int 
         src->n_seq != dst->n_seq || src->n_kv_heads != dst->n_kv_heads)
         return TRI_ERR_INVALID_ARG;
     if (budget < 1) return TRI_ERR_INVALID_ARG;
-    if (dst->capacity < budget) return TRI_ERR_INVALID_ARG;
+    const int64_t rows = pruning && src->capacity < budget ? src->capacity : budget;
+    if (dst->capacity < rows) return TRI_ERR_INVALID_ARG;
     if (in_place) *in_place = same_storage(src, dst);
     if (!(in_place && *in_place) &&
         (dst->k == src->k || dst->v == src->v || dst->pos == src->pos || dst->k == src->v || dst->v == src->k))
@@ -541,7 +547,7 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
                         tri_stream_t stream) {
     if (path != TRI_PATH_AUTO && path != TRI_PATH_FULL && path != TRI_PATH_CANDIDATES) return TRI_ERR_INVALID_ARG;
     bool in_place = false;
-    int rc = check_pair(src, dst, budget, &in_place);
+    int rc = check_pair(src, dst, budget, &in_place, true);
     if (rc) return rc;
     if ((rc = check_calib_vs_cache(calib, src))) return rc;
     if (!t || !n_kept) return TRI_ERR_INVALID_ARG;

@@ -653,6 +653,35 @@ def test_prune_with_exactly_the_reported_workspace(gpu_lib, n_seq, n_keys):
     assert int(untouched["lengths"].abs().sum()) == 0 and int((untouched["pos"] != -1).sum()) == 0
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_budget_above_capacity_copies_through(gpu_lib, dtype):
+    """A cache whose capacity (64) is below the budget (128): every segment is
+    copied through unchanged out of place (n_kept = lengths), and an in-place
+    pass leaves the cache as it was."""
+    T = gpu_lib
+    B, cap = 128, 64
+    cfg = W.CONFIGS["tiny"].replace(head_dim=64, group=2, dtype=dtype, n_kv_heads=2, n_seq=2, n_keys=cap, t=cap,
+                                    budget=B, seed=61)
+    log(f"case budget above capacity {dtype}")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([0, 1, 63, 64], dtype=torch.int32)
+    g = _to(cpu, "cuda")
+    calib, _ = calib_for(T, cfg)
+    desc = dense_desc(T, cfg, g)
+    ws = T.workspace(calib, desc, B)
+    out = empty_like_dense(g, B)
+    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), out["lengths"], ws)
+    T.tri_prune_window(calib, desc, g["t"], B, desc, g["lengths"], ws)       # in place: nothing to do
+    torch.cuda.synchronize()
+    assert torch.equal(out["lengths"].cpu(), cpu["lengths"])
+    for s in range(cfg.n_seg):
+        N = int(cpu["lengths"][s])
+        for key in ("k", "v", "pos"):
+            assert torch.equal(out[key][s, :N].cpu(), cpu[key][s, :N]), f"seg {s} {key} not copied through"
+    for key in ("k", "v", "pos", "lengths"):
+        assert torch.equal(g[key].cpu(), cpu[key]), f"in place: {key} changed"
+
+
 def test_fallback_count_zero_without_candidate_mode(gpu_lib):
     """A pass that never enters candidate mode (fp32 here) reports zero
     fallbacks even on a workspace holding stale bytes."""
