@@ -116,11 +116,12 @@ def test_candidate_select_36_keys_per_thread(gpu_lib):
     _dense_in_place(gpu_lib, cfg, cpu, B, "in place J36")
 
 
-def test_in_place_paged(gpu_lib):
+@pytest.mark.parametrize("page_size", [16, 24])
+def test_in_place_paged(gpu_lib, page_size):
     """A ragged paged pool (random page tables) pruned where it is."""
     T = gpu_lib
-    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=27)
-    log("case in place paged")
+    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=27, page_size=page_size)
+    log(f"case in place paged, {page_size}-token pages")
     pc = W.paged_cache(cfg, "cpu")
     g = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in pc.items()}
     calib, cal = calib_for(T, cfg)

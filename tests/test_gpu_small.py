@@ -144,10 +144,13 @@ def test_select_kernel_bit_exact(gpu_lib, cap):
         assert np.array_equal(idx[s, :len(ref)].numpy(), ref), f"cap {cap} seg {s} N {N}"
 
 
-def test_paged_small_every_step(gpu_lib):
+@pytest.mark.parametrize("page_size", [16, 8, 24, 64])
+def test_paged_small_every_step(gpu_lib, page_size):
+    """Ragged paged pool, every step against the oracle; page sizes other than
+    the 16 tokens of the workloads, one of them not a power of two."""
     T = gpu_lib
-    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=3)
-    log("case paged small")
+    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=3, page_size=page_size)
+    log(f"case paged small, {page_size}-token pages")
     pc = W.paged_cache(cfg, "cpu")
     g = _to(pc, "cuda")
     calib, cal = calib_for(T, cfg)
