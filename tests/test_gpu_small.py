@@ -387,13 +387,14 @@ def test_score_variants_every_step(gpu_lib, name):
     _check_all(cfg, cal, cpu, r, B, cpu["lengths"].numpy(), f"variant {name}", variant=orc_flag)
 
 
-def test_paged_decode_attention_over_pruned_pages(gpu_lib):
+@pytest.mark.parametrize("page_size", [16, 24, 8])
+def test_paged_decode_attention_over_pruned_pages(gpu_lib, page_size):
     """Decode attention reading a pruned paged cache in place (fresh pages with
     random page tables, per-KV-head kept counts) against the oracle."""
     import math
     T = gpu_lib
-    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=4)
-    log("case paged decode attention")
+    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=4, page_size=page_size)
+    log(f"case paged decode attention, {page_size}-token pages")
     pc = W.paged_cache(cfg, "cpu")
     g = _to(pc, "cuda")
     calib, cal = calib_for(T, cfg)
