@@ -144,13 +144,16 @@ def test_select_kernel_bit_exact(gpu_lib, cap):
         assert np.array_equal(idx[s, :len(ref)].numpy(), ref), f"cap {cap} seg {s} N {N}"
 
 
-@pytest.mark.parametrize("page_size", [16, 8, 24, 64])
-def test_paged_small_every_step(gpu_lib, page_size):
+@pytest.mark.parametrize("page_size,dtype", [(16, torch.bfloat16), (8, torch.bfloat16), (24, torch.bfloat16),
+                                             (64, torch.bfloat16), (16, torch.float32), (24, torch.float32)])
+def test_paged_small_every_step(gpu_lib, page_size, dtype):
     """Ragged paged pool, every step against the oracle; page sizes other than
-    the 16 tokens of the workloads, one of them not a power of two."""
+    the 16 tokens of the workloads (one of them not a power of two), bf16 and
+    fp32 pools."""
     T = gpu_lib
-    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=3, page_size=page_size)
-    log(f"case paged small, {page_size}-token pages")
+    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=3, page_size=page_size,
+                                      dtype=dtype)
+    log(f"case paged small, {page_size}-token pages, {dtype}")
     pc = W.paged_cache(cfg, "cpu")
     g = _to(pc, "cuda")
     calib, cal = calib_for(T, cfg)
