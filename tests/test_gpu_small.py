@@ -689,6 +689,46 @@ def test_budget_above_capacity_copies_through(gpu_lib, dtype):
         assert torch.equal(g[key].cpu(), cpu[key]), f"in place: {key} changed"
 
 
+def test_two_streams_two_workspaces(gpu_lib):
+    """Two caches pruned and attended on two streams at once, each call with
+    its own workspace, give the bytes the same calls give one after another on
+    the default stream."""
+    import math
+    T = gpu_lib
+    B, cap = 600, 12000
+    cfgs = [W.CONFIGS["tiny"].replace(head_dim=128, group=4, dtype=torch.bfloat16, theta=1e6, n_kv_heads=3, n_seq=3,
+                                      n_keys=cap, t=cap + 1, budget=B, sigma=None, seed=seed) for seed in (71, 72)]
+    log("case two streams")
+    cpus = [W.dense_cache(c, "cpu") for c in cfgs]
+    calib, _ = calib_for(T, cfgs[0])
+    q = torch.randn((1, 3, 12, 128), generator=torch.Generator().manual_seed(73)).to(torch.bfloat16).cuda()
+    scale = 1.0 / math.sqrt(128)
+
+    def run(streams):
+        res = []
+        for cfg, cpu, st in zip(cfgs, cpus, streams):
+            g = _to(cpu, "cuda")
+            desc = dense_desc(T, cfg, g)
+            ws = T.workspace(calib, desc, B)
+            out = empty_like_dense(g, B)
+            att = torch.empty((1, 3, 12, 128), device="cuda")
+            torch.cuda.synchronize()
+            T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), out["lengths"], ws, stream=st,
+                               path=T.TRI_PATH_CANDIDATES)
+            T.tri_decode_attn(dense_desc(T, cfg, out), 12, q, scale, att, stream=st)
+            res.append((out, att, g, ws))
+        torch.cuda.synchronize()
+        return [({k: v.cpu() for k, v in out.items()}, att.cpu()) for out, att, _, _ in res]
+
+    serial = run([None, None])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    concurrent = run([s1, s2])
+    for (o_a, a_a), (o_b, a_b) in zip(serial, concurrent):
+        for key in ("k", "v", "pos", "lengths"):
+            assert torch.equal(o_a[key], o_b[key]), f"two streams: {key} differs"
+        assert torch.equal(a_a, a_b), "two streams: attention differs"
+
+
 def test_fallback_count_zero_without_candidate_mode(gpu_lib):
     """A pass that never enters candidate mode (fp32 here) reports zero
     fallbacks even on a workspace holding stale bytes."""
