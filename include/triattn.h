@@ -27,10 +27,14 @@
  *    s = (l * n_seq + b) * n_kv_heads + h; query heads h*G .. h*G+G-1 share it.
  *  - Pointers marked "device" are device memory owned by the caller; pointers
  *    marked "host" are host memory read during the call.  The library never
- *    allocates per call; only tri_calib_load allocates (a small table it owns).
+ *    allocates per call; only tri_calib_load allocates (a small table it owns),
+ *    and the timing instrumentation, when enabled, creates HIP events once and
+ *    reuses them.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream).
- *    Return codes report host-side validation and launch errors only; on any
- *    error nothing is launched and outputs are untouched.
+ *    Return codes report host-side validation and launch errors only; on a
+ *    validation error nothing is launched and outputs are untouched (a launch
+ *    error part way through a multi-kernel call can leave earlier kernels'
+ *    writes behind).
  *  - Supported: head_dim 64 or 128, GQA group 1, 2, 4 or 8, bf16 or fp32
  *    storage, segments of at most 65536 keys, budget at most 8192.
  */
