@@ -58,17 +58,17 @@ def _load():
     lib.orc_score_segment.argtypes = [P, i32, P, i64, i32, dbl, i64, P, P, P, i32, P, i32, P, P, P]
     lib.orc_score_segment_variant.argtypes = [P, i32, P, i64, i32, dbl, i64, P, P, P, i32, P, i32, i32, P, P, P]
     lib.orc_zscore_max.argtypes = [P, i32, i64, P, P, P]
-    lib.orc_select_topb.argtypes = [P, i64, i64, P, P]
-    lib.orc_select_topb_f32.argtypes = [P, i64, i64, P, P]
+    lib.orc_select_topb.argtypes = [P, P, i64, i64, P, P]
+    lib.orc_select_topb_f32.argtypes = [P, P, i64, i64, P, P]
     lib.orc_gather_rows.argtypes = [P, i64, P, i64, P]
     lib.orc_paged_rows.argtypes = [P, i64, P, i32, i64, P]
-    lib.orc_inplace_layout.argtypes = [P, i64, i64, P]
+    lib.orc_fill_freed_layout.argtypes = [P, i64, i64, P]
     lib.orc_decode_attn.argtypes = [P, i32, P, P, i32, i64, i32, i32, dbl, P]
     lib.orc_calibrate.argtypes = [P, i32, i64, i32, P, P, P]
     for fn in (lib.orc_score_segment, lib.orc_zscore_max, lib.orc_select_topb,
                lib.orc_select_topb_f32, lib.orc_gather_rows, lib.orc_paged_rows,
                lib.orc_decode_attn, lib.orc_calibrate, lib.orc_score_segment_variant,
-               lib.orc_inplace_layout):
+               lib.orc_fill_freed_layout):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -129,18 +129,24 @@ def zscore_max(S):
     return mu, sigma, A
 
 
-def select_topb(A, B):
-    """Ascending kept slots.  A: fp64 or fp32 aggregated scores [N]."""
+def select_topb(A, B, pos=None):
+    """Ascending kept slots.  A: fp64 or fp32 aggregated scores [N]; pos: the
+    slots' positions [N] (ties at the cut go to the earlier position), or None
+    when slot order is position order."""
     lib = _load()
     A = np.ascontiguousarray(A)
     N = A.shape[0]
+    if pos is not None:
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        assert pos.shape == (N,)
     idx = np.empty(max(min(N, B), 1), dtype=np.int32)
     nk = ctypes.c_int64(0)
+    pp = _ptr(pos) if pos is not None else None
     if A.dtype == np.float32:
-        rc = lib.orc_select_topb_f32(_ptr(A), N, int(B), _ptr(idx), ctypes.byref(nk))
+        rc = lib.orc_select_topb_f32(_ptr(A), pp, N, int(B), _ptr(idx), ctypes.byref(nk))
     else:
         A = A.astype(np.float64, copy=False)
-        rc = lib.orc_select_topb(_ptr(A), N, int(B), _ptr(idx), ctypes.byref(nk))
+        rc = lib.orc_select_topb(_ptr(A), pp, N, int(B), _ptr(idx), ctypes.byref(nk))
     _check(rc, "select_topb")
     return idx[: nk.value].copy()
 
@@ -156,13 +162,14 @@ def gather_rows(src, idx):
     return dst
 
 
-def inplace_layout(kept, N):
-    """Slot arrangement of a segment pruned in place: entry j is the pre-prune
-    slot of the key now in slot j (kept slots below len(kept) stay put; the
-    kept slots above fill the freed ones in ascending order)."""
+def fill_freed_layout(kept, N):
+    """Slot arrangement of a segment pruned in place in the fill-freed-slots
+    mode: entry j is the pre-prune slot of the key now in slot j (kept slots
+    below len(kept) stay put; the kept slots above fill the freed ones in
+    ascending order)."""
     kept = np.ascontiguousarray(kept, dtype=np.int32)
     out = np.empty(len(kept), dtype=np.int32)
-    _check(_load().orc_inplace_layout(_ptr(kept), len(kept), int(N), _ptr(out)), "inplace_layout")
+    _check(_load().orc_fill_freed_layout(_ptr(kept), len(kept), int(N), _ptr(out)), "fill_freed_layout")
     return out
 
 
@@ -210,7 +217,7 @@ def prune_segment(K, V, pos, t, theta, M, phi, R, offsets, B, variant=0):
     """The whole path for one segment: scores, z/max, top-B, compaction."""
     S = score_segment(K, pos, t, theta, M, phi, R, offsets, variant=variant)
     mu, sigma, A = zscore_max(S)
-    idx = select_topb(A, B)
+    idx = select_topb(A, B, pos)
     return {
         "S": S, "mu": mu, "sigma": sigma, "A": A, "idx": idx,
         "K": gather_rows(K, idx), "V": gather_rows(V, idx),
@@ -218,11 +225,24 @@ def prune_segment(K, V, pos, t, theta, M, phi, R, offsets, B, variant=0):
     }
 
 
+def host_threads() -> int:
+    """Threads the oracle runs on: the process's CPU share, which is
+    OMP_NUM_THREADS where the host sets one (the cores a job is given on a
+    shared machine), else every core the process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
 def run_parallel(fn, items, threads=None):
     """Map fn over independent items on a thread pool (the C calls release the GIL)."""
     items = list(items)
     if threads is None:
-        threads = min(len(items), os.cpu_count() or 1, 16) or 1
+        threads = min(len(items), host_threads()) or 1
     if threads <= 1:
         return [fn(x) for x in items]
     with ThreadPoolExecutor(max_workers=threads) as ex:

@@ -185,15 +185,18 @@ int orc_zscore_max(const double* S, int G, int64_t N, double* mu, double* sigma,
 
 typedef struct {
     double a;
+    int32_t pos;
     int32_t slot;
 } ranked_key;
 
-/* Higher aggregated score first; among equal scores the lower slot first. */
-static int by_score_then_slot(const void* x, const void* y) {
+/* Higher aggregated score first; among equal scores the earlier position
+ * first, and among equal positions the lower slot. */
+static int by_score_then_position(const void* x, const void* y) {
     const ranked_key* p = (const ranked_key*)x;
     const ranked_key* q = (const ranked_key*)y;
     if (p->a > q->a) return -1;
     if (p->a < q->a) return 1;
+    if (p->pos != q->pos) return p->pos < q->pos ? -1 : 1;
     return (p->slot > q->slot) - (p->slot < q->slot);
 }
 
@@ -205,11 +208,14 @@ static int ascending_i32(const void* x, const void* y) {
 /*
  * Budgeted selection ([YY] 主要方法, paragraph on windowed batch pruning): when
  * the segment holds more than B keys keep only the B best by aggregated score;
- * otherwise keep everything.  Reading: ties at the cut go to the lower slot
- * (earlier key); the kept slots are returned in ascending order.
+ * otherwise keep everything.  Reading: among keys whose scores tie at the cut,
+ * the earlier position (the key generated first) is kept; keys that share a
+ * position as well go by lower slot.  pos: [N] positions of the slots, or
+ * NULL when slot order is position order.  The kept slots are returned in
+ * ascending order.
  * A: [N]; idx: [min(N,B)] output; *n_kept = min(N, B).
  */
-int orc_select_topb(const double* A, int64_t N, int64_t B, int32_t* idx, int64_t* n_kept) {
+int orc_select_topb(const double* A, const int32_t* pos, int64_t N, int64_t B, int32_t* idx, int64_t* n_kept) {
     if (B <= 0 || N < 0) return -1;
     if (N <= B) {
         for (int64_t i = 0; i < N; ++i) idx[i] = (int32_t)i;
@@ -220,9 +226,10 @@ int orc_select_topb(const double* A, int64_t N, int64_t B, int32_t* idx, int64_t
     if (!r) return -1;
     for (int64_t i = 0; i < N; ++i) {
         r[i].a = A[i];
+        r[i].pos = pos ? pos[i] : (int32_t)i;
         r[i].slot = (int32_t)i;
     }
-    qsort(r, (size_t)N, sizeof(ranked_key), by_score_then_slot);
+    qsort(r, (size_t)N, sizeof(ranked_key), by_score_then_position);
     for (int64_t j = 0; j < B; ++j) idx[j] = r[j].slot;
     qsort(idx, (size_t)B, sizeof(int32_t), ascending_i32);
     free(r);
@@ -232,12 +239,12 @@ int orc_select_topb(const double* A, int64_t N, int64_t B, int32_t* idx, int64_t
 
 /* Same selection on single-precision scores (widened exactly to double, so
  * -0 and +0 compare equal, as IEEE comparison has them). */
-int orc_select_topb_f32(const float* A, int64_t N, int64_t B, int32_t* idx, int64_t* n_kept) {
+int orc_select_topb_f32(const float* A, const int32_t* pos, int64_t N, int64_t B, int32_t* idx, int64_t* n_kept) {
     if (N < 0) return -1;
     double* a = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
     if (!a) return -1;
     for (int64_t i = 0; i < N; ++i) a[i] = (double)A[i];
-    const int rc = orc_select_topb(a, N, B, idx, n_kept);
+    const int rc = orc_select_topb(a, pos, N, B, idx, n_kept);
     free(a);
     return rc;
 }
@@ -252,18 +259,20 @@ int orc_gather_rows(const void* src, int64_t row_bytes, const int32_t* idx, int6
 }
 
 /*
- * Layout of a segment pruned in place.  The pages fix which keys survive a
- * prune ([YY] 主要方法: keep the top-B keys) but not where they sit afterwards;
- * attention and later prunes read each key with its stored position, so any
- * arrangement of the kept rows in slots [0, n_kept) is a valid cache.  Reading
- * taken for the in-place prune: a kept key already below n_kept stays in its
- * slot, and the kept keys at or above n_kept fill the freed slots below
- * n_kept, the lowest such key going to the lowest freed slot, and so on.
+ * Arrangement of a segment pruned in place in the "fill freed slots" mode, a
+ * mode a caller asks for explicitly.  The pages fix which keys survive a prune
+ * ([YY] 主要方法: keep the top-B keys), not where they sit afterwards; attention
+ * and later prunes read each key with its stored position, so any arrangement
+ * of the kept rows in slots [0, n_kept) is a valid cache.  The default
+ * arrangement, in place or not, is slot order (the gather above).  In this
+ * mode a kept key already below n_kept stays in its slot, and the kept keys at
+ * or above n_kept fill the freed slots below n_kept, the lowest such key
+ * going to the lowest freed slot, and so on.
  * kept: the kept slots in ascending order, n of them, all < N.
  * src_of: [n] output; slot j of the pruned segment holds the key that was in
  * slot src_of[j] before the prune.
  */
-int orc_inplace_layout(const int32_t* kept, int64_t n, int64_t N, int32_t* src_of) {
+int orc_fill_freed_layout(const int32_t* kept, int64_t n, int64_t N, int32_t* src_of) {
     if (n < 0 || n > N) return -1;
     for (int64_t i = 0; i < n; ++i)
         if (kept[i] < 0 || kept[i] >= N || (i > 0 && kept[i] <= kept[i - 1])) return -1;

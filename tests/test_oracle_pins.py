@@ -11,9 +11,12 @@ never against the oracle itself.
   maps; G = 1.
 * Top-B against a brute-force rank count on tiny inputs with ties.
 * Gather, paged read-out and decode attention against numpy / torch.
-* In-place layout: hand-worked cases (tests/golden/inplace_layout.json), a
-  brute-force search over every arrangement of tiny kept sets for the one
-  that obeys the layout's two rules, and invariants on large kept sets.
+* Top-B ties at the cut: the earlier position wins, on caches whose slots
+  are not in position order, by the same brute-force rank count.
+* Fill-freed-slots layout (the optional in-place arrangement): hand-worked
+  cases (tests/golden/fill_freed_layout.json), a brute-force search over
+  every arrangement of tiny kept sets for the one that obeys the layout's two
+  rules, and invariants on large kept sets.
 """
 import json
 import math
@@ -182,6 +185,16 @@ def test_zscore_constant_head_gives_zero():
 
 
 # ---------------------------------------------------------------- selection
+def _brute_kept(A, B, pos=None):
+    """Key i is kept iff fewer than B keys rank above it: a higher score, or
+    the same score at an earlier position (the same position: a lower slot)."""
+    N = len(A)
+    p = list(range(N)) if pos is None else [int(x) for x in pos]
+    return [i for i in range(N)
+            if sum(1 for j in range(N)
+                   if A[j] > A[i] or (A[j] == A[i] and (p[j], j) < (p[i], i))) < B]
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_select_matches_brute_force_rank(seed):
     rng = np.random.default_rng(seed)
@@ -191,15 +204,41 @@ def test_select_matches_brute_force_rank(seed):
     if seed % 3 == 0:
         A = rng.normal(size=N)
     idx = oracle.select_topb(A, B)
-    kept = [i for i in range(N)
-            if sum(1 for j in range(N) if A[j] > A[i] or (A[j] == A[i] and j < i)) < B]
-    assert list(idx) == kept
+    assert list(idx) == _brute_kept(A, B)
     assert len(idx) == min(N, B)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_select_ties_go_to_the_earlier_position(seed):
+    """Positions scrambled across slots (a cache whose slots are not in
+    position order): among tied scores the earliest positions are kept, not
+    the lowest slots; repeated positions fall back to the lower slot."""
+    rng = np.random.default_rng(100 + seed)
+    N = int(rng.integers(2, 65))
+    B = int(rng.integers(1, N))
+    A = rng.integers(-2, 3, size=N).astype(np.float64)            # heavy ties
+    pos = rng.permutation(N * 3)[:N].astype(np.int32)
+    if seed % 4 == 3:
+        pos = rng.integers(0, 6, size=N).astype(np.int32)          # repeated positions
+    idx = oracle.select_topb(A, B, pos)
+    assert list(idx) == _brute_kept(A, B, pos)
+    assert list(oracle.select_topb(A.astype(np.float32), B, pos)) == list(idx)
+
+
+def test_select_tie_rule_hand_case():
+    """Four keys tie at the cut with slots in reverse position order: the two
+    earliest positions (slots 3 and 2) survive, where slot order would keep 0
+    and 1."""
+    A = np.array([1.0, 1.0, 1.0, 1.0, 5.0])
+    pos = np.array([40, 30, 20, 10, 0], dtype=np.int32)
+    assert list(oracle.select_topb(A, 3, pos)) == [2, 3, 4]
+    assert list(oracle.select_topb(A, 3)) == [0, 1, 4]
 
 
 def test_select_f32_signed_zero_and_budget_at_least_n():
     A = np.array([0.0, -0.0, 1.0, -0.0, 0.0], dtype=np.float32)
     assert list(oracle.select_topb(A, 3)) == [0, 1, 2]
+    assert list(oracle.select_topb(A, 3, np.array([9, 8, 7, 1, 2], dtype=np.int32))) == [2, 3, 4]
     assert list(oracle.select_topb(np.array([3.0, 1.0, 2.0]), 3)) == [0, 1, 2]
     assert list(oracle.select_topb(np.array([3.0, 1.0, 2.0]), 10)) == [0, 1, 2]
     assert len(oracle.select_topb(np.zeros(0), 4)) == 0
@@ -384,15 +423,15 @@ def test_variant_flags_are_checked():
         oracle.score_segment(K, pos, 5100, 1e4, M, phi, R, [1], variant=16)
 
 
-# ---------------------------------------------------------------- in-place layout
-def test_inplace_layout_hand_cases():
-    cases = json.load(open(os.path.join(GOLDEN, "inplace_layout.json")))["cases"]
+# ---------------------------------------------------------------- fill-freed-slots layout
+def test_fill_freed_layout_hand_cases():
+    cases = json.load(open(os.path.join(GOLDEN, "fill_freed_layout.json")))["cases"]
     for c in cases:
-        got = oracle.inplace_layout(c["kept"], c["N"])
+        got = oracle.fill_freed_layout(c["kept"], c["N"])
         assert got.tolist() == c["src_of"], c["why"]
 
 
-def _brute_inplace(kept, N):
+def _brute_fill_freed(kept, N):
     """Every arrangement of the kept keys over slots [0, n), filtered by the two
     rules: a kept key below n keeps its slot, and the keys that move land in
     freed slots in the same order as their old slots.  Exactly one survives."""
@@ -409,20 +448,20 @@ def _brute_inplace(kept, N):
     return found[0]
 
 
-def test_inplace_layout_brute_force_tiny():
+def test_fill_freed_layout_brute_force_tiny():
     import itertools
     for N in range(1, 8):
         for n in range(0, N + 1):
             for kept in itertools.combinations(range(N), n):
-                got = oracle.inplace_layout(list(kept), N).tolist()
-                assert got == _brute_inplace(list(kept), N), (kept, N)
+                got = oracle.fill_freed_layout(list(kept), N).tolist()
+                assert got == _brute_fill_freed(list(kept), N), (kept, N)
 
 
-def test_inplace_layout_invariants():
+def test_fill_freed_layout_invariants():
     rng = np.random.default_rng(11)
     for N, n in [(1152, 1024), (32768, 2048), (5000, 4096), (300, 1)]:
         kept = np.sort(rng.choice(N, size=n, replace=False)).astype(np.int32)
-        src_of = oracle.inplace_layout(kept, N)
+        src_of = oracle.fill_freed_layout(kept, N)
         assert np.array_equal(np.sort(src_of), kept)             # the same keys, each once
         stay = kept[kept < n]
         assert np.array_equal(src_of[stay], stay)                 # kept keys below n do not move
@@ -431,8 +470,8 @@ def test_inplace_layout_invariants():
         assert np.all(src_of[moved] >= n) and np.all(np.diff(src_of[moved]) > 0)
 
 
-def test_inplace_layout_rejects_bad_lists():
+def test_fill_freed_layout_rejects_bad_lists():
     with pytest.raises(ValueError):
-        oracle.inplace_layout([3, 1], 5)                          # not ascending
+        oracle.fill_freed_layout([3, 1], 5)                          # not ascending
     with pytest.raises(ValueError):
-        oracle.inplace_layout([0, 5], 5)                          # slot out of range
+        oracle.fill_freed_layout([0, 5], 5)                          # slot out of range
