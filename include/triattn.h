@@ -17,7 +17,8 @@
  * geometric offset set, plus a norm term that grows where the band is not
  * concentrated), z-scored inside each query head, max-aggregated over the GQA
  * group, and when a segment holds more than B keys only the B best survive
- * (ties to the earlier slot) and K/V/positions are compacted in slot order.
+ * (ties at the cut to the earlier position) and K/V/positions are compacted in
+ * slot order.
  *
  * Conventions shared by every entry point
  *  - Rotary layout: half-split pairing.  Band f of a row x is x[f] + i x[f+F],
@@ -183,13 +184,21 @@ int tri_score(tri_calib_t calib, const tri_cache_desc* kv, const int32_t* t, flo
  *   agg     : device fp32 [n_seg][capacity] aggregated scores.
  *   lengths : device int32 [n_seg].
  *   idx     : device int32 [n_seg][budget]; row s receives the kept slots in
- *             ascending order: the budget largest scores, ties at the cut to
- *             the lower slot (-0 and +0 are equal); all slots when
- *             lengths[s] <= budget.
+ *             ascending order: the budget largest scores (-0 and +0 are
+ *             equal); all slots when lengths[s] <= budget.
  *   n_kept  : device int32 [n_seg], min(lengths[s], budget).
+ * Keys tied at the cut: the earlier position is kept.  tri_select_topb has no
+ * positions and takes slot order as position order (true of every cache this
+ * library appends to and prunes, which stay in position order); the lower
+ * slot wins.  tri_select_topb_ex takes the slots' positions, pos: device
+ * int32 [n_seg][capacity] (NULL: as tri_select_topb); keys that tie at the
+ * cut in score and position as well go by lower slot.  ws and ws_bytes are
+ * not used (may be NULL, 0).
  */
 int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int capacity, int budget,
                     int32_t* idx, int32_t* n_kept, void* ws, size_t ws_bytes, tri_stream_t stream);
+int tri_select_topb_ex(const float* agg, const int32_t* pos, const int32_t* lengths, int n_seg, int capacity,
+                       int budget, int32_t* idx, int32_t* n_kept, void* ws, size_t ws_bytes, tri_stream_t stream);
 
 /*
  * Compaction: for each segment, dst slot j <- src slot idx[s][j] for
@@ -208,17 +217,20 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
  * with lengths[s] <= budget are copied through unchanged, so dst is always a
  * complete cache; n_kept (device int32 [n_seg]) gets min(lengths[s], budget).
  *
+ * Keys tied at the cut keep the earlier position (read from the cache's
+ * positions; equal positions go by lower slot), so the kept set does not
+ * depend on how the cache's slots are arranged.
+ *
  * In place: when dst names src's storage (same k, v, pos, layout, capacity,
  * layer0 and, if paged, the same page table), the cache is pruned where it
- * is.  The kept set is the same; the arrangement is not slot order: a kept
- * key already below n_kept[s] stays in its slot, and the kept keys at or
- * above it move into the freed slots below, lowest key into lowest freed
- * slot.  Only those keys are copied (at most lengths[s] - budget rows per
- * segment); segments with lengths[s] <= budget are not touched.  n_kept may
- * then be src->lengths itself.  Any other sharing of memory between src and
- * dst is TRI_ERR_INVALID_ARG.  dst must hold min(budget, src->capacity) rows
- * per segment (else TRI_ERR_INVALID_ARG); a cache whose capacity is below
- * the budget is copied through, or left as it is in place.
+ * is, with the same result as out of place: the kept rows end up in slots
+ * 0..n_kept[s]-1 in their old slot order.  Rows before the first dropped slot
+ * stay where they are and are not copied; every later kept row moves down.
+ * Segments with lengths[s] <= budget are not touched.  n_kept may then be
+ * src->lengths itself.  Any other sharing of memory between src and dst is
+ * TRI_ERR_INVALID_ARG.  dst must hold min(budget, src->capacity) rows per
+ * segment (else TRI_ERR_INVALID_ARG); a cache whose capacity is below the
+ * budget is copied through, or left as it is in place.
  */
 int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
                      const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes,
@@ -242,6 +254,16 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
  * TRI_PATH_CANDIDATES (the candidate pass whenever the cache allows it,
  * whatever its segment count).  Any other value is TRI_ERR_INVALID_ARG.
  *
+ * TRI_INPLACE_FILL_FREED, or'ed into path, changes only the arrangement an
+ * in-place prune leaves (no effect out of place): a kept key already below
+ * n_kept[s] stays in its slot, and the kept keys at or above it move into the
+ * freed slots below, lowest key into lowest freed slot.  Fewer rows move (at
+ * most lengths[s] - budget per segment, against every kept row after the
+ * first dropped slot), but slot order no longer follows position order, so
+ * a later tri_select_topb (which has no positions) would break ties by a
+ * different order; tri_prune_window itself reads positions and keeps the
+ * same set either way.
+ *
  * tri_prune_fallbacks: number of segments the last tri_prune_window on this
  * workspace had to redo in full (host int32 *count; 0 after a full-score
  * pass).  Synchronises `stream`.
@@ -249,6 +271,7 @@ int tri_prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t
 #define TRI_PATH_AUTO 0
 #define TRI_PATH_FULL 1
 #define TRI_PATH_CANDIDATES 2
+#define TRI_INPLACE_FILL_FREED 16
 int tri_prune_window_ex(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
                         const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes, int path,
                         tri_stream_t stream);

@@ -462,6 +462,11 @@ int tri_score(tri_calib_t calib, const tri_cache_desc* kv, const int32_t* t, flo
 
 int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int capacity, int budget,
                     int32_t* idx, int32_t* n_kept, void* ws, size_t ws_bytes, tri_stream_t stream) {
+    return tri_select_topb_ex(agg, nullptr, lengths, n_seg, capacity, budget, idx, n_kept, ws, ws_bytes, stream);
+}
+
+int tri_select_topb_ex(const float* agg, const int32_t* pos, const int32_t* lengths, int n_seg, int capacity,
+                       int budget, int32_t* idx, int32_t* n_kept, void* ws, size_t ws_bytes, tri_stream_t stream) {
     (void)ws;
     (void)ws_bytes;
     if (!agg || !lengths || !idx || n_seg < 0 || capacity < 1 || budget < 1) return TRI_ERR_INVALID_ARG;
@@ -478,6 +483,9 @@ int tri_select_topb(const float* agg, const int32_t* lengths, int n_seg, int cap
     a.idx_stride = budget;
     a.n_kept = n_kept;
     a.gather = 0;
+    a.tie = pos ? TIE_POS_ARRAY : TIE_SLOT;
+    a.tie_pos = pos;
+    a.tie_stride = capacity;
     a.n_seg = n_seg;
     a.cap = capacity;
     return hip_status(launch_select(a, 0, SELECT_A, capacity, static_cast<hipStream_t>(stream)), "select kernel");
@@ -545,6 +553,8 @@ constexpr int64_t kCandidateMinSegs = 256;
 static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
                         const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes, int path,
                         tri_stream_t stream) {
+    const bool fill = (path & TRI_INPLACE_FILL_FREED) != 0;
+    path &= ~TRI_INPLACE_FILL_FREED;
     if (path != TRI_PATH_AUTO && path != TRI_PATH_FULL && path != TRI_PATH_CANDIDATES) return TRI_ERR_INVALID_ARG;
     bool in_place = false;
     int rc = check_pair(src, dst, budget, &in_place, true);
@@ -584,7 +594,8 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
     a.budget = budget;
     a.n_kept = n_kept;
     const bool split = !in_place && split_gather(src);
-    a.gather = in_place ? GATHER_IN_PLACE : split ? GATHER_NONE : GATHER_COPY;
+    a.gather = in_place ? (fill ? GATHER_IN_PLACE_FILL : GATHER_IN_PLACE) : split ? GATHER_NONE : GATHER_COPY;
+    a.tie = TIE_POS_CACHE;
     a.src = view_of(src);
     a.dst = out_of(dst);
     a.row_bytes = src->head_dim * elem_size(src->dtype);

@@ -139,16 +139,28 @@ struct SelectArgs {
     int64_t idx_stride;
     int32_t* n_kept;        // optional [n_seg]
     int32_t gather;         // GatherMode
+    int32_t tie;            // TieMode: how keys tied at the cut are ordered
+    const int32_t* tie_pos; // TIE_POS_ARRAY: positions [n_seg][tie_stride]
+    int64_t tie_stride;
     CacheView src;
     CacheOut dst;
     int32_t row_bytes;
     int32_t n_seg;
 };
 // GATHER_COPY: kept row j of each segment -> dst slot j (dst is another cache).
-// GATHER_IN_PLACE: dst is src; kept rows below n_kept stay, the kept rows at or
-// above n_kept move into the freed slots below it, in ascending order (reads
-// only from slots >= n_kept, writes only to slots < n_kept: no overlap).
-enum GatherMode : int { GATHER_NONE = 0, GATHER_COPY = 1, GATHER_IN_PLACE = 2 };
+// GATHER_IN_PLACE: dst is src; kept row j -> slot j as in GATHER_COPY (slot
+// order kept).  kept[j] >= j, so rows move down only; the rows before the
+// first freed slot stay, and the rest move in batches: each batch reads all
+// its rows, then (after a barrier) writes them, and later batches read only
+// slots at or above what earlier ones wrote.
+// GATHER_IN_PLACE_FILL: dst is src; kept rows below n_kept stay, the kept rows
+// at or above n_kept move into the freed slots below it, in ascending order
+// (reads only from slots >= n_kept, writes only to slots < n_kept: no overlap).
+enum GatherMode : int { GATHER_NONE = 0, GATHER_COPY = 1, GATHER_IN_PLACE = 2, GATHER_IN_PLACE_FILL = 3 };
+// Order among keys tied at the cut: the lower slot (TIE_SLOT), or the earlier
+// position, then the lower slot; positions from tie_pos (TIE_POS_ARRAY) or
+// from the source cache (TIE_POS_CACHE).
+enum TieMode : int { TIE_SLOT = 0, TIE_POS_ARRAY = 1, TIE_POS_CACHE = 2 };
 // mode A: select on aggregated scores (group 0); S: on interleaved scores;
 // C: on candidate lists, with the certificate and fallback list; S_FALLBACK:
 // mode S over the segments listed in fb_list.

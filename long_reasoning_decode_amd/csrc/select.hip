@@ -5,14 +5,18 @@
 // segment holds the segment's aggregated scores in registers as order-preserving
 // 32-bit keys, finds the exact B-th largest key T with an MSB-first radix select
 // (11 + 11 + 10 bit digits, 2048-bin LDS histograms, one block scan per digit),
-// then keeps every key > T and the lowest-slot keys equal to T.  The kept slots
-// are emitted in ascending order from wave ballots plus one block scan over
-// (register index, wave) counts, so the result is identical run to run.
+// then keeps every key > T and, of the keys equal to T, those at the earliest
+// positions (a second radix select over their positions, run only when more
+// keys tie at T than fit; equal positions, and callers without positions, go
+// by lower slot).  The kept slots are emitted in ascending order from wave
+// ballots plus one block scan over (register index, wave) counts, so the
+// result is identical run to run.
 //
 // In gather mode the same workgroup then copies the kept K/V rows and positions
 // (bit-exact, slot order) into the destination cache: the fused pruning pass.
-// In place, only the kept rows at or above the kept count move, into the slots
-// freed below it.
+// In place, the kept rows move down to their slot-order slots in batches; or,
+// in the fill mode, only the kept rows at or above the kept count move, into
+// the slots freed below it.
 #include "launch.h"
 #include "stats.h"
 
@@ -194,6 +198,80 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
     return nc;
 }
 
+// MSB-first radix select over the block's register entries (entry j of a
+// thread: key[j], entry number j * 1024 + tid).  Among the entries below nv
+// (and, with use_sel, whose bit j of sel is set), finds the need-th largest
+// key: 11 + 11 + 10 bit digits, one 2048-bin LDS histogram and one block scan
+// per digit.  On return T is that key, need the number of entries equal to T
+// that rank within the first `need` (entries > T plus that many entries == T
+// make up the original need), and n_eq the number of such entries equal to T.
+template <int J>
+__device__ __forceinline__ void radix_select(const uint32_t (&key)[J], int nv, uint64_t sel, bool use_sel,
+                                             int& need, uint32_t& T, uint32_t& n_eq, uint32_t* hist,
+                                             uint32_t* wsum, uint32_t* pick) {
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+        const uint32_t dmask = pass < 2 ? 0x7ffu : 0x3ffu;
+        hist[tid] = 0u;
+        hist[tid + kSelThreads] = 0u;
+        if (tid == 0) {
+            pick[0] = 0u;
+            pick[1] = 0u;
+            pick[2] = 0u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const bool in = j * kSelThreads + tid < nv && (!use_sel || ((sel >> j) & 1u));
+            if (in && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        // Thread t owns bins 2047-2t and 2046-2t: a scan in thread order is a
+        // cumulative count from the top bin down.
+        const int b0 = 2047 - 2 * tid, b1 = b0 - 1;
+        const uint32_t h0 = hist[b0], h1 = hist[b1];
+        const uint32_t incl = block_incl_scan(h0 + h1, wsum);
+        const uint32_t above0 = incl - (h0 + h1);
+        const uint32_t above1 = above0 + h0;
+        const uint32_t un = (uint32_t)need;
+        if (above0 < un && above0 + h0 >= un) {
+            pick[0] = (uint32_t)b0;
+            pick[1] = above0;
+            pick[2] = h0;
+        } else if (above1 < un && above1 + h1 >= un) {
+            pick[0] = (uint32_t)b1;
+            pick[1] = above1;
+            pick[2] = h1;
+        }
+        __syncthreads();
+        prefix |= pick[0] << shift;
+        pmask |= dmask << shift;
+        need -= (int)pick[1];
+        n_eq = pick[2];
+        __syncthreads();
+    }
+    T = prefix;
+}
+
+// Slot of candidate entry n of a segment of N keys (mode C: entry n is the
+// n-th candidate key in slot order).
+__device__ __forceinline__ int cand_slot(int n, int N, const uint32_t* pre, const uint32_t* mw) {
+    int b, q;
+    cand_block(n, (N + 31) / 32, pre, b, q);
+    return 32 * b + nth_bit(mw[b], q);
+}
+
+// Instances built for 8 waves per SIMD (at most 64 VGPRs), so two workgroups
+// share a CU and one's gather overlaps the other's select phase.
+constexpr bool select_low_regs(int J, int G) { return (J <= 16 && G <= 4) || (J <= 2 && G == 8); }
+
+// Orderable key of a position for the tie rule: an earlier (smaller, signed)
+// position gives a larger key.
+__device__ __forceinline__ uint32_t pos_order_key(int32_t p) { return ~((uint32_t)p ^ 0x80000000u); }
+
 // Top-B of segment s.  MODE: SELECT_A reads aggregated scores, SELECT_S the
 // interleaved per-head scores and chunk statistics, SELECT_C the candidate
 // lists.  In mode C the result stands only if it provably equals mode S's: an
@@ -207,13 +285,14 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
 template <int J, int G, int MODE>
 __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s) {
     constexpr bool CAND = MODE == SELECT_C;
+    constexpr bool LOW_REGS = select_low_regs(J, G);
     // mode C holds at most J*1024 >= N/2 candidates (launch_select), so a segment
     // has at most 64 J blocks of 32 keys (and at most 2048, N <= 65536)
     constexpr int NB = CAND ? (64 * J < 2048 ? 64 * J : 2048) : 1;
     constexpr int GZ = G > 0 ? G : 1;
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t wsum[kSelWaves];
-    __shared__ uint32_t pick[2];
+    __shared__ uint32_t pick[3];
     __shared__ uint32_t cnt_gt[J * kSelWaves], cnt_eq[J * kSelWaves];
     __shared__ int32_t kept[kMaxBudget];
     __shared__ double scratch[(kSelWaves + 1) * GZ];
@@ -229,7 +308,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
     uint32_t key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) key[j] = 0u;
-    uint32_t T = 0u;
+    uint32_t T = 0u, n_eq = 0u;
     int need = 0;
     int nv = N;                                         // register entries, in slot order
 
@@ -299,47 +378,8 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         }
 
         // ---- radix select of the B-th largest key
-        uint32_t prefix = 0u, pmask = 0u;
         need = B;
-#pragma unroll
-        for (int pass = 0; pass < 3; ++pass) {
-            const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-            const uint32_t dmask = pass < 2 ? 0x7ffu : 0x3ffu;
-            hist[tid] = 0u;
-            hist[tid + kSelThreads] = 0u;
-            if (tid == 0) {
-                pick[0] = 0u;
-                pick[1] = 0u;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int n = j * kSelThreads + tid;
-                if (n < nv && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
-            }
-            __syncthreads();
-            // Thread t owns bins 2047-2t and 2046-2t: a scan in thread order is a
-            // cumulative count from the top bin down.
-            const int b0 = 2047 - 2 * tid, b1 = b0 - 1;
-            const uint32_t h0 = hist[b0], h1 = hist[b1];
-            const uint32_t incl = block_incl_scan(h0 + h1, wsum);
-            const uint32_t above0 = incl - (h0 + h1);
-            const uint32_t above1 = above0 + h0;
-            const uint32_t un = (uint32_t)need;
-            if (above0 < un && above0 + h0 >= un) {
-                pick[0] = (uint32_t)b0;
-                pick[1] = above0;
-            } else if (above1 < un && above1 + h1 >= un) {
-                pick[0] = (uint32_t)b1;
-                pick[1] = above1;
-            }
-            __syncthreads();
-            prefix |= pick[0] << shift;
-            pmask |= dmask << shift;
-            need -= (int)pick[1];
-            __syncthreads();
-        }
-        T = prefix;
+        radix_select<J>(key, nv, 0ull, false, need, T, n_eq, hist, wsum, pick);
 
         if constexpr (CAND) {
             if (nv < N) {                               // certificate for the keys left out
@@ -354,14 +394,46 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         }
     }
 
+    // ---- ties at the cut: when more keys equal T than fit, the earliest
+    // positions among them are kept.  Their register entries (bit j of eqm)
+    // are overwritten with the order keys of their positions (earlier = larger)
+    // and a second radix select finds the position cut P: tied keys above it
+    // are kept, and of those at it (a shared position) the lowest slots.
+    const bool by_pos = !all && a.tie != TIE_SLOT && (int)n_eq > need;   // block-uniform
+    uint64_t eqm = 0ull;
+    uint32_t P = 0u;
+    if (by_pos) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int n = j * kSelThreads + tid;
+            if (n < nv && key[j] == T) {
+                int slot = n;
+                if constexpr (CAND) slot = cand_slot(n, N, pre, mw);
+                const int32_t p = a.tie == TIE_POS_ARRAY ? a.tie_pos[(int64_t)s * a.tie_stride + slot]
+                                                         : a.src.pos[a.src.row(s, slot)];
+                key[j] = pos_order_key(p);
+                eqm |= 1ull << j;
+            }
+        }
+        uint32_t n_eq2 = 0u;
+        radix_select<J>(key, nv, eqm, true, need, P, n_eq2, hist, wsum, pick);
+    }
+#define TRI_CLASSIFY(j, gt, eq)                                             \
+    const bool valid_##j = (j) * kSelThreads + tid < nv;                    \
+    bool gt, eq;                                                            \
+    if (by_pos && ((eqm >> (j)) & 1u)) {                                    \
+        gt = key[j] > P;                                                    \
+        eq = key[j] == P;                                                   \
+    } else {                                                                \
+        gt = valid_##j && (all || key[j] > T);                              \
+        eq = valid_##j && !all && !by_pos && key[j] == T;                   \
+    }
+
     // ---- ordered emission: entry k = j*1024 + w*64 + lane, in (j, w, lane) order
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const int n = j * kSelThreads + tid;
-        const bool valid = n < nv;
-        const bool gt = valid && (all || key[j] > T);
-        const bool eq = valid && !all && key[j] == T;
+        TRI_CLASSIFY(j, gt, eq)
         const uint64_t bg = __ballot(gt), be = __ballot(eq);
         if (lane == 0) {
             cnt_gt[j * kSelWaves + w] = (uint32_t)__popcll(bg);
@@ -383,27 +455,21 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
     const int nk = min(N, B);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-        const int n = j * kSelThreads + tid;
-        const bool valid = n < nv;
-        const bool gt = valid && (all || key[j] > T);
-        const bool eq = valid && !all && key[j] == T;
+        TRI_CLASSIFY(j, gt, eq)
         const uint64_t bg = __ballot(gt), be = __ballot(eq);
         const int eb = (int)cnt_eq[j * kSelWaves + w] + __popcll(be & below);
         const int gb = (int)cnt_gt[j * kSelWaves + w] + __popcll(bg & below);
         const int out = gb + min(eb, need);
         if ((gt || (eq && eb < need)) && out < nk) {
-            int slot = n;
+            int slot = j * kSelThreads + tid;
             if constexpr (CAND) {
-                if (!all) {                             // candidate n -> its slot
-                    int b, q;
-                    cand_block(n, (N + 31) / 32, pre, b, q);
-                    slot = 32 * b + nth_bit(mw[b], q);
-                }
+                if (!all) slot = cand_slot(slot, N, pre, mw);
             }
             if (a.gather) kept[out] = slot;
             else a.idx_out[(int64_t)s * a.idx_stride + out] = slot;
         }
     }
+#undef TRI_CLASSIFY
     __syncthreads();                                    // every wave has read lengths[s] (n_kept may alias it)
     if (a.n_kept && tid == 0) a.n_kept[s] = nk;
     if (!a.gather) return;
@@ -411,6 +477,66 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
     const int cpr = a.row_bytes >> 4;
     const int lg = 31 - __clz(cpr);
     if (a.gather == GATHER_IN_PLACE) {
+        // kept[j] >= j, and kept[j] - j does not decrease: rows j < c (kept[j] ==
+        // j) stay, and every row from c on moves down to slot j.  Batches of
+        // rows [j0, j0 + nb): all of a batch's rows are read into registers
+        // (four 16-byte K and V pieces per thread), then, after a barrier,
+        // written.  A batch writes slots below j0 + nb and later batches read
+        // slots kept[j] >= j >= j0 + nb, so no row is overwritten before it is
+        // read.
+        int lo = 0, hi = nk;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (kept[mid] == mid) lo = mid + 1;
+            else hi = mid;
+        }
+        // (pieces held in named registers: a local array here was placed in
+        // scratch and LDS, with a wait after every load; two pieces in the
+        // instances built for 64 registers)
+        constexpr int UP = LOW_REGS ? 2 : 4;
+        const int per = (kSelThreads * UP) >> lg;       // rows per batch (<= 512: rows are >= 128 bytes)
+        for (int j0 = lo; j0 < nk; j0 += per) {
+            const int lim = min(per, nk - j0) * cpr;    // 16-byte pieces in the batch
+            uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+            int32_t pv = 0;
+#define TRI_IP_LOAD(u, kx, vx)                                                              \
+            if ((u) * kSelThreads + tid < lim) {                                            \
+                const int e = (u) * kSelThreads + tid;                                      \
+                const int64_t sr = a.src.row(s, kept[j0 + (e >> lg)]);                     \
+                kx = reinterpret_cast<const uint4*>(a.src.k + sr * a.row_bytes)[e & (cpr - 1)]; \
+                vx = reinterpret_cast<const uint4*>(a.src.v + sr * a.row_bytes)[e & (cpr - 1)]; \
+            }
+#define TRI_IP_STORE(u, kx, vx)                                                             \
+            if ((u) * kSelThreads + tid < lim) {                                            \
+                const int e = (u) * kSelThreads + tid;                                      \
+                const int64_t dr = a.dst.row(s, j0 + (e >> lg));                           \
+                reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[e & (cpr - 1)] = kx;  \
+                reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[e & (cpr - 1)] = vx;  \
+            }
+            TRI_IP_LOAD(0, k0, v0)
+            TRI_IP_LOAD(1, k1, v1)
+            if constexpr (UP == 4) {
+                TRI_IP_LOAD(2, k2, v2)
+                TRI_IP_LOAD(3, k3, v3)
+            }
+            if (tid * cpr < lim) pv = a.src.pos[a.src.row(s, kept[j0 + tid])];
+            // every row of the batch has been read: the loads have returned
+            // (the barrier alone does not wait for them) before any wave writes
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            __syncthreads();
+            TRI_IP_STORE(0, k0, v0)
+            TRI_IP_STORE(1, k1, v1)
+            if constexpr (UP == 4) {
+                TRI_IP_STORE(2, k2, v2)
+                TRI_IP_STORE(3, k3, v3)
+            }
+            if (tid * cpr < lim) a.dst.pos[a.dst.row(s, j0 + tid)] = pv;
+#undef TRI_IP_LOAD
+#undef TRI_IP_STORE
+        }
+        return;
+    }
+    if (a.gather == GATHER_IN_PLACE_FILL) {
         // kept[0..c) are below nk and stay; kept[c..nk) fill the freed slots
         // below nk in ascending order.  The r-th freed slot is r + p, where p
         // counts the kept slots below it, i.e. the entries i < c with
@@ -470,7 +596,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
 // J <= 16, G <= 4: two workgroups per CU (at most 64 VGPRs and the SGPRs of 8 waves per
 // SIMD), so one workgroup's gather overlaps the other's select phase.
 template <int J, int G, int MODE>
-__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu((J <= 16 && G <= 4) || (J <= 2 && G == 8) ? 8 : 1))) void k_select(
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(select_low_regs(J, G) ? 8 : 1))) void k_select(
     SelectArgs a) {
     select_segment<J, G, MODE>(a, blockIdx.x);
 }

@@ -32,6 +32,7 @@ TRI_VARIANT_R_WEIGHTED_TRIG = 8
 TRI_PATH_AUTO = 0
 TRI_PATH_FULL = 1
 TRI_PATH_CANDIDATES = 2
+TRI_INPLACE_FILL_FREED = 16
 
 EXPORTS = (
     "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
@@ -39,7 +40,7 @@ EXPORTS = (
     "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name", "tri_last_error",
     "tri_timing_mask",
     "tri_prune_fallbacks", "tri_calibrate_workspace_size", "tri_calibrate", "tri_calib_load_ex",
-    "tri_prune_window_ex",
+    "tri_prune_window_ex", "tri_select_topb_ex",
 )
 
 
@@ -85,6 +86,7 @@ def load():
         "tri_workspace_size": [P, DP, I, ctypes.POINTER(SZ)],
         "tri_score": [P, DP, P, P, P, P, P, SZ, P],
         "tri_select_topb": [P, P, I, I, I, P, P, P, SZ, P],
+        "tri_select_topb_ex": [P, P, P, I, I, I, P, P, P, SZ, P],
         "tri_compact": [DP, P, P, I, DP, P],
         "tri_prune_window": [P, DP, P, I, DP, P, P, SZ, P],
         "tri_prune_window_ex": [P, DP, P, I, DP, P, P, SZ, I, P],
@@ -214,11 +216,20 @@ def tri_score(calib, desc, t, agg, ws, scores=None, mu_sigma=None, stream=None):
     _check("tri_score", rc)
 
 
-def tri_select_topb(agg, lengths, budget, idx, n_kept=None, stream=None):
+def tri_select_topb(agg, lengths, budget, idx, n_kept=None, stream=None, pos=None):
+    """pos None: tri_select_topb (ties at the cut to the lower slot); else
+    tri_select_topb_ex with the slots' positions [n_seg, capacity]."""
     n_seg, cap = agg.shape
-    rc = load().tri_select_topb(_p(agg), _p(lengths), n_seg, cap, int(budget), _p(idx), _p(n_kept), None, 0,
-                                _stream(stream))
-    _check("tri_select_topb", rc)
+    if pos is None:
+        rc = load().tri_select_topb(_p(agg), _p(lengths), n_seg, cap, int(budget), _p(idx), _p(n_kept), None, 0,
+                                    _stream(stream))
+        _check("tri_select_topb", rc)
+    else:
+        if pos.dtype != torch.int32 or tuple(pos.shape) != (n_seg, cap) or not pos.is_contiguous():
+            raise ValueError("pos must be contiguous int32 [n_seg, capacity]")
+        rc = load().tri_select_topb_ex(_p(agg), _p(pos), _p(lengths), n_seg, cap, int(budget), _p(idx), _p(n_kept),
+                                       None, 0, _stream(stream))
+        _check("tri_select_topb_ex", rc)
 
 
 def tri_compact(src, idx, n_kept, budget, dst, stream=None):
@@ -229,7 +240,8 @@ def tri_compact(src, idx, n_kept, budget, dst, stream=None):
 
 def tri_prune_window(calib, src, t, budget, dst, n_kept, ws, stream=None, path=None):
     """path None: tri_prune_window (the automatic path); else tri_prune_window_ex
-    with TRI_PATH_AUTO / TRI_PATH_FULL / TRI_PATH_CANDIDATES."""
+    with TRI_PATH_AUTO / TRI_PATH_FULL / TRI_PATH_CANDIDATES, optionally or'ed
+    with TRI_INPLACE_FILL_FREED."""
     if path is None:
         rc = load().tri_prune_window(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
                                      _p(n_kept), _p(ws), ws.numel(), _stream(stream))

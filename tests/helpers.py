@@ -4,12 +4,17 @@ tolerance checks.
 
 Tolerances (from the arithmetic: fp32 accumulation of exact bf16 products and
 an fp32 aggregate, against the oracle's fp64):
-  scores S_h : |gpu - ref| <= 1e-4 * max(|ref|, rms of the head's ref scores)
+  scores S_h : |gpu - ref| <= 1e-4 * max(|ref|, rms of the head's ref scores).
+               The fp32 error is bounded relative to the sum of the terms'
+               magnitudes, not to |S|: scores near zero (the trig term
+               cancelling the norm term) measured up to 8e-3 of |S| against
+               the fp64 oracle at head_dim 64, so a bare relative bound cannot
+               hold there
   mu, sigma  : |gpu - ref| <= 1e-4 * max(|ref mu|, ref sigma)
   A          : |gpu - ref| <= 1e-4 * max(|ref|, 1)
   top-B      : same count, ascending; a slot may differ from the oracle's set
-               only if |A_ref - T| <= 1e-4 * max(|T|, 1), T = oracle's B-th
-               largest aggregated score
+               only if |A_ref - T| <= 1e-4 * |T|, T = oracle's B-th largest
+               aggregated score (ties at the cut: the earlier position)
   K', V', p' : bit-exact copies of the rows the GPU kept
 """
 from __future__ import annotations
@@ -74,7 +79,16 @@ def oracle_segment(cfg, cal, K, V, pos, t, s, B, layer0=0, variant=0):
     return oracle.prune_segment(K, V, pos, t, cfg.theta, M, phi, R, cfg.offsets, B, variant=variant)
 
 
+def oracle_select(cfg, cal, K, pos, t, s, B, layer0=0):
+    """Oracle scores, statistics, aggregate and top-B of one segment (no gather)."""
+    M, phi, R = seg_calib(cal, cfg, s, layer0)
+    S = oracle.score_segment(K, pos, t, cfg.theta, M, phi, R, cfg.offsets)
+    mu, sigma, A = oracle.zscore_max(S)
+    return {"S": S, "mu": mu, "sigma": sigma, "A": A, "idx": oracle.select_topb(A, B, pos)}
+
+
 def check_scores(S_gpu, S_ref, what=""):
+    """Error per score relative to max(|S|, the head's rms score)."""
     S_gpu = np.asarray(S_gpu, dtype=np.float64)
     rms = np.sqrt(np.mean(S_ref ** 2, axis=1, keepdims=True))
     scale = np.maximum(np.abs(S_ref), rms)
@@ -96,8 +110,9 @@ def check_agg(A_gpu, A_ref, what=""):
     assert err.max() <= RTOL, f"{what} aggregate mismatch: max err {err.max():.3e}"
 
 
-def check_selection(idx_gpu, A_ref, B, what=""):
-    """idx_gpu against the oracle's top-B of A_ref under the tie tolerance."""
+def check_selection(idx_gpu, A_ref, B, what="", pos=None):
+    """idx_gpu against the oracle's top-B of A_ref (ties at the cut to the
+    earlier of the slots' positions pos; None: slot order) under the tie band."""
     idx_gpu = np.asarray(idx_gpu)
     N = len(A_ref)
     if N <= B:
@@ -106,10 +121,10 @@ def check_selection(idx_gpu, A_ref, B, what=""):
     assert len(idx_gpu) == B, f"{what}: kept {len(idx_gpu)} != {B}"
     assert np.all(np.diff(idx_gpu) > 0), f"{what}: kept slots not strictly ascending"
     assert idx_gpu.min() >= 0 and idx_gpu.max() < N
-    ref = oracle.select_topb(A_ref, B)
+    ref = oracle.select_topb(A_ref, B, pos)
     thr = np.sort(A_ref)[-B]
     diff = np.setxor1d(ref, idx_gpu)
-    band = RTOL * max(abs(thr), 1.0)
+    band = RTOL * abs(thr)
     bad = [int(i) for i in diff if abs(A_ref[i] - thr) > band]
     assert not bad, f"{what}: {len(bad)} slots differ away from the cut (e.g. {bad[:5]}, thr {thr})"
     return len(diff)
@@ -134,12 +149,12 @@ def stored(x):
     return W.to_stored_numpy(x)
 
 
-def check_in_place(cfg, cal, Kb, Vb, Pb, Ka, Va, Pa, N, nk, t, s, B, tag, oop_kept=None):
+def check_in_place(cfg, cal, Kb, Vb, Pb, Ka, Va, Pa, N, nk, t, s, B, tag, oop_kept=None, fill=False):
     """One segment pruned in place.  b: its rows before the prune (all slots);
     a: after.  The kept set against the oracle's top-B (and, when given, the
-    out-of-place pass's set), the arrangement against the oracle's in-place
-    layout of that set, rows bit-exact, rows at or above the kept count
-    untouched."""
+    out-of-place pass's set); the arrangement: slot order, as out of place, or
+    with fill the oracle's fill-freed-slots layout of that set; rows
+    bit-exact, rows at or above the kept count untouched."""
     nks = min(N, B)
     assert nk == nks, f"{tag}: kept count {nk} != {nks}"
     if N == 0:
@@ -148,10 +163,11 @@ def check_in_place(cfg, cal, Kb, Vb, Pb, Ka, Va, Pa, N, nk, t, s, B, tag, oop_ke
     ix = kept_slots_from_positions(P, Pa[:nks])
     kept = np.sort(ix)
     ref = oracle_segment(cfg, cal, K, V, P, t, s, B)
-    check_selection(kept, ref["A"], B, tag)
+    check_selection(kept, ref["A"], B, tag, pos=P)
     if oop_kept is not None:
         assert np.array_equal(kept, oop_kept), f"{tag}: kept set differs from the out-of-place pass"
-    assert np.array_equal(ix, oracle.inplace_layout(kept, N)), f"{tag}: arrangement is not the in-place layout"
+    layout = oracle.fill_freed_layout(kept, N) if fill else kept
+    assert np.array_equal(ix, layout), f"{tag}: arrangement is not the {'fill-freed' if fill else 'slot-order'} layout"
     check_compaction(K, V, P, Ka[:nks], Va[:nks], Pa[:nks], ix, tag)
     assert np.array_equal(Ka[nks:], Kb[nks:]) and np.array_equal(Va[nks:], Vb[nks:]) and \
         np.array_equal(Pa[nks:], Pb[nks:]), f"{tag}: rows at or above the kept count were written"

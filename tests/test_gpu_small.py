@@ -122,24 +122,32 @@ def test_equal_scores_keep_lowest_slots(gpu_lib):
     _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "equal")
 
 
+@pytest.mark.parametrize("with_pos", [False, True])
 @pytest.mark.parametrize("cap", [2048, 8192, 32768, 32896, 40000, 65536])
-def test_select_kernel_bit_exact(gpu_lib, cap):
+def test_select_kernel_bit_exact(gpu_lib, cap, with_pos):
     """tri_select_topb on seeded score arrays (ties, signed zeros, all-equal)
-    equals the oracle's selection exactly."""
+    equals the oracle's selection exactly; with positions (tri_select_topb_ex:
+    a random permutation in even segments, a few hundred repeated values in odd
+    ones), ties at the cut go to the earliest position, then the lower slot."""
     T = gpu_lib
     n_seg = 8
     A = W.synthetic_scores(n_seg, cap, seed=cap)
     B = min(4096, cap // 3)
     lengths = torch.tensor([cap, 0, 1, B, B + 1, cap - 1, cap // 2 + 7, cap], dtype=torch.int32)
-    log(f"case select cap={cap} B={B}")
+    log(f"case select cap={cap} B={B} positions={with_pos}")
+    pos = None
+    if with_pos:
+        gen = torch.Generator().manual_seed(cap + 1)
+        pos = torch.stack([torch.randperm(cap, generator=gen) if s % 2 == 0 else
+                           torch.randint(-300, 300, (cap,), generator=gen) for s in range(n_seg)]).to(torch.int32)
     idx = torch.full((n_seg, B), -1, dtype=torch.int32, device="cuda")
     nk = torch.full((n_seg,), -1, dtype=torch.int32, device="cuda")
-    T.tri_select_topb(A.cuda(), lengths.cuda(), B, idx, nk)
+    T.tri_select_topb(A.cuda(), lengths.cuda(), B, idx, nk, pos=None if pos is None else pos.cuda())
     torch.cuda.synchronize()
     idx, nk = idx.cpu(), nk.cpu()
     for s in range(n_seg):
         N = int(lengths[s])
-        ref = oracle.select_topb(A[s, :N].numpy(), B)
+        ref = oracle.select_topb(A[s, :N].numpy(), B, None if pos is None else pos[s, :N].numpy())
         assert int(nk[s]) == len(ref), f"seg {s}"
         assert np.array_equal(idx[s, :len(ref)].numpy(), ref), f"cap {cap} seg {s} N {N}"
 
@@ -209,10 +217,13 @@ def test_paged_small_every_step(gpu_lib, page_size, dtype):
         check_compaction(K, V, P, Kd, Vd, Pd, ix, tag)
 
 
-@pytest.mark.parametrize("in_place", [False, True])
+@pytest.mark.parametrize("in_place", [False, True, "fill"])
 def test_decode_loop_small(gpu_lib, in_place):
     """Append + decode attention each step, prune after each window (into the
-    other buffer, or in place), on a GPT-OSS-shaped but small cache."""
+    other buffer, or in place, or in place filling freed slots), on a
+    GPT-OSS-shaped but small cache.  In place, the same window state is also
+    pruned out of place first: slot order gives the same bytes, the fill mode
+    the same kept set."""
     T = gpu_lib
     cfg = W.CONFIGS["gptoss"].replace(n_layers=2, n_seq=3, budget=64, window=8, windows=3, start_pos_range=512)
     log(f"case decode small, in place {in_place}")
@@ -250,14 +261,25 @@ def test_decode_loop_small(gpu_lib, in_place):
         desc = dense_desc(T, cfg, c)
         ws = T.workspace(calib, desc, cfg.budget)
         if in_place:
+            fill = in_place == "fill"
             before = {k: c[k].cpu() for k in ("k", "v", "pos", "lengths")}
-            T.tri_prune_window(calib, desc, c["t"], cfg.budget, desc, c["lengths"], ws)
+            oop = empty_like_dense(c, cfg.budget)
+            T.tri_prune_window(calib, desc, c["t"], cfg.budget, dense_desc(T, cfg, oop), oop["lengths"], ws)
+            T.tri_prune_window(calib, desc, c["t"], cfg.budget, desc, c["lengths"], ws,
+                               path=T.TRI_INPLACE_FILL_FREED if fill else T.TRI_PATH_AUTO)
             torch.cuda.synchronize()
             Ka, Va, Pa = stored(c["k"].cpu()), stored(c["v"].cpu()), c["pos"].cpu().numpy()
             Kb, Vb, Pb = stored(before["k"]), stored(before["v"]), before["pos"].numpy()
+            Po = oop["pos"].cpu().numpy()
             for s in range(cfg.n_seg):
-                check_in_place(cfg, cal, Kb[s], Vb[s], Pb[s], Ka[s], Va[s], Pa[s], int(before["lengths"][s]),
-                               int(c["lengths"][s]), t, s, cfg.budget, f"decode window {w} seg {s} in place")
+                N, nks = int(before["lengths"][s]), int(c["lengths"][s])
+                oop_kept = np.sort(kept_slots_from_positions(Pb[s, :N], Po[s, :nks]))
+                check_in_place(cfg, cal, Kb[s], Vb[s], Pb[s], Ka[s], Va[s], Pa[s], N, nks, t, s, cfg.budget,
+                               f"decode window {w} seg {s} in place", oop_kept, fill=fill)
+                if not fill:
+                    assert np.array_equal(Pa[s, :nks], Po[s, :nks]) and \
+                        np.array_equal(Ka[s, :nks], stored(oop["k"][s, :nks].cpu())), \
+                        f"decode window {w} seg {s}: in place differs from out of place"
             continue
         nxt = caches[1 - cur]
         nk = nxt["lengths"]
