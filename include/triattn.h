@@ -278,6 +278,28 @@ int tri_prune_window_ex(tri_calib_t calib, const tri_cache_desc* src, const int3
 int tri_prune_fallbacks(const void* ws, size_t ws_bytes, int32_t* count, tri_stream_t stream);
 
 /*
+ * tri_prune_window_ex without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a device array the
+ * library holds, TRI_STATIC_SCRATCH_BYTES per device, on every device it
+ * runs on, until the process ends.  This call allocates nothing.
+ *  - Same arguments and result as tri_prune_window_ex (path included), minus
+ *    ws/ws_bytes.
+ *  - A cache whose tri_workspace_size exceeds TRI_STATIC_SCRATCH_BYTES is
+ *    refused with TRI_ERR_WORKSPACE (tri_last_error gives both sizes); 64 MiB
+ *    holds, e.g., one 32K-key layer of 8 KV heads at GQA 4.
+ *  - Every call on one device shares that device's array, which keeps what
+ *    the last call left; nothing in it needs to start at zero (each pass
+ *    writes what it reads).  Calls whose work overlaps on one device (two
+ *    streams, or two threads) race on it: serialise them.
+ *  - The first call on a device looks up that device's copy of the array
+ *    (hipGetSymbolAddress); later calls reuse the address.
+ */
+#define TRI_STATIC_SCRATCH_BYTES (64u << 20)
+int tri_prune_window_static(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
+                            const tri_cache_desc* dst, int32_t* n_kept, int path, tri_stream_t stream);
+
+/*
  * Appends one token to every segment: row lengths[s] of segment s receives
  * k_new[s], v_new[s] (device [n_seg][head_dim], cache dtype) and position
  * pos_new[b] (device int32 [n_seq]); lengths[s] then grows by one.  A segment
@@ -302,7 +324,9 @@ int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, floa
 const char* tri_strerror(int code);
 
 /* For the calling thread's most recent TRI_ERR_HIP: which step failed and the
- * HIP error string ("" if none).  Valid until the next failing call. */
+ * HIP error string; for a tri_prune_window_static refused for size: the
+ * workspace needed and the scratch size ("" if none).  Valid until the next
+ * failing call. */
 const char* tri_last_error(void);
 
 /*

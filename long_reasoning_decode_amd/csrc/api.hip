@@ -550,9 +550,43 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
 // with the candidate pass, 0.13 ms without).
 constexpr int64_t kCandidateMinSegs = 256;
 
+// ---------------------------------------------------------------- library-owned scratch
+// Workspace of tri_prune_window_static: a file-scope device array, so the
+// entry point allocates nothing.  The loader places one copy on every device
+// the library runs on, held until the process ends.  In host code `scratch`
+// is only a stand-in for the symbol: its device address on the current device
+// comes from hipGetSymbolAddress, taken once per device on the first call
+// there, and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[TRI_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_addr;    // device -> address of that device's copy of `scratch`
+
+static int static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "scratch: current device");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    auto it = g_scratch_addr.find(dev);
+    if (it == g_scratch_addr.end()) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "scratch: symbol address");
+        if (!p || !aligned256(p)) {
+            snprintf(t_last_error, sizeof t_last_error, "scratch: symbol address %p not 256-byte aligned", p);
+            return TRI_ERR_HIP;
+        }
+        it = g_scratch_addr.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return TRI_OK;
+}
+
+// use_static: the workspace is the library's `scratch` on the current device
+// (ws and ws_bytes are ignored), for caches whose workspace fits in it.
 static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
                         const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes, int path,
-                        tri_stream_t stream) {
+                        tri_stream_t stream, bool use_static = false) {
     const bool fill = (path & TRI_INPLACE_FILL_FREED) != 0;
     path &= ~TRI_INPLACE_FILL_FREED;
     if (path != TRI_PATH_AUTO && path != TRI_PATH_FULL && path != TRI_PATH_CANDIDATES) return TRI_ERR_INVALID_ARG;
@@ -563,6 +597,17 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
     if (!t || !n_kept) return TRI_ERR_INVALID_ARG;
     if (src->capacity > kMaxLen) return TRI_ERR_UNSUPPORTED;
     const WsPlan p = plan_workspace(calib, src);
+    if (use_static) {
+        if (p.total > (size_t)TRI_STATIC_SCRATCH_BYTES) {
+            snprintf(t_last_error, sizeof t_last_error,
+                     "the pass needs %zu bytes of workspace; the library's scratch holds %zu", p.total,
+                     (size_t)TRI_STATIC_SCRATCH_BYTES);
+            return TRI_ERR_WORKSPACE;
+        }
+        if (!device_present()) return TRI_ERR_NO_DEVICE;
+        if ((rc = static_scratch(&ws))) return rc;
+        ws_bytes = TRI_STATIC_SCRATCH_BYTES;
+    }
     if (!ws || ws_bytes < p.total || !aligned256(ws)) return TRI_ERR_WORKSPACE;
     if (!device_present()) return TRI_ERR_NO_DEVICE;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -666,6 +711,11 @@ int tri_prune_window_ex(tri_calib_t calib, const tri_cache_desc* src, const int3
                         const tri_cache_desc* dst, int32_t* n_kept, void* ws, size_t ws_bytes, int path,
                         tri_stream_t stream) {
     return prune_window(calib, src, t, budget, dst, n_kept, ws, ws_bytes, path, stream);
+}
+
+int tri_prune_window_static(tri_calib_t calib, const tri_cache_desc* src, const int32_t* t, int budget,
+                            const tri_cache_desc* dst, int32_t* n_kept, int path, tri_stream_t stream) {
+    return prune_window(calib, src, t, budget, dst, n_kept, nullptr, 0, path, stream, true);
 }
 
 int tri_prune_fallbacks(const void* ws, size_t ws_bytes, int32_t* count, tri_stream_t stream) {

@@ -33,6 +33,7 @@ TRI_PATH_AUTO = 0
 TRI_PATH_FULL = 1
 TRI_PATH_CANDIDATES = 2
 TRI_INPLACE_FILL_FREED = 16
+TRI_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = (
     "tri_calib_load", "tri_calib_free", "tri_workspace_size", "tri_score", "tri_select_topb",
@@ -40,7 +41,7 @@ EXPORTS = (
     "tri_timing_enable", "tri_timing_reset", "tri_timing_read", "tri_timing_name", "tri_last_error",
     "tri_timing_mask",
     "tri_prune_fallbacks", "tri_calibrate_workspace_size", "tri_calibrate", "tri_calib_load_ex",
-    "tri_prune_window_ex", "tri_select_topb_ex",
+    "tri_prune_window_ex", "tri_select_topb_ex", "tri_prune_window_static",
 )
 
 
@@ -90,6 +91,7 @@ def load():
         "tri_compact": [DP, P, P, I, DP, P],
         "tri_prune_window": [P, DP, P, I, DP, P, P, SZ, P],
         "tri_prune_window_ex": [P, DP, P, I, DP, P, P, SZ, I, P],
+        "tri_prune_window_static": [P, DP, P, I, DP, P, I, P],
         "tri_append": [DP, P, P, P, P],
         "tri_decode_attn": [DP, I, P, F, P, P],
         "tri_strerror": [I],
@@ -250,6 +252,13 @@ def tri_prune_window(calib, src, t, budget, dst, n_kept, ws, stream=None, path=N
         rc = load().tri_prune_window_ex(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
                                         _p(n_kept), _p(ws), ws.numel(), int(path), _stream(stream))
         _check("tri_prune_window_ex", rc)
+
+
+def tri_prune_window_static(calib, src, t, budget, dst, n_kept, path=TRI_PATH_AUTO, stream=None):
+    """tri_prune_window_ex on the library's own scratch (no workspace argument)."""
+    rc = load().tri_prune_window_static(calib.handle, ctypes.byref(src), _p(t), int(budget), ctypes.byref(dst),
+                                        _p(n_kept), int(path), _stream(stream))
+    _check("tri_prune_window_static", rc)
 
 
 def tri_calibrate(q, mag, phase, conc, ws=None, stream=None):
