@@ -59,11 +59,29 @@ def algorithmic_bytes(n_keys_total, n_seg, n_kept_total, d, es):
     return score, gather
 
 
+# The pages' own figures for the method, end to end (decode throughput and KV
+# memory at full-attention accuracy, Qwen3-8B on AIME25; hardware not named):
+# context for the result line, not this kernel's metric.
+PAGES_CONTEXT = {
+    "decode_throughput_vs_full_attention": 2.5,
+    "kv_memory_reduction": 10.7,
+    "source": "zingnex.cn TriAttention page, section 实验验证; yeyulingfeng.com TriAttention page, "
+              "section (二)主实验结果",
+    "note": "end-to-end serving figures on hardware the pages do not name; they measure the whole decode, "
+            "not the pruning pass timed here",
+}
+
+
 def cpu_baseline(W, cfg, g, cal, B, n_sample):
     import numpy as np
 
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1, n_sample))
+    threads = oracle.host_threads()
+    n_sample = max(n_sample, threads)                   # every thread gets a segment
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
     per_l = cfg.n_seq * cfg.n_kv_heads
     segs = [int(s) for s in np.linspace(0, cfg.n_seg - 1, n_sample).round()]
     data = {s: (W.to_stored_numpy(g["k"][s]), W.to_stored_numpy(g["v"][s]), g["pos"][s].cpu().numpy())
@@ -83,8 +101,11 @@ def cpu_baseline(W, cfg, g, cal, B, n_sample):
     dt = time.perf_counter() - t0
     keys = len(segs) * cfg.n_keys
     return {"value": keys / dt / 1e9, "unit": "G keys/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"{len(segs)} whole segments ({cfg.n_keys} keys each, full prune chain) spread over "
-                      f"layers/sequences/heads; {dt:.1f} s wall on {threads} threads"}
+                      f"layers/sequences/heads; {dt:.1f} s wall on {threads} threads (the process's CPU "
+                      f"share: OMP_NUM_THREADS, else its affinity set)"}
 
 
 def kernel_breakdown(T, step, steps):
@@ -116,6 +137,27 @@ def timed_steps(T, step, steps, stream, kernels):
     torch.cuda.synchronize()
     T.tri_timing_enable(False)
     return ev0.elapsed_time(ev1) / steps, T.tri_timing_read()
+
+
+def flushed_steps(step, steps, stream, flush_mib):
+    """Each step timed alone (events on its stream) right after writing a
+    flush_mib buffer, so the step starts with nothing of its inputs in the
+    last-level cache; the flush itself is outside every timed interval.
+    Returns the mean ms per step."""
+    import torch
+    buf = torch.empty(flush_mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        buf.fill_(float(i))
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    del buf
+    torch.cuda.empty_cache()
+    return ms
 
 
 def copy_bandwidth(mib=4096, reps=5):
@@ -165,8 +207,11 @@ def bench_decode_loop(args, T, W):
     (append one token to every segment, single-query attention of every query
     head over its cache) followed by the window's prune back to B.  Tokens are
     generated before timing and reused window after window.  The prune runs in
-    place (only the kept rows above B move) unless --out-of-place is given, in
-    which case it compacts into a second cache and the two alternate."""
+    place unless --out-of-place is given, in
+    which case it compacts into a second cache and the two alternate.  In place
+    the cache stays in slot order (every kept row after the first dropped slot
+    moves), or with --fill-freed only the kept rows above B move, into the freed
+    slots."""
     import math
 
     import torch
@@ -214,7 +259,8 @@ def bench_decode_loop(args, T, W):
         tvec.fill_(t0 + (state["w"] + 1) * win)
         if in_place:
             before = caches[cur]["pos"][:, :B].clone() if count_moves else None
-            T.tri_prune_window(calib, d, tvec, B, d, caches[cur]["lengths"], ws, stream=stream)
+            T.tri_prune_window(calib, d, tvec, B, d, caches[cur]["lengths"], ws, stream=stream,
+                               path=T.TRI_INPLACE_FILL_FREED if args.fill_freed else T.TRI_PATH_AUTO)
             if count_moves:             # rows the prune wrote: slots below B whose key changed
                 moved["rows"] = int((caches[cur]["pos"][:, :B] != before).sum())
         else:
@@ -259,7 +305,10 @@ def bench_decode_loop(args, T, W):
                                 f"GQA {cfg.group}, head_dim {cfg.head_dim}, bf16, B={B}; a step is one {win}-token "
                                 f"window (append + decode attention per token, then the prune "
                                 f"{'in place' if in_place else 'into a second cache'})"),
-                   "tokens_per_step": tokens},
+                   "tokens_per_step": tokens,
+                   "in_place_layout": (("fill freed slots" if args.fill_freed else "slot order") if in_place
+                                       else None)},
+        "pages_context": PAGES_CONTEXT,
         "roofline": {"bound": "hbm", "kernel": "decode_attn", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic("decode_attn", "gptoss")},
@@ -399,7 +448,13 @@ def main():
                     help="qwen workloads: measure a 4 GiB device copy as a reference bandwidth (0: skip)")
     ap.add_argument("--out-of-place", action="store_true",
                     help="gptoss: prune into a second cache instead of in place")
-    ap.add_argument("--cpu-sample", type=int, default=16, help="oracle segments for the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=16,
+                    help="oracle segments for the CPU baseline (at least one per host thread; 0: skip)")
+    ap.add_argument("--flush-mib", type=int, default=-1,
+                    help="qwen workloads: MiB written before each timed pass to flush the last-level cache "
+                         "(default: 1024 for caches under 16M keys, else 0)")
+    ap.add_argument("--fill-freed", action="store_true",
+                    help="gptoss: in-place prune in the fill-freed-slots arrangement instead of slot order")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
                          "(known-size reference for hardware byte counters)")
@@ -463,7 +518,20 @@ def main():
     kt = kernel_breakdown(T, step, args.steps)
     heavy = ("score", "select_gather", "gather")
     dom = max(heavy, key=lambda k: kt.get(k, (0, 0.0))[1] / max(kt.get(k, (0, 0.0))[0], 1))
-    ms, kt_timed = timed_steps(T, step, args.steps, stream, [dom])
+    # Small caches fit the 256 MB last-level cache, and back to back each pass
+    # would find the last one's inputs there: those workloads are timed pass by
+    # pass, each after a 1 GiB flush.  The 36-layer cache (48 GB) needs none.
+    flush_mib = args.flush_mib if args.flush_mib >= 0 else (1024 if cfg.n_seg * cfg.n_keys < (1 << 24) else 0)
+    if flush_mib:
+        T.tri_timing_reset()
+        T.tri_timing_enable(True, only=[dom])
+        ms = flushed_steps(step, args.steps, stream, flush_mib)
+        T.tri_timing_enable(False)
+        kt_timed = T.tri_timing_read()
+        warm_ms, _ = timed_steps(T, step, args.steps, stream, [])
+    else:
+        ms, kt_timed = timed_steps(T, step, args.steps, stream, [dom])
+        warm_ms = None
     fallbacks = T.tri_prune_fallbacks(ws)
     print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
@@ -537,8 +605,13 @@ def main():
             "workload": (f"{cfg.name}: Qwen3-8B-shaped cache, {cfg.n_layers} layers x {cfg.n_seq} sequences x "
                          f"{cfg.n_kv_heads} KV heads x {cfg.n_keys} keys, head_dim {cfg.head_dim}, GQA {cfg.group}, "
                          f"B={B}, {len(cfg.offsets)} geometric offsets, one prune pass"),
-            "kv_dtype": "bf16" if es == 2 else "f32", "keys_per_step": n_keys, "kept_per_step": n_kept,
+            "kv_dtype": "bf16" if es == 2 else "f32", "score_dtype": "f32", "keys_per_step": n_keys,
+            "kept_per_step": n_kept,
+            "timing": (f"each pass timed alone after a {flush_mib} MiB flush of the last-level cache"
+                       if flush_mib else "passes back to back between two events"),
         },
+        "warm_ms_per_step": round(warm_ms, 4) if warm_ms is not None else None,
+        "pages_context": PAGES_CONTEXT,
         "pass_hbm": {"algorithmic_bytes": b_score + b_gather, "achieved_GBs": round(pass_gbs, 1),
                      "frac_of_peak": round(pass_gbs / HBM_PEAK_GBS, 4),
                      "device_copy_GBs": round(copy_gbs, 1) if copy_gbs else None,
