@@ -26,7 +26,8 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kMaxBudget = 8192;
 
-// Inclusive scan of one uint32 per thread over the 1024-thread block.
+// Inclusive scan of one uint32 per thread over a block of NT threads.
+template <int NT = kSelThreads>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t x, uint32_t* wsum) {
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     x = wave_incl_scan(x);
@@ -205,18 +206,19 @@ __device__ __forceinline__ int load_candidates(const SelectArgs& a, const int s,
 // per digit.  On return T is that key, need the number of entries equal to T
 // that rank within the first `need` (entries > T plus that many entries == T
 // make up the original need), and n_eq the number of such entries equal to T.
-template <int J>
+template <int J, int NT>
 __device__ __forceinline__ void radix_select(const uint32_t (&key)[J], int nv, uint64_t sel, bool use_sel,
                                              int& need, uint32_t& T, uint32_t& n_eq, uint32_t* hist,
                                              uint32_t* wsum, uint32_t* pick) {
+    constexpr int HB = 2048 / NT;                       // histogram bins per thread
     const int tid = threadIdx.x;
     uint32_t prefix = 0u, pmask = 0u;
 #pragma unroll
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
         const uint32_t dmask = pass < 2 ? 0x7ffu : 0x3ffu;
-        hist[tid] = 0u;
-        hist[tid + kSelThreads] = 0u;
+#pragma unroll
+        for (int i = 0; i < HB; ++i) hist[tid + i * NT] = 0u;
         if (tid == 0) {
             pick[0] = 0u;
             pick[1] = 0u;
@@ -225,26 +227,28 @@ __device__ __forceinline__ void radix_select(const uint32_t (&key)[J], int nv, u
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const bool in = j * kSelThreads + tid < nv && (!use_sel || ((sel >> j) & 1u));
+            const bool in = j * NT + tid < nv && (!use_sel || ((sel >> j) & 1u));
             if (in && (key[j] & pmask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
         }
         __syncthreads();
-        // Thread t owns bins 2047-2t and 2046-2t: a scan in thread order is a
-        // cumulative count from the top bin down.
-        const int b0 = 2047 - 2 * tid, b1 = b0 - 1;
-        const uint32_t h0 = hist[b0], h1 = hist[b1];
-        const uint32_t incl = block_incl_scan(h0 + h1, wsum);
-        const uint32_t above0 = incl - (h0 + h1);
-        const uint32_t above1 = above0 + h0;
+        // Thread t owns bins 2047 - HB t down to 2048 - HB (t + 1): a scan in
+        // thread order is a cumulative count from the top bin down.
+        uint32_t h[HB], hs = 0u;
+#pragma unroll
+        for (int i = 0; i < HB; ++i) {
+            h[i] = hist[2047 - HB * tid - i];
+            hs += h[i];
+        }
+        uint32_t above = block_incl_scan<NT>(hs, wsum) - hs;
         const uint32_t un = (uint32_t)need;
-        if (above0 < un && above0 + h0 >= un) {
-            pick[0] = (uint32_t)b0;
-            pick[1] = above0;
-            pick[2] = h0;
-        } else if (above1 < un && above1 + h1 >= un) {
-            pick[0] = (uint32_t)b1;
-            pick[1] = above1;
-            pick[2] = h1;
+#pragma unroll
+        for (int i = 0; i < HB; ++i) {
+            if (above < un && above + h[i] >= un) {
+                pick[0] = (uint32_t)(2047 - HB * tid - i);
+                pick[1] = above;
+                pick[2] = h[i];
+            }
+            above += h[i];
         }
         __syncthreads();
         prefix |= pick[0] << shift;
@@ -266,7 +270,9 @@ __device__ __forceinline__ int cand_slot(int n, int N, const uint32_t* pre, cons
 
 // Instances built for 8 waves per SIMD (at most 64 VGPRs), so two workgroups
 // share a CU and one's gather overlaps the other's select phase.
-constexpr bool select_low_regs(int J, int G) { return (J <= 16 && G <= 4) || (J <= 2 && G == 8); }
+constexpr bool select_low_regs(int J, int G, int NT = 1024) {
+    return NT < 1024 || (J <= 16 && G <= 4) || (J <= 2 && G == 8);
+}
 
 // Orderable key of a position for the tie rule: an earlier (smaller, signed)
 // position gives a larger key.
@@ -282,20 +288,24 @@ __device__ __forceinline__ uint32_t pos_order_key(int32_t p) { return ~((uint32_
 // cut T (the B-th largest A') exceeds U, the keys at or above it, their A and
 // their tie order are exactly those of the full computation.  Otherwise the
 // segment goes on the fallback list and nothing is written for it here.
-template <int J, int G, int MODE>
+template <int J, int G, int MODE, int NT = kSelThreads>
 __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s) {
     constexpr bool CAND = MODE == SELECT_C;
-    constexpr bool LOW_REGS = select_low_regs(J, G);
+    constexpr bool LOW_REGS = select_low_regs(J, G, NT);
+    constexpr int NW = NT / kWave;
+    // kept slots: at most the budget, and at most the J * NT entries held
+    constexpr int KEPT = J * NT < kMaxBudget ? J * NT : kMaxBudget;
+    static_assert(NT == kSelThreads || !CAND, "candidate lists are read by 1024-thread blocks");
     // mode C holds at most J*1024 >= N/2 candidates (launch_select), so a segment
     // has at most 64 J blocks of 32 keys (and at most 2048, N <= 65536)
     constexpr int NB = CAND ? (64 * J < 2048 ? 64 * J : 2048) : 1;
     constexpr int GZ = G > 0 ? G : 1;
     __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wsum[kSelWaves];
+    __shared__ uint32_t wsum[NW];
     __shared__ uint32_t pick[3];
-    __shared__ uint32_t cnt_gt[J * kSelWaves], cnt_eq[J * kSelWaves];
-    __shared__ int32_t kept[kMaxBudget];
-    __shared__ double scratch[(kSelWaves + 1) * GZ];
+    __shared__ uint32_t cnt_gt[J * NW], cnt_eq[J * NW];
+    __shared__ int32_t kept[KEPT];
+    __shared__ double scratch[(NW + 1) * GZ];
     __shared__ uint32_t pre[NB], lpos[NB], mw[NB];
     __shared__ __align__(16) uint32_t hwl[CAND ? NB * GZ : 1];      // mode C: the segment's mask words
     __shared__ uint32_t bcast[1];
@@ -320,7 +330,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
             const double2* st = a.stats + (int64_t)s * a.n_chunks * G;
             auto merge = [&]() {
                 return a.n_chunks <= kWave ? merge_stats_wave<G>(st, a.n_chunks, a.chunk, N)
-                                           : merge_stats<G, kSelThreads>(st, a.n_chunks, a.chunk, N, scratch);
+                                           : merge_stats<G, NT>(st, a.n_chunks, a.chunk, N, scratch);
             };
             if constexpr (CAND) {
                 z = merge();
@@ -338,7 +348,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
                 constexpr int LB = WIDE ? 16 : 8;
                 constexpr int L0 = WIDE ? LB : 0;                  // keys loaded before the merge
                 auto load_scores = [&](int j, float (&S)[G]) {
-                    const float* p = a.s_int + ((int64_t)s * a.cap + j * kSelThreads + tid) * G;
+                    const float* p = a.s_int + ((int64_t)s * a.cap + j * NT + tid) * G;
                     if constexpr (G % 4 == 0) {
 #pragma unroll
                         for (int g = 0; g < G; g += 4) {
@@ -353,14 +363,14 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
                 float S0[L0 > 0 ? L0 : 1][G];
 #pragma unroll
                 for (int j = 0; j < L0; ++j)
-                    if (j * kSelThreads + tid < N) load_scores(j, S0[j]);
+                    if (j * NT + tid < N) load_scores(j, S0[j]);
                 z = merge();
 #pragma unroll
                 for (int j = 0; j < L0; ++j)
-                    if (j * kSelThreads + tid < N) key[j] = order_key(aggregate<G>(S0[j], z));
+                    if (j * NT + tid < N) key[j] = order_key(aggregate<G>(S0[j], z));
 #pragma unroll
                 for (int j = L0; j < J; ++j) {
-                    if (j * kSelThreads + tid < N) {
+                    if (j * NT + tid < N) {
                         float S[G];
                         load_scores(j, S);
                         key[j] = order_key(aggregate<G>(S, z));
@@ -371,7 +381,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         } else {
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                const int n = j * kSelThreads + tid;
+                const int n = j * NT + tid;
                 if (n < N) key[j] = order_key(a.agg[(int64_t)s * a.agg_stride + n]);
                 if ((j & 15) == 15) __builtin_amdgcn_sched_barrier(0);
             }
@@ -379,7 +389,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
 
         // ---- radix select of the B-th largest key
         need = B;
-        radix_select<J>(key, nv, 0ull, false, need, T, n_eq, hist, wsum, pick);
+        radix_select<J, NT>(key, nv, 0ull, false, need, T, n_eq, hist, wsum, pick);
 
         if constexpr (CAND) {
             if (nv < N) {                               // certificate for the keys left out
@@ -405,7 +415,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
     if (by_pos) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int n = j * kSelThreads + tid;
+            const int n = j * NT + tid;
             if (n < nv && key[j] == T) {
                 int slot = n;
                 if constexpr (CAND) slot = cand_slot(n, N, pre, mw);
@@ -416,10 +426,10 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
             }
         }
         uint32_t n_eq2 = 0u;
-        radix_select<J>(key, nv, eqm, true, need, P, n_eq2, hist, wsum, pick);
+        radix_select<J, NT>(key, nv, eqm, true, need, P, n_eq2, hist, wsum, pick);
     }
 #define TRI_CLASSIFY(j, gt, eq)                                             \
-    const bool valid_##j = (j) * kSelThreads + tid < nv;                    \
+    const bool valid_##j = (j) * NT + tid < nv;                    \
     bool gt, eq;                                                            \
     if (by_pos && ((eqm >> (j)) & 1u)) {                                    \
         gt = key[j] > P;                                                    \
@@ -436,17 +446,17 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         TRI_CLASSIFY(j, gt, eq)
         const uint64_t bg = __ballot(gt), be = __ballot(eq);
         if (lane == 0) {
-            cnt_gt[j * kSelWaves + w] = (uint32_t)__popcll(bg);
-            cnt_eq[j * kSelWaves + w] = (uint32_t)__popcll(be);
+            cnt_gt[j * NW + w] = (uint32_t)__popcll(bg);
+            cnt_eq[j * NW + w] = (uint32_t)__popcll(be);
         }
     }
     __syncthreads();
     {
-        const uint32_t vg = tid < J * kSelWaves ? cnt_gt[tid] : 0u;
-        const uint32_t ve = tid < J * kSelWaves ? cnt_eq[tid] : 0u;
-        const uint32_t ig = block_incl_scan(vg, wsum);
-        const uint32_t ie = block_incl_scan(ve, wsum);
-        if (tid < J * kSelWaves) {
+        const uint32_t vg = tid < J * NW ? cnt_gt[tid] : 0u;
+        const uint32_t ve = tid < J * NW ? cnt_eq[tid] : 0u;
+        const uint32_t ig = block_incl_scan<NT>(vg, wsum);
+        const uint32_t ie = block_incl_scan<NT>(ve, wsum);
+        if (tid < J * NW) {
             cnt_gt[tid] = ig - vg;
             cnt_eq[tid] = ie - ve;
         }
@@ -457,11 +467,11 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
     for (int j = 0; j < J; ++j) {
         TRI_CLASSIFY(j, gt, eq)
         const uint64_t bg = __ballot(gt), be = __ballot(eq);
-        const int eb = (int)cnt_eq[j * kSelWaves + w] + __popcll(be & below);
-        const int gb = (int)cnt_gt[j * kSelWaves + w] + __popcll(bg & below);
+        const int eb = (int)cnt_eq[j * NW + w] + __popcll(be & below);
+        const int gb = (int)cnt_gt[j * NW + w] + __popcll(bg & below);
         const int out = gb + min(eb, need);
         if ((gt || (eq && eb < need)) && out < nk) {
-            int slot = j * kSelThreads + tid;
+            int slot = j * NT + tid;
             if constexpr (CAND) {
                 if (!all) slot = cand_slot(slot, N, pre, mw);
             }
@@ -494,21 +504,21 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         // scratch and LDS, with a wait after every load; two pieces in the
         // instances built for 64 registers)
         constexpr int UP = LOW_REGS ? 2 : 4;
-        const int per = (kSelThreads * UP) >> lg;       // rows per batch (<= 512: rows are >= 128 bytes)
+        const int per = (NT * UP) >> lg;       // rows per batch (<= 512: rows are >= 128 bytes)
         for (int j0 = lo; j0 < nk; j0 += per) {
             const int lim = min(per, nk - j0) * cpr;    // 16-byte pieces in the batch
             uint4 k0, k1, k2, k3, v0, v1, v2, v3;
             int32_t pv = 0;
 #define TRI_IP_LOAD(u, kx, vx)                                                              \
-            if ((u) * kSelThreads + tid < lim) {                                            \
-                const int e = (u) * kSelThreads + tid;                                      \
+            if ((u) * NT + tid < lim) {                                            \
+                const int e = (u) * NT + tid;                                      \
                 const int64_t sr = a.src.row(s, kept[j0 + (e >> lg)]);                     \
                 kx = reinterpret_cast<const uint4*>(a.src.k + sr * a.row_bytes)[e & (cpr - 1)]; \
                 vx = reinterpret_cast<const uint4*>(a.src.v + sr * a.row_bytes)[e & (cpr - 1)]; \
             }
 #define TRI_IP_STORE(u, kx, vx)                                                             \
-            if ((u) * kSelThreads + tid < lim) {                                            \
-                const int e = (u) * kSelThreads + tid;                                      \
+            if ((u) * NT + tid < lim) {                                            \
+                const int e = (u) * NT + tid;                                      \
                 const int64_t dr = a.dst.row(s, j0 + (e >> lg));                           \
                 reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[e & (cpr - 1)] = kx;  \
                 reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[e & (cpr - 1)] = vx;  \
@@ -552,7 +562,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         const int c = lo, m = nk - c;
         for (int base = 0; base < m; base += 2048) {
             const int nb = min(2048, m - base);
-            for (int r = tid; r < nb; r += kSelThreads) {
+            for (int r = tid; r < nb; r += NT) {
                 int l2 = 0, h2 = c;
                 while (l2 < h2) {
                     const int mid = (l2 + h2) >> 1;
@@ -562,7 +572,7 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
                 hist[r] = (uint32_t)(base + r + l2);
             }
             __syncthreads();
-            for (int u = tid; u < nb * cpr; u += kSelThreads) {
+            for (int u = tid; u < nb * cpr; u += NT) {
                 const int jr = u >> lg, q = u & (cpr - 1);
                 const int64_t sr = a.src.row(s, kept[c + base + jr]);
                 const int64_t dr = a.dst.row(s, (int)hist[jr]);
@@ -571,34 +581,71 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
                 reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[q] = kv;
                 reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[q] = vv;
             }
-            for (int jr = tid; jr < nb; jr += kSelThreads)
+            for (int jr = tid; jr < nb; jr += NT)
                 a.dst.pos[a.dst.row(s, (int)hist[jr])] = a.src.pos[a.src.row(s, kept[c + base + jr])];
             __syncthreads();                            // hist is refilled by the next batch
         }
         return;
     }
 
-    // ---- compaction of the kept rows (16-byte copies), then positions
+    // ---- compaction of the kept rows (16-byte copies), then positions.  Each
+    // thread issues all the loads of a batch (UG K and UG V pieces, in named
+    // registers) before its stores, so a workgroup keeps UG times more bytes in
+    // flight than a load-store loop, which waits out one memory round trip per
+    // 16-byte piece: the gather of one workgroup then keeps up with HBM while
+    // the other workgroup on its CU is in its select phase.
+    constexpr int UG = LOW_REGS ? 4 : 8;
     const int total = nk * cpr;
-    for (int u = tid; u < total; u += kSelThreads) {
-        const int jrow = u >> lg, q = u & (cpr - 1);
-        const int64_t sr = a.src.row(s, kept[jrow]);
-        const int64_t dr = a.dst.row(s, jrow);
-        const uint4 kv = reinterpret_cast<const uint4*>(a.src.k + sr * a.row_bytes)[q];
-        const uint4 vv = reinterpret_cast<const uint4*>(a.src.v + sr * a.row_bytes)[q];
-        reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[q] = kv;
-        reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[q] = vv;
+    for (int u0 = 0; u0 < total; u0 += NT * UG) {
+        uint4 k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+#define TRI_G_LOAD(i, kx, vx)                                                                  \
+        if (u0 + (i) * NT + tid < total) {                                            \
+            const int u = u0 + (i) * NT + tid;                                        \
+            const int64_t sr = a.src.row(s, kept[u >> lg]);                                    \
+            kx = reinterpret_cast<const uint4*>(a.src.k + sr * a.row_bytes)[u & (cpr - 1)];    \
+            vx = reinterpret_cast<const uint4*>(a.src.v + sr * a.row_bytes)[u & (cpr - 1)];    \
+        }
+#define TRI_G_STORE(i, kx, vx)                                                                 \
+        if (u0 + (i) * NT + tid < total) {                                            \
+            const int u = u0 + (i) * NT + tid;                                        \
+            const int64_t dr = a.dst.row(s, u >> lg);                                          \
+            reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[u & (cpr - 1)] = kx;          \
+            reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[u & (cpr - 1)] = vx;          \
+        }
+        TRI_G_LOAD(0, k0, v0)
+        TRI_G_LOAD(1, k1, v1)
+        TRI_G_LOAD(2, k2, v2)
+        TRI_G_LOAD(3, k3, v3)
+        if constexpr (UG == 8) {
+            TRI_G_LOAD(4, k4, v4)
+            TRI_G_LOAD(5, k5, v5)
+            TRI_G_LOAD(6, k6, v6)
+            TRI_G_LOAD(7, k7, v7)
+        }
+        TRI_G_STORE(0, k0, v0)
+        TRI_G_STORE(1, k1, v1)
+        TRI_G_STORE(2, k2, v2)
+        TRI_G_STORE(3, k3, v3)
+        if constexpr (UG == 8) {
+            TRI_G_STORE(4, k4, v4)
+            TRI_G_STORE(5, k5, v5)
+            TRI_G_STORE(6, k6, v6)
+            TRI_G_STORE(7, k7, v7)
+        }
+#undef TRI_G_LOAD
+#undef TRI_G_STORE
     }
-    for (int jrow = tid; jrow < nk; jrow += kSelThreads)
+    for (int jrow = tid; jrow < nk; jrow += NT)
         a.dst.pos[a.dst.row(s, jrow)] = a.src.pos[a.src.row(s, kept[jrow])];
 }
 
-// J <= 16, G <= 4: two workgroups per CU (at most 64 VGPRs and the SGPRs of 8 waves per
-// SIMD), so one workgroup's gather overlaps the other's select phase.
-template <int J, int G, int MODE>
-__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(select_low_regs(J, G) ? 8 : 1))) void k_select(
+// J <= 16, G <= 4 (and every 256-thread instance): at most 64 VGPRs and the
+// SGPRs of 8 waves per SIMD, so two 1024-thread (or eight 256-thread)
+// workgroups share a CU and one's gather overlaps another's select phase.
+template <int J, int G, int MODE, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(select_low_regs(J, G, NT) ? 8 : 1))) void k_select(
     SelectArgs a) {
-    select_segment<J, G, MODE>(a, blockIdx.x);
+    select_segment<J, G, MODE, NT>(a, blockIdx.x);
 }
 
 // Mode S over the segments whose candidate pass failed its certificate.
@@ -611,37 +658,45 @@ __global__ __launch_bounds__(kSelThreads) void k_select_fallback(SelectArgs a) {
     }
 }
 
-template <int J, int G>
+template <int J, int G, int NT>
 static bool select_launch(const SelectArgs& a, int mode, hipStream_t stream) {
-    const dim3 block(kSelThreads);
+    const dim3 block(NT);
     if (mode == SELECT_S_FALLBACK) {
-        if constexpr (G > 0)
+        if constexpr (G > 0 && NT == kSelThreads)
             hipLaunchKernelGGL((k_select_fallback<J, G>), dim3((unsigned)(a.n_seg < 512 ? a.n_seg : 512)), block, 0, stream, a);
-        return G > 0;
+        return G > 0 && NT == kSelThreads;
     }
     const dim3 grid((unsigned)a.n_seg);
     if constexpr (G == 0) {
-        hipLaunchKernelGGL((k_select<J, 0, SELECT_A>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((k_select<J, 0, SELECT_A, NT>), grid, block, 0, stream, a);
     } else if (mode == SELECT_C) {
-        hipLaunchKernelGGL((k_select<J, G, SELECT_C>), grid, block, 0, stream, a);
+        if constexpr (NT == kSelThreads) hipLaunchKernelGGL((k_select<J, G, SELECT_C, NT>), grid, block, 0, stream, a);
+        else return false;
     } else {
-        hipLaunchKernelGGL((k_select<J, G, SELECT_S>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((k_select<J, G, SELECT_S, NT>), grid, block, 0, stream, a);
     }
     return true;
 }
 
-template <int J>
+template <int J, int NT = kSelThreads>
 static bool select_group(const SelectArgs& a, int group, int mode, hipStream_t stream) {
     if ((group == 0) != (mode == SELECT_A)) return false;
     switch (group) {
-        case 0: return select_launch<J, 0>(a, mode, stream);
-        case 1: return select_launch<J, 1>(a, mode, stream);
-        case 2: return select_launch<J, 2>(a, mode, stream);
-        case 4: return select_launch<J, 4>(a, mode, stream);
-        case 8: return select_launch<J, 8>(a, mode, stream);
+        case 0: return select_launch<J, 0, NT>(a, mode, stream);
+        case 1: return select_launch<J, 1, NT>(a, mode, stream);
+        case 2: return select_launch<J, 2, NT>(a, mode, stream);
+        case 4: return select_launch<J, 4, NT>(a, mode, stream);
+        case 8: return select_launch<J, 8, NT>(a, mode, stream);
         default: return false;
     }
 }
+
+// Segments of at most this many keys are selected by 256-thread workgroups:
+// eight of them share a CU, so the latency-bound select phases (statistics
+// merge, three radix passes, emission, each a chain of block barriers) of
+// many short segments overlap, where a 1024-thread workgroup would hold a
+// quarter of a CU for a segment that fills a fraction of its threads.
+constexpr int64_t kSmallSegKeys = 4096;
 
 hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_len, hipStream_t stream) {
     if (a.n_seg == 0) return hipSuccess;
@@ -660,7 +715,13 @@ hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_l
     const KernelId id = mode == SELECT_S_FALLBACK ? KID_SELECT_FALLBACK : a.gather ? KID_SELECT_GATHER : KID_SELECT;
     TimedLaunch tl(id, stream);
     bool ok;
-    if (held <= 2 * kSelThreads) ok = select_group<2>(a, group, mode, stream);
+    constexpr int ST = 256;
+    if (mode != SELECT_C && mode != SELECT_S_FALLBACK && held <= kSmallSegKeys) {
+        if (held <= 4 * ST) ok = select_group<4, ST>(a, group, mode, stream);
+        else if (held <= 8 * ST) ok = select_group<8, ST>(a, group, mode, stream);
+        else ok = select_group<16, ST>(a, group, mode, stream);
+    }
+    else if (held <= 2 * kSelThreads) ok = select_group<2>(a, group, mode, stream);
     else if (held <= 8 * kSelThreads) ok = select_group<8>(a, group, mode, stream);
     else if (mode == SELECT_C && held <= 16 * kSelThreads) ok = select_group<16>(a, group, mode, stream);
     else if (held <= 32 * kSelThreads) ok = select_group<32>(a, group, mode, stream);

@@ -123,7 +123,7 @@ def test_equal_scores_keep_lowest_slots(gpu_lib):
 
 
 @pytest.mark.parametrize("with_pos", [False, True])
-@pytest.mark.parametrize("cap", [2048, 8192, 32768, 32896, 40000, 65536])
+@pytest.mark.parametrize("cap", [700, 2048, 4096, 8192, 32768, 32896, 40000, 65536])
 def test_select_kernel_bit_exact(gpu_lib, cap, with_pos):
     """tri_select_topb on seeded score arrays (ties, signed zeros, all-equal)
     equals the oracle's selection exactly; with positions (tri_select_topb_ex:
