@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtriattn.so")
+# TRIATTN_LIB: another build of the same library (the CPU sanitizer test loads
+# one built with AddressSanitizer); by default the in-tree build.
+LIB_PATH = os.environ.get("TRIATTN_LIB") or os.path.join(_HERE, "libtriattn.so")
 
 TRI_OK = 0
 TRI_ERR_INVALID_ARG = -1
