@@ -203,7 +203,11 @@ int tri_select_topb_ex(const float* agg, const int32_t* pos, const int32_t* leng
 /*
  * Compaction: for each segment, dst slot j <- src slot idx[s][j] for
  * j < n_kept[s] (K row, V row and position, bit-exact).  Out of place: dst
- * must not share memory with src.  dst describes a cache with the same
+ * must not share memory with src (TRI_ERR_INVALID_ARG when dense arrays
+ * overlap by any byte, or paged caches share a base address), except that a
+ * paged dst may use src's pool through a different page table: its pages
+ * must then be pages src does not use (fresh pages of a shared pool; not
+ * checked).  dst describes a cache with the same
  * n_layers/n_seq/n_kv_heads/head_dim/dtype; its lengths are not written
  * (n_kept holds them).  idx rows are budget apart.
  */
@@ -227,7 +231,8 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
  * 0..n_kept[s]-1 in their old slot order.  Rows before the first dropped slot
  * stay where they are and are not copied; every later kept row moves down.
  * Segments with lengths[s] <= budget are not touched.  n_kept may then be
- * src->lengths itself.  Any other sharing of memory between src and dst is
+ * src->lengths itself.  Out of place, dst and src share memory only as
+ * tri_compact allows (fresh pages of src's pool); any other overlap is
  * TRI_ERR_INVALID_ARG.  dst must hold min(budget, src->capacity) rows per
  * segment (else TRI_ERR_INVALID_ARG); a cache whose capacity is below the
  * budget is copied through, or left as it is in place.

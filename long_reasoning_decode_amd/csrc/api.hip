@@ -500,8 +500,43 @@ static bool same_storage(const tri_cache_desc* s, const tri_cache_desc* d) {
     return true;
 }
 
+// Bytes a dense cache's k (or v) array spans, and its pos array.
+static int64_t dense_kv_bytes(const tri_cache_desc* c) {
+    return n_segments(c) * (int64_t)c->capacity * c->head_dim * elem_size(c->dtype);
+}
+static bool ranges_meet(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+// Whether dst's storage may overlap src's where a compaction writes.  Dense
+// caches: any byte of dst's k, v or pos arrays inside src's (their extents
+// are known).  Paged caches: a pool's size is not in the descriptor, so only
+// the base addresses are compared; two paged caches on the same pool with
+// different page tables are accepted (the caller guarantees that dst's pages
+// are not src's pages: fresh pages of a shared pool), any other shared base is
+// refused.
+static bool storage_overlaps(const tri_cache_desc* s, const tri_cache_desc* d) {
+    if (s->layout == TRI_LAYOUT_DENSE && d->layout == TRI_LAYOUT_DENSE) {
+        const int64_t ns = dense_kv_bytes(s), nd = dense_kv_bytes(d);
+        const int64_t ps = n_segments(s) * (int64_t)s->capacity * 4, pd = n_segments(d) * (int64_t)d->capacity * 4;
+        const void* sa[3] = {s->k, s->v, s->pos};
+        const int64_t sn[3] = {ns, ns, ps};
+        const void* da[3] = {d->k, d->v, d->pos};
+        const int64_t dn[3] = {nd, nd, pd};
+        for (int i = 0; i < 3; ++i)
+            for (int j = 0; j < 3; ++j)
+                if (ranges_meet(sa[i], sn[i], da[j], dn[j])) return true;
+        return false;
+    }
+    const bool same_base = d->k == s->k || d->v == s->v || d->pos == s->pos || d->k == s->v || d->v == s->k;
+    if (s->layout == TRI_LAYOUT_PAGED && d->layout == TRI_LAYOUT_PAGED && same_base)
+        return !(d->k == s->k && d->v == s->v && d->pos == s->pos && d->page_table != s->page_table);
+    return same_base;
+}
+
 // src -> dst compaction arguments.  With `in_place` non-null, a dst that names
-// src's storage is accepted (and reported); any other sharing is an error.
+// src's storage is accepted (and reported); any other overlap is an error.
 // dst must hold `budget` rows per segment for tri_compact (its kept counts
 // come from the caller), and min(budget, src capacity) for a pruning pass,
 // which keeps at most that many (a cache smaller than the budget is copied
@@ -518,9 +553,7 @@ static int check_pair(const tri_cache_desc* src, const tri_cache_desc* dst, int 
     const int64_t rows = pruning && src->capacity < budget ? src->capacity : budget;
     if (dst->capacity < rows) return TRI_ERR_INVALID_ARG;
     if (in_place) *in_place = same_storage(src, dst);
-    if (!(in_place && *in_place) &&
-        (dst->k == src->k || dst->v == src->v || dst->pos == src->pos || dst->k == src->v || dst->v == src->k))
-        return TRI_ERR_INVALID_ARG;
+    if (!(in_place && *in_place) && storage_overlaps(src, dst)) return TRI_ERR_INVALID_ARG;
     if (budget > kMaxBudget) return TRI_ERR_UNSUPPORTED;
     return TRI_OK;
 }

@@ -235,3 +235,44 @@ def test_append_refuses_paged_caches():
     p = torch.zeros(2, dtype=torch.int32)
     assert lib.tri_append(ctypes.byref(d), T._p(kn), T._p(kn), T._p(p), None) == T.TRI_ERR_UNSUPPORTED
     assert lib.tri_append(ctypes.byref(d), None, T._p(kn), T._p(p), None) == T.TRI_ERR_INVALID_ARG
+
+
+def test_compaction_refuses_overlapping_storage():
+    """Out-of-place compaction: dense arrays that overlap src's by any byte are
+    refused before any launch; adjacent arrays are not; a paged dst on src's
+    pool through another page table (fresh pages of a shared pool) is
+    accepted, the same page table is not (that is src itself)."""
+    lib = T.load()
+    idx = torch.zeros(4, 8, dtype=torch.int32)
+    nk = torch.zeros(4, dtype=torch.int32)
+    big = torch.zeros(3 * 4 * 16 * 64, dtype=torch.bfloat16)        # room for k, v and a shifted k
+    pos = torch.zeros(2 * 4 * 16, dtype=torch.int32)
+    ln = torch.zeros(4, dtype=torch.int32)
+    kv_elems = 4 * 16 * 64
+
+    def dense(k_off, v_off, p_off):
+        d = T.cache_desc(big[:kv_elems].view(4, 16, 64), big[:kv_elems].view(4, 16, 64), pos[:64].view(4, 16), ln,
+                         n_layers=1, n_seq=2, n_kv_heads=2)
+        d.k = big.data_ptr() + 2 * k_off
+        d.v = big.data_ptr() + 2 * v_off
+        d.pos = pos.data_ptr() + 4 * p_off
+        return d
+
+    def compact(src, dst):
+        return lib.tri_compact(ctypes.byref(src), T._p(idx), T._p(nk), 8, ctypes.byref(dst), None)
+
+    src = dense(0, kv_elems, 0)
+    ok = T.TRI_ERR_NO_DEVICE if not torch.cuda.is_available() else None
+    assert compact(src, dense(2 * kv_elems - 64, 2 * kv_elems + 0, 64)) == T.TRI_ERR_INVALID_ARG   # dst.k in src.v
+    assert compact(src, dense(2 * kv_elems, 2 * kv_elems, 32)) == T.TRI_ERR_INVALID_ARG            # pos overlap
+    if ok is not None:
+        assert compact(src, dense(2 * kv_elems, 2 * kv_elems, 64)) == ok                           # adjacent
+    pool = torch.zeros(16, 16, 64, dtype=torch.bfloat16)
+    ppos = torch.zeros(16, 16, dtype=torch.int32)
+    pt_src = torch.arange(8, dtype=torch.int32).view(4, 2)
+    pt_dst = torch.arange(8, 16, dtype=torch.int32).view(4, 2)
+    paged = lambda pt: T.cache_desc(pool, pool, ppos, ln, n_layers=1, n_seq=2, n_kv_heads=2, page_table=pt,
+                                    page_size=16, max_pages=2)
+    assert compact(paged(pt_src), paged(pt_src)) == T.TRI_ERR_INVALID_ARG
+    if ok is not None:
+        assert compact(paged(pt_src), paged(pt_dst)) == ok

@@ -217,6 +217,45 @@ def test_paged_small_every_step(gpu_lib, page_size, dtype):
         check_compaction(K, V, P, Kd, Vd, Pd, ix, tag)
 
 
+def test_paged_prune_into_fresh_pages_of_the_same_pool(gpu_lib):
+    """Out of place into pages of the source's own pool (a second page table
+    over pages the source does not use): the same pages' contents as pruning
+    into a separate pool, and the source pages untouched."""
+    T = gpu_lib
+    cfg = W.CONFIGS["ragged"].replace(n_seq=3, len_range=(100, 3000), budget=256, seed=5)
+    log("case paged prune into the source pool")
+    pc = W.paged_cache(cfg, "cpu")
+    g = _to(pc, "cuda")
+    calib, _ = calib_for(T, cfg)
+    B = cfg.budget
+    src = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["page_table"], page_size=cfg.page_size,
+                       max_pages=g["max_pages"])
+    ws = T.workspace(calib, src, B)
+    nk = torch.zeros((cfg.n_seg,), dtype=torch.int32, device="cuda")
+    sep = T.cache_desc(g["out_k"], g["out_v"], g["out_pos"], nk, n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["out_page_table"], page_size=cfg.page_size,
+                       max_pages=g["out_max_pages"])
+    T.tri_prune_window(calib, src, g["t"], B, sep, nk, ws)
+    # one pool holding the source pages and, after them, the fresh pages
+    n_src = g["k"].shape[0]
+    pool = {key: torch.cat([g[key], torch.zeros_like(g["out_" + key])]) for key in ("k", "v", "pos")}
+    src2 = T.cache_desc(pool["k"], pool["v"], pool["pos"], g["lengths"], n_layers=1, n_seq=cfg.n_seq,
+                        n_kv_heads=cfg.n_kv_heads, page_table=g["page_table"], page_size=cfg.page_size,
+                        max_pages=g["max_pages"])
+    pt2 = (g["out_page_table"] + n_src).contiguous()
+    nk2 = torch.zeros_like(nk)
+    dst2 = T.cache_desc(pool["k"], pool["v"], pool["pos"], nk2, n_layers=1, n_seq=cfg.n_seq,
+                        n_kv_heads=cfg.n_kv_heads, page_table=pt2, page_size=cfg.page_size,
+                        max_pages=g["out_max_pages"])
+    T.tri_prune_window(calib, src2, g["t"], B, dst2, nk2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(nk2, nk)
+    for key in ("k", "v", "pos"):
+        assert torch.equal(pool[key][n_src:], g["out_" + key]), f"{key}: fresh pages differ from the separate pool"
+        assert torch.equal(pool[key][:n_src], g[key]), f"{key}: source pages were written"
+
+
 @pytest.mark.parametrize("in_place", [False, True, "fill"])
 def test_decode_loop_small(gpu_lib, in_place):
     """Append + decode attention each step, prune after each window (into the
