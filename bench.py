@@ -578,7 +578,7 @@ def main():
             kernels[name] = {"avg_ms": round(avg, 4), "launches": launches,
                              "algorithmic_bytes": bytes_per_launch,
                              "achieved_GBs": round(bytes_per_launch / (avg * 1e-3) / 1e9, 1)}
-    for name in ("phase", "sample", "select", "score_fallback", "select_fallback"):
+    for name in ("phase", "sample", "select", "split_select", "score_fallback", "select_fallback"):
         launches, total = kt.get(name, (0, 0.0))
         if launches:
             kernels[name] = {"avg_ms": round(total / launches, 4), "launches": launches}

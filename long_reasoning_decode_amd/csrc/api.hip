@@ -58,7 +58,7 @@ int64_t g_launches[KID_COUNT] = {};
 double g_ms[KID_COUNT] = {};
 const char* kKernelNames[KID_COUNT] = {"phase",  "score",  "zmax",   "select",         "select_gather",
                                        "gather", "append", "decode_attn", "sample", "score_fallback",
-                                       "select_fallback", "calibrate", "calibrate_final"};
+                                       "select_fallback", "calibrate", "calibrate_final", "split_select"};
 
 void drain_timing_locked() {
     for (auto& p : g_pending) {
@@ -178,7 +178,7 @@ int pick_chunk(const tri_cache_desc* kv) {
 // Workspace layout.  The fallback counter of the last pruning pass sits at
 // offset 0 so tri_prune_fallbacks can find it without the cache shape.
 struct WsPlan {
-    size_t fb_count, fb_list, ctab, stats, thr, masks, s_int, idx, total;
+    size_t fb_count, fb_list, ctab, stats, thr, masks, s_int, idx, akey, shist, ccnt, total;
     int64_t mask_stride;
 };
 
@@ -189,6 +189,19 @@ struct WsPlan {
 // segment.
 constexpr int64_t kSplitGatherSegs = 256;
 bool split_gather(const tri_cache_desc* kv) { return n_segments(kv) < kSplitGatherSegs; }
+
+// Fewer segments than CUs, of many keys: the select runs one workgroup per
+// (segment, chunk) (launch_split_select) instead of one per segment, which
+// would leave most CUs idle (one 32K-key layer: 8 workgroups; its select 57 ->
+// about 40 us).  Out of place only; the kept rows are then copied by the
+// many-workgroup gather.  Not for batches that fill the GPU: on the ragged
+// batch (512 segments of 4K..64K keys) the split select and the separate
+// gather took 0.55 + 0.46 ms against 0.75 ms for the fused select + gather.
+constexpr int64_t kSplitSelectMinCap = 8192;
+bool split_select(const tri_cache_desc* kv) {
+    return n_segments(kv) < kSplitGatherSegs && kv->capacity >= kSplitSelectMinCap;
+}
+constexpr int kSplitHistWords = 3 * 2048 + 8;      // per segment: three digit histograms, then its state
 
 WsPlan plan_workspace(const tri_calib_s* c, const tri_cache_desc* kv) {
     const int64_t n_seg = n_segments(kv);
@@ -204,7 +217,11 @@ WsPlan plan_workspace(const tri_calib_s* c, const tri_cache_desc* kv) {
     p.s_int = p.masks + align256((size_t)n_seg * p.mask_stride * c->G * sizeof(uint32_t));
     p.idx = p.s_int + align256((size_t)n_seg * kv->capacity * c->G * sizeof(float));
     const int64_t idx_len = kv->capacity < kMaxBudget ? kv->capacity : kMaxBudget;   // budget <= both
-    p.total = p.idx + (split_gather(kv) ? align256((size_t)n_seg * idx_len * sizeof(int32_t)) : 0);
+    const bool ssel = split_select(kv);
+    p.akey = p.idx + (split_gather(kv) || ssel ? align256((size_t)n_seg * idx_len * sizeof(int32_t)) : 0);
+    p.shist = p.akey + (ssel ? align256((size_t)n_seg * kv->capacity * sizeof(uint32_t)) : 0);
+    p.ccnt = p.shist + (ssel ? align256((size_t)n_seg * kSplitHistWords * sizeof(uint32_t)) : 0);
+    p.total = p.ccnt + (ssel ? align256((size_t)n_seg * max_chunks * 2 * sizeof(uint32_t)) : 0);
     return p;
 }
 
@@ -671,7 +688,8 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
     a.lengths = src->lengths;
     a.budget = budget;
     a.n_kept = n_kept;
-    const bool split = !in_place && split_gather(src);
+    const bool ssel = !in_place && split_select(src);
+    const bool split = !in_place && (split_gather(src) || ssel);
     a.gather = in_place ? (fill ? GATHER_IN_PLACE_FILL : GATHER_IN_PLACE) : split ? GATHER_NONE : GATHER_COPY;
     a.tie = TIE_POS_CACHE;
     a.src = view_of(src);
@@ -699,7 +717,40 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
         ga.n_seg = a.n_seg;
         return hip_status(launch_gather(ga, st), "gather kernel");
     };
-    if (!cand) {
+    if (ssel) {
+        // split select; segments it lists (ties at the cut beyond the budget,
+        // failed certificates) go through the fallback kernels below
+        SplitSelArgs ss;
+        ss.s_int = s_int;
+        ss.stats = stats;
+        ss.thr = reinterpret_cast<const float*>(w + p.thr);
+        ss.masks = reinterpret_cast<const uint32_t*>(w + p.masks);
+        ss.mask_stride = p.mask_stride;
+        ss.chunk = chunk;
+        ss.n_chunks = a.n_chunks;
+        ss.cap = src->capacity;
+        ss.lengths = src->lengths;
+        ss.budget = budget;
+        ss.akey = reinterpret_cast<uint32_t*>(w + p.akey);
+        ss.hist = reinterpret_cast<uint32_t*>(w + p.shist);
+        ss.ccnt = reinterpret_cast<uint32_t*>(w + p.ccnt);
+        ss.state = ss.hist + (int64_t)a.n_seg * 3 * 2048;
+        ss.fb_list = reinterpret_cast<int32_t*>(w + p.fb_list);
+        ss.fb_count = reinterpret_cast<int32_t*>(w + p.fb_count);
+        ss.idx = a.idx_out;
+        ss.idx_stride = idx_stride;
+        ss.n_kept = n_kept;
+        ss.n_seg = a.n_seg;
+        if ((rc = hip_status(launch_split_select(ss, calib->G, cand, st), "split select kernels"))) return rc;
+        a.fb_list = ss.fb_list;
+        a.fb_count = ss.fb_count;
+        if (!cand) {
+            if ((rc = hip_status(launch_select(a, calib->G, SELECT_S_FALLBACK, src->capacity, st),
+                                 "fallback select kernel")))
+                return rc;
+            return gather_split();
+        }
+    } else if (!cand) {
         if ((rc = hip_status(launch_select(a, calib->G, SELECT_S, src->capacity, st), "select+gather kernel")))
             return rc;
         return gather_split();
@@ -709,7 +760,7 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
     a.mask_stride = p.mask_stride;
     a.fb_list = reinterpret_cast<int32_t*>(w + p.fb_list);
     a.fb_count = reinterpret_cast<int32_t*>(w + p.fb_count);
-    if ((rc = hip_status(launch_select(a, calib->G, SELECT_C, src->capacity, st), "select+gather kernel")))
+    if (!ssel && (rc = hip_status(launch_select(a, calib->G, SELECT_C, src->capacity, st), "select+gather kernel")))
         return rc;
     ScoreArgs sa;
     memset(&sa, 0, sizeof sa);

@@ -23,6 +23,7 @@ enum KernelId : int {
     KID_SELECT_FALLBACK,
     KID_CALIB,
     KID_CALIB_FINAL,
+    KID_SPLIT_SELECT,
     KID_COUNT
 };
 
@@ -166,6 +167,37 @@ enum TieMode : int { TIE_SLOT = 0, TIE_POS_ARRAY = 1, TIE_POS_CACHE = 2 };
 // mode S over the segments listed in fb_list.
 enum SelectMode : int { SELECT_A = 0, SELECT_S = 1, SELECT_C = 2, SELECT_S_FALLBACK = 3 };
 hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_len, hipStream_t stream);
+
+// --- split select: the top-B of each segment over many workgroups, one per
+// (segment, chunk of keys), in five launches (aggregate + first digit
+// histogram, second digit, third digit, per-chunk counts, ordered emission).
+// Kept slots go to idx (rows idx_stride apart) and n_kept; the rows are then
+// copied by launch_gather.  A segment whose keys tie at the cut with more
+// keys than fit (the position rule needs the single-workgroup select), or in
+// candidate mode whose certificate fails, is listed in fb_list and left to
+// the fallback kernels.
+struct SplitSelArgs {
+    const float* s_int;     // mode S: [n_seg][cap][G]; mode C: the chunks' candidate lists
+    const double2* stats;   // [n_seg][n_chunks][G]
+    const float* thr;       // mode C: [n_seg][G]
+    const uint32_t* masks;  // mode C: [n_seg][mask_stride][G]
+    int64_t mask_stride;
+    int32_t chunk, n_chunks;
+    int64_t cap;
+    const int32_t* lengths;
+    int32_t budget;
+    uint32_t* akey;         // workspace [n_seg][cap]: order keys of the aggregates
+    uint32_t* hist;         // workspace [n_seg][3][2048]: digit histograms (zeroed by the first launch's fill)
+    uint32_t* ccnt;         // workspace [n_seg][n_chunks][2]: keys above / at the cut per chunk
+    uint32_t* state;        // workspace [n_seg][4]: N, cut, how many at the cut to keep, fallback flag
+    int32_t* fb_list;
+    int32_t* fb_count;
+    int32_t* idx;           // [n_seg][idx_stride]
+    int64_t idx_stride;
+    int32_t* n_kept;
+    int32_t n_seg;
+};
+hipError_t launch_split_select(const SplitSelArgs& a, int group, bool cand, hipStream_t stream);
 
 // --- gather (unfused compaction)
 struct GatherArgs {

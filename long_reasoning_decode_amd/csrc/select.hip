@@ -732,6 +732,369 @@ hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_l
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ split select
+// The top-B of a segment computed by one 256-thread workgroup per (segment,
+// chunk of keys) instead of one workgroup per segment, for batches with few or
+// uneven segments, where one workgroup per segment leaves most of the chip
+// idle.  Same radix select as select_segment (11 + 11 + 10 bit digits of the
+// aggregate's order key), with the histograms summed over a segment's chunks
+// in the workspace, one launch per digit:
+//   1. each chunk forms its keys' aggregates (exactly as select_segment: the
+//      same statistics merge and aggregate, so the same bits), stores their
+//      order keys and adds its first-digit histogram to the segment's;
+//   2, 3. each chunk reads the finished histograms of the digits before, picks
+//      the digit holding the B-th key, and histograms the next digit of its
+//      keys that match;
+//   4. the cut T, how many keys at T to keep, and each chunk's counts of keys
+//      above and at T; a segment with more keys at T than fit (the tie rule
+//      needs positions) or, in candidate mode, a failed certificate goes to
+//      the fallback list;
+//   5. each chunk emits its kept slots at their places in slot order.
+constexpr int kSplitThreads = 256;
+constexpr int kSplitState = 8;     // words of per-segment state
+constexpr int kSplitHist = 3 * 2048;
+
+// Digit level lv of the radix select: shift and mask of its bits.
+__device__ __forceinline__ int split_shift(int lv) { return lv == 0 ? 21 : lv == 1 ? 10 : 0; }
+__device__ __forceinline__ uint32_t split_mask(int lv) { return lv < 2 ? 0x7ffu : 0x3ffu; }
+
+// Walks the segment's finished histograms of levels 0..levels-1: the prefix
+// of the cut, its mask, the keys at or above the cut still needed, and the
+// count of keys in the last picked bin.
+__device__ __forceinline__ void split_walk(const uint32_t* hist, int levels, int budget, uint32_t& prefix,
+                                           uint32_t& pmask, int& need, uint32_t& n_at, uint32_t* wsum,
+                                           uint32_t* pick) {
+    constexpr int HB = 2048 / kSplitThreads;
+    const int tid = threadIdx.x;
+    prefix = 0u;
+    pmask = 0u;
+    need = budget;
+    n_at = 0u;
+    for (int lv = 0; lv < levels; ++lv) {
+        const uint32_t* h = hist + lv * 2048;
+        if (tid == 0) {
+            pick[0] = 0u;
+            pick[1] = 0u;
+            pick[2] = 0u;
+        }
+        uint32_t hv[HB], hs = 0u;
+#pragma unroll
+        for (int i = 0; i < HB; ++i) {
+            hv[i] = h[2047 - HB * tid - i];
+            hs += hv[i];
+        }
+        uint32_t above = block_incl_scan<kSplitThreads>(hs, wsum) - hs;     // (synchronises)
+        const uint32_t un = (uint32_t)need;
+#pragma unroll
+        for (int i = 0; i < HB; ++i) {
+            if (above < un && above + hv[i] >= un) {
+                pick[0] = (uint32_t)(2047 - HB * tid - i);
+                pick[1] = above;
+                pick[2] = hv[i];
+            }
+            above += hv[i];
+        }
+        __syncthreads();
+        prefix |= pick[0] << split_shift(lv);
+        pmask |= split_mask(lv) << split_shift(lv);
+        need -= (int)pick[1];
+        n_at = pick[2];
+        __syncthreads();
+    }
+}
+
+// Segment statistics as select_segment merges them (bit for bit).
+template <int G>
+__device__ __forceinline__ ZParams<G> split_zparams(const SplitSelArgs& a, int s, int N, double* scratch) {
+    const double2* st = a.stats + (int64_t)s * a.n_chunks * G;
+    return a.n_chunks <= kWave ? merge_stats_wave<G>(st, a.n_chunks, a.chunk, N)
+                               : merge_stats<G, kSplitThreads>(st, a.n_chunks, a.chunk, N, scratch);
+}
+
+__global__ __launch_bounds__(256) void k_split_fill(uint32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// Launch 1: aggregates of chunk (blockIdx.x) of segment (blockIdx.y), their
+// order keys, and the segment's first-digit histogram.
+template <int G, bool CAND>
+__global__ __launch_bounds__(kSplitThreads) void k_split_first(SplitSelArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ double scratch[(kSplitThreads / kWave + 1) * G];
+    __shared__ uint32_t hw[64 * G], fl[64], lp[64], unl[1];
+    const int s = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+    const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
+    const int c0 = c * a.chunk;
+    if (N <= a.budget || c0 >= N) return;
+    const int cnt = min(a.chunk, N - c0);
+    const ZParams<G> z = split_zparams<G>(a, s, N, scratch);
+    for (int b = tid; b < 2048; b += kSplitThreads) hist[b] = 0u;
+    if constexpr (CAND) {
+        // the chunk's mask words and, per block, the floats listed before it in
+        // its wave's list (blocks r, r - 4, ... were scored by the same wave)
+        const int nbk = (cnt + 31) / 32;
+        if (tid < nbk) {
+            const uint32_t* mp = a.masks + ((int64_t)s * a.mask_stride + c0 / 32 + tid) * G;
+            uint32_t f = 0u;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                hw[tid * G + g] = mp[g];
+                f += __popc(mp[g]);
+            }
+            fl[tid] = f;
+        }
+        if (tid == 0) unl[0] = 0u;
+        __syncthreads();
+        if (tid < nbk) {
+            uint32_t before = 0u;
+            for (int r = tid - 4; r >= 0; r -= 4) before += fl[r];
+            lp[tid] = before;
+        }
+    }
+    __syncthreads();
+    uint32_t unlisted = 0u;
+    for (int i = tid; i < cnt; i += kSplitThreads) {
+        const int k = c0 + i;
+        uint32_t key;
+        if constexpr (CAND) {
+            const int r = i >> 5, bit = i & 31;
+            const uint32_t below = (1u << bit) - 1u;
+            uint32_t any = 0u;
+            int foff = 0;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                any |= hw[r * G + g] >> bit;
+                foff += __popc(hw[r * G + g] & below);
+            }
+            if (any & 1u) {
+                const int base = wave_list_base(r & 3, cnt);
+                const float* p = a.s_int + ((int64_t)s * a.cap + c0 + base) * G + lp[r] + foff;
+                float A = -__builtin_inff();
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    if ((hw[r * G + g] >> bit) & 1u) {
+                        const float S = *p++;
+                        A = fmaxf(A, ((S - z.mu_hi[g]) - z.mu_lo[g]) * z.inv[g]);
+                    }
+                }
+                key = order_key(A);
+            } else {
+                key = 0u;                                 // below every listed key; covered by the certificate
+                ++unlisted;
+            }
+        } else {
+            float S[G];
+            const float* p = a.s_int + ((int64_t)s * a.cap + k) * G;
+#pragma unroll
+            for (int g = 0; g < G; ++g) S[g] = p[g];
+            key = order_key(aggregate<G>(S, z));
+        }
+        a.akey[(int64_t)s * a.cap + k] = key;
+        atomicAdd(&hist[key >> 21], 1u);
+    }
+    if constexpr (CAND) {
+        if (unlisted) atomicAdd(&unl[0], unlisted);
+    }
+    __syncthreads();
+    uint32_t* gh = a.hist + (int64_t)s * kSplitHist;
+    for (int b = tid; b < 2048; b += kSplitThreads)
+        if (hist[b]) atomicAdd(&gh[b], hist[b]);
+    if constexpr (CAND) {
+        if (tid == 0 && unl[0]) atomicAdd(&a.state[(int64_t)s * kSplitState + 4], unl[0]);
+    }
+}
+
+// Launches 2 and 3: histogram of digit LV of the keys matching the cut's
+// prefix so far.
+template <int LV>
+__global__ __launch_bounds__(kSplitThreads) void k_split_next(SplitSelArgs a) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t wsum[kSplitThreads / kWave], pick[3];
+    const int s = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+    const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
+    const int c0 = c * a.chunk;
+    if (N <= a.budget || c0 >= N) return;
+    const int cnt = min(a.chunk, N - c0);
+    uint32_t* gh = a.hist + (int64_t)s * kSplitHist;
+    uint32_t prefix, pmask, n_at;
+    int need;
+    split_walk(gh, LV, a.budget, prefix, pmask, need, n_at, wsum, pick);
+    for (int b = tid; b < 2048; b += kSplitThreads) hist[b] = 0u;
+    __syncthreads();
+    const uint32_t* ak = a.akey + (int64_t)s * a.cap + c0;
+    for (int i = tid; i < cnt; i += kSplitThreads) {
+        const uint32_t key = ak[i];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> split_shift(LV)) & split_mask(LV)], 1u);
+    }
+    __syncthreads();
+    for (int b = tid; b < 2048; b += kSplitThreads)
+        if (hist[b]) atomicAdd(&gh[LV * 2048 + b], hist[b]);
+}
+
+// Launch 4: the cut, the fallback decision, and each chunk's counts of keys
+// above and at the cut.
+template <int G, bool CAND>
+__global__ __launch_bounds__(kSplitThreads) void k_split_count(SplitSelArgs a) {
+    __shared__ uint32_t wsum[kSplitThreads / kWave], pick[3], red[2 * kSplitThreads / kWave];
+    __shared__ double scratch[(kSplitThreads / kWave + 1) * G];
+    const int s = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), w = tid / kWave;
+    const int N = (int)min((int64_t)max(a.lengths[s], 0), a.cap);
+    uint32_t* st = a.state + (int64_t)s * kSplitState;
+    if (c == 0 && tid == 0) st[0] = (uint32_t)N;      // launch 5 reads N here (n_kept may alias lengths)
+    const int c0 = c * a.chunk;
+    if (N <= a.budget || c0 >= N) return;
+    const int cnt = min(a.chunk, N - c0);
+    uint32_t T, pmask, n_at;
+    int need;
+    split_walk(a.hist + (int64_t)s * kSplitHist, 3, a.budget, T, pmask, need, n_at, wsum, pick);
+    bool fallback = (int)n_at > need;                 // keys tied at the cut beyond the budget: by position
+    if constexpr (CAND) {
+        if (!fallback && st[4] > 0u) {                // some keys unlisted: the certificate
+            const ZParams<G> z = split_zparams<G>(a, s, N, scratch);
+            float L[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) L[g] = a.thr[(int64_t)s * G + g];
+            fallback = !(T > order_key(aggregate<G>(L, z)));
+        }
+    }
+    if (fallback) {
+        if (c == 0 && tid == 0) {
+            st[3] = 1u;
+            a.fb_list[atomicAdd(a.fb_count, 1)] = s;
+        }
+        return;
+    }
+    if (c == 0 && tid == 0) {
+        st[1] = T;
+        st[2] = (uint32_t)need;
+    }
+    const uint32_t* ak = a.akey + (int64_t)s * a.cap + c0;
+    uint32_t ngt = 0u, neq = 0u;
+    for (int i = tid; i < cnt; i += kSplitThreads) {
+        const uint32_t key = ak[i];
+        ngt += key > T;
+        neq += key == T;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        ngt += __shfl_xor(ngt, m, kWave);
+        neq += __shfl_xor(neq, m, kWave);
+    }
+    if (lane == 0) {
+        red[2 * w] = ngt;
+        red[2 * w + 1] = neq;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t g2 = 0u, e2 = 0u;
+        for (int i = 0; i < kSplitThreads / kWave; ++i) {
+            g2 += red[2 * i];
+            e2 += red[2 * i + 1];
+        }
+        a.ccnt[((int64_t)s * a.n_chunks + c) * 2] = g2;
+        a.ccnt[((int64_t)s * a.n_chunks + c) * 2 + 1] = e2;
+    }
+}
+
+// Launch 5: kept slots of the chunk, each at its place in slot order
+// (out = keys above the cut before it + min(keys at the cut before it, need)).
+__global__ __launch_bounds__(kSplitThreads) void k_split_emit(SplitSelArgs a) {
+    __shared__ uint32_t wsum[kSplitThreads / kWave], bg_w[kSplitThreads / kWave], be_w[kSplitThreads / kWave];
+    __shared__ uint32_t base[2];
+    const int s = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), w = tid / kWave;
+    const uint32_t* st = a.state + (int64_t)s * kSplitState;
+    const int N = (int)st[0];
+    const int c0 = c * a.chunk;
+    int32_t* idx = a.idx + (int64_t)s * a.idx_stride;
+    if (N <= a.budget) {                              // every key kept, in slot order
+        for (int i = c0 + tid; i < min(N, c0 + a.chunk); i += kSplitThreads) idx[i] = i;
+        if (c == 0 && tid == 0 && a.n_kept) a.n_kept[s] = N;
+        return;
+    }
+    if (c0 >= N || st[3]) return;                     // no keys here, or left to the fallback
+    const int cnt = min(a.chunk, N - c0);
+    const uint32_t T = st[1];
+    const int need = (int)st[2];
+    // keys above and at the cut in the chunks before this one
+    {
+        uint32_t g2 = 0u, e2 = 0u;
+        for (int cc = tid; cc < c; cc += kSplitThreads) {
+            g2 += a.ccnt[((int64_t)s * a.n_chunks + cc) * 2];
+            e2 += a.ccnt[((int64_t)s * a.n_chunks + cc) * 2 + 1];
+        }
+        const uint32_t gi = block_incl_scan<kSplitThreads>(g2, wsum);
+        if (tid == kSplitThreads - 1) base[0] = gi;
+        const uint32_t ei = block_incl_scan<kSplitThreads>(e2, wsum);
+        if (tid == kSplitThreads - 1) base[1] = ei;
+        __syncthreads();
+    }
+    uint32_t gb = base[0], eb = base[1];
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    const uint32_t* ak = a.akey + (int64_t)s * a.cap + c0;
+    for (int i0 = 0; i0 < cnt; i0 += kSplitThreads) {   // block-uniform
+        const int i = i0 + tid;
+        const uint32_t key = i < cnt ? ak[i] : 0u;
+        const bool gt = i < cnt && key > T, eq = i < cnt && key == T;
+        const uint64_t mg = __ballot(gt), me = __ballot(eq);
+        if (lane == 0) {
+            bg_w[w] = (uint32_t)__popcll(mg);
+            be_w[w] = (uint32_t)__popcll(me);
+        }
+        __syncthreads();
+        uint32_t g_before = gb + (uint32_t)__popcll(mg & below), e_before = eb + (uint32_t)__popcll(me & below);
+        uint32_t g_all = 0u, e_all = 0u;
+        for (int v = 0; v < kSplitThreads / kWave; ++v) {
+            if (v < w) {
+                g_before += bg_w[v];
+                e_before += be_w[v];
+            }
+            g_all += bg_w[v];
+            e_all += be_w[v];
+        }
+        if (gt || (eq && (int)e_before < need)) {
+            const uint32_t out = g_before + min(e_before, (uint32_t)need);
+            if (out < (uint32_t)a.budget) idx[out] = c0 + i;
+        }
+        gb += g_all;
+        eb += e_all;
+        __syncthreads();                                // bg_w / be_w are rewritten next pass
+    }
+    if (c == 0 && tid == 0 && a.n_kept) a.n_kept[s] = a.budget;
+}
+
+template <int G>
+static void split_launch_g(const SplitSelArgs& a, bool cand, hipStream_t stream) {
+    const dim3 grid((unsigned)a.n_chunks, (unsigned)a.n_seg), block(kSplitThreads);
+    if (cand) hipLaunchKernelGGL((k_split_first<G, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_split_first<G, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(k_split_next<1>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(k_split_next<2>, grid, block, 0, stream, a);
+    if (cand) hipLaunchKernelGGL((k_split_count<G, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_split_count<G, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(k_split_emit, grid, block, 0, stream, a);
+}
+
+hipError_t launch_split_select(const SplitSelArgs& a, int group, bool cand, hipStream_t stream) {
+    if (a.n_seg == 0) return hipSuccess;
+    if (a.budget > kMaxBudget || a.chunk % 32 || a.chunk > 2048 || a.n_chunks > 65535) return hipErrorInvalidValue;
+    TimedLaunch tl(KID_SPLIT_SELECT, stream);
+    // histograms and state start at zero
+    const int64_t words = (int64_t)a.n_seg * (kSplitHist + kSplitState);
+    static_assert(kSplitHist % 64 == 0, "the state words follow the histograms");
+    const int64_t fill_blocks = (words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096;
+    hipLaunchKernelGGL(k_split_fill, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.hist, words);
+    switch (group) {
+        case 1: split_launch_g<1>(a, cand, stream); break;
+        case 2: split_launch_g<2>(a, cand, stream); break;
+        case 4: split_launch_g<4>(a, cand, stream); break;
+        case 8: split_launch_g<8>(a, cand, stream); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ gather
 // Unfused compaction: workgroup (segment, block of rows) copies kept rows.
 __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {

@@ -217,6 +217,49 @@ def test_paged_small_every_step(gpu_lib, page_size, dtype):
         check_compaction(K, V, P, Kd, Vd, Pd, ix, tag)
 
 
+@pytest.mark.parametrize("d,G,dtype", [(128, 4, torch.bfloat16), (64, 8, torch.bfloat16), (128, 1, torch.bfloat16),
+                                       (64, 2, torch.float32)])
+@pytest.mark.parametrize("path", ["full", "candidates"])
+def test_split_select_matches_the_single_workgroup_select(gpu_lib, d, G, dtype, path):
+    """Fewer than 256 segments of at least 8192 slots, out of place: the split
+    select (one workgroup per segment and chunk) and the many-workgroup
+    gather.  In place the same cache goes through the one-workgroup select and
+    gather, which leaves the same bytes; both are compared on lengths at and
+    around the budget, chunk boundaries and the capacity, and against the
+    oracle's selection."""
+    T = gpu_lib
+    B, cap = 600, 9000
+    cfg = W.CONFIGS["tiny"].replace(head_dim=d, group=G, dtype=dtype, theta=1e6, n_kv_heads=2, n_seq=7,
+                                    n_keys=cap, t=cap + 3, budget=B, sigma=None, seed=61)
+    log(f"case split select d={d} G={G} {dtype} {path}")
+    cpu = W.dense_cache(cfg, "cpu")
+    cpu["lengths"] = torch.tensor([0, 1, B - 1, B, B + 1, 511, 512, 513, 2047, 2049, 4096, 4801, cap - 1, cap],
+                                  dtype=torch.int32)
+    calib, cal = calib_for(T, cfg)
+    p = T.TRI_PATH_FULL if path == "full" else T.TRI_PATH_CANDIDATES
+    g = _to(cpu, "cuda")
+    desc = dense_desc(T, cfg, g)
+    ws = T.workspace(calib, desc, B)
+    out = empty_like_dense(g, B)
+    T.tri_prune_window(calib, desc, g["t"], B, dense_desc(T, cfg, out), out["lengths"], ws, path=p)
+    fb = T.tri_prune_fallbacks(ws)
+    T.tri_prune_window(calib, desc, g["t"], B, desc, g["lengths"], ws, path=p)
+    torch.cuda.synchronize()
+    log(f"  split select fallbacks: {fb}")
+    lengths = cpu["lengths"].numpy()
+    assert torch.equal(out["lengths"], g["lengths"])
+    for s in range(cfg.n_seg):
+        nk = min(int(lengths[s]), B)
+        for key in ("k", "v", "pos"):
+            assert torch.equal(out[key][s, :nk], g[key][s, :nk]), f"seg {s} N={lengths[s]}: {key} differs"
+        N = int(lengths[s])
+        if N > B:
+            P = cpu["pos"][s, :N].numpy()
+            ref = oracle_segment(cfg, cal, stored(cpu["k"][s, :N]), stored(cpu["v"][s, :N]), P,
+                                 int(cpu["t"][seg_seq(cfg, s)]), s, B)
+            check_selection(out["pos"][s, :nk].cpu().numpy(), ref["A"], B, f"split seg {s} N={N}", pos=P)
+
+
 def test_paged_prune_into_fresh_pages_of_the_same_pool(gpu_lib):
     """Out of place into pages of the source's own pool (a second page table
     over pages the source does not use): the same pages' contents as pruning
@@ -392,7 +435,9 @@ def test_candidate_pass_fallback_redoes_segment(gpu_lib):
 def test_candidate_pass_equal_scores(gpu_lib):
     """All keys identical in candidate mode (N = 8B): the sample has no spread,
     so every key is a candidate (N of them, which the select step can hold),
-    and the kept set is the lowest B slots."""
+    and the kept set is the lowest B slots.  (This one-segment batch takes the
+    split select, which hands ties at the cut beyond the budget, here every
+    key, to the single-workgroup select: one fallback.)"""
     T = gpu_lib
     cfg = W.CONFIGS["tiny"].replace(head_dim=128, dtype=torch.bfloat16, theta=1e6, n_keys=9000, t=9000, budget=1125)
     log("case candidate equal scores")
@@ -402,7 +447,7 @@ def test_candidate_pass_equal_scores(gpu_lib):
     cpu["pos"][0, :] = 5
     calib, cal = calib_for(T, cfg)
     r = _run_unfused(T, cfg, _to(cpu, "cuda"), calib, cfg.budget)
-    assert r["fallbacks"] == 0
+    assert r["fallbacks"] == 1
     assert torch.equal(r["out2"]["v"][0], cpu["v"][0, :1125])
     _check_all(cfg, cal, cpu, r, cfg.budget, cpu["lengths"].numpy(), "candidate equal")
 
