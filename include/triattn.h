@@ -144,7 +144,8 @@ int tri_calib_free(tri_calib_t calib);
  *   phase = arg of the sum of q_f (0 when that sum is 0),
  *   conc  = | mean of q_f / |q_f| |   (a sample with q_f = 0 adds no direction).
  *   q     : device [n_layers][n_samples][n_q_heads][head_dim], dtype TRI_DTYPE_*
- *           (pre-RoPE rows: one per sampled token and query head).
+ *           (pre-RoPE rows: one per sampled token and query head), 16-byte
+ *           aligned (TRI_ERR_INVALID_ARG otherwise).
  *   mag, phase, conc : device fp32 [n_layers][n_q_heads][head_dim/2] outputs,
  *           the layout tri_calib_load takes (copy them to the host for it).
  *   ws    : device workspace of tri_calibrate_workspace_size bytes, 256-byte

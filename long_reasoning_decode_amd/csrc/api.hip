@@ -875,7 +875,7 @@ int tri_calibrate(const void* q, int dtype, int n_layers, int n_samples, int n_q
                   float* phase, float* conc, void* ws, size_t ws_bytes, tri_stream_t stream) {
     int rc = check_calib_shape(n_layers, n_samples, n_q_heads, head_dim);
     if (rc) return rc;
-    if (!q || !mag || !phase || !conc) return TRI_ERR_INVALID_ARG;
+    if (!q || !mag || !phase || !conc || (reinterpret_cast<uintptr_t>(q) & 15)) return TRI_ERR_INVALID_ARG;
     if (dtype != TRI_DTYPE_F32 && dtype != TRI_DTYPE_BF16) return TRI_ERR_INVALID_ARG;
     if (!ws || ws_bytes < calib_ws_bytes(n_layers, n_samples, n_q_heads, head_dim) || !aligned256(ws))
         return TRI_ERR_WORKSPACE;

@@ -6,8 +6,9 @@
 // resultant length).  These are the inputs tri_calib_load folds.
 //
 // Layout: q [L][n_samples][Hq][d] (one row per sample and head); band f of a row
-// is q[f] + i q[f+F].  Pass 1: one-wave workgroup (layer, chunk of chunk_len
-// samples, block of 64 (head, 4-band) groups); lane t owns one group and loads
+// is q[f] + i q[f+F].  Pass 1: one wave per (layer, chunk of chunk_len samples,
+// block of 64 (head, 4-band) groups), up to eight such waves of one (layer,
+// chunk) in a workgroup; lane t owns one group and loads
 // the 4 real parts and the matching 4 imaginary parts per sample, so the wave
 // reads 1 KB of each sample's rows contiguously (four heads at head_dim 128).
 // Per sample and band it forms |q_f| and q_f/|q_f| in fp32 and adds them to
@@ -21,13 +22,29 @@
 
 namespace tri {
 
+// Waves per pass-1 workgroup: neighbouring blocks of 64 band groups of one
+// (layer, chunk) run together, so a sample's rows are read by co-resident waves.
+constexpr int kCalibWavesPerGroup = 8;
+
+// Samples are read once: non-temporal loads keep them from displacing cached lines.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint2 ldnt(const uint2* p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ inline float4 ldnt(const float4* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 1))) void k_calib_partial(CalibArgs a) {
+__global__ __launch_bounds__(64 * kCalibWavesPerGroup) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 1))) void k_calib_partial(CalibArgs a) {
     constexpr int ES = BF16 ? 2 : 4, NB = kCalibBands;
     using raw_t = typename std::conditional<BF16, uint2, float4>::type;   // one lane's NB stored values
     const int F = a.head_dim / 2, gpr = F / NB;          // band groups per head
     const int l = blockIdx.x / a.n_chunks, c = blockIdx.x - l * a.n_chunks;
-    const int g = blockIdx.y * 64 + threadIdx.x;         // (head, band group)
+    const int g = blockIdx.y * blockDim.x + threadIdx.x; // (head, band group)
     if (g >= a.n_q_heads * gpr) return;
     const int h = g / gpr, f0 = (g - h * gpr) * NB;
     const int s0 = c * a.chunk_len, s1 = min(s0 + a.chunk_len, a.n_samples);
@@ -83,16 +100,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BF16 ? 4 : 1
         raw_t rv[U], iv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            rv[u] = *reinterpret_cast<const raw_t*>(pr + (int64_t)(s + u) * sstride);
-            iv[u] = *reinterpret_cast<const raw_t*>(pi + (int64_t)(s + u) * sstride);
+            rv[u] = ldnt(reinterpret_cast<const raw_t*>(pr + (int64_t)(s + u) * sstride));
+            iv[u] = ldnt(reinterpret_cast<const raw_t*>(pi + (int64_t)(s + u) * sstride));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) add(rv[u], iv[u]);
         fold();
     }
     for (; s < s1; ++s)
-        add(*reinterpret_cast<const raw_t*>(pr + (int64_t)s * sstride),
-            *reinterpret_cast<const raw_t*>(pi + (int64_t)s * sstride));
+        add(ldnt(reinterpret_cast<const raw_t*>(pr + (int64_t)s * sstride)),
+            ldnt(reinterpret_cast<const raw_t*>(pi + (int64_t)s * sstride)));
     fold();
     // partials [L][chunk][Hq][F][5]
     double* out = a.part + ((((int64_t)l * a.n_chunks + c) * a.n_q_heads + h) * F + f0) * 5;
@@ -129,9 +146,11 @@ hipError_t launch_calibrate(const CalibArgs& a, bool bf16, hipStream_t stream) {
     const int groups = a.n_q_heads * (a.head_dim / 2 / kCalibBands);
     {
         TimedLaunch tl(KID_CALIB, stream);
-        const dim3 grid((unsigned)(a.n_layers * a.n_chunks), (unsigned)((groups + 63) / 64));
-        if (bf16) hipLaunchKernelGGL(k_calib_partial<true>, grid, dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL(k_calib_partial<false>, grid, dim3(64), 0, stream, a);
+        const int blocks = (groups + 63) / 64;
+        const int waves = blocks < kCalibWavesPerGroup ? blocks : kCalibWavesPerGroup;
+        const dim3 grid((unsigned)(a.n_layers * a.n_chunks), (unsigned)((blocks + waves - 1) / waves));
+        if (bf16) hipLaunchKernelGGL(k_calib_partial<true>, grid, dim3(64 * waves), 0, stream, a);
+        else hipLaunchKernelGGL(k_calib_partial<false>, grid, dim3(64 * waves), 0, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

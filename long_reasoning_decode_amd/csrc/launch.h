@@ -239,9 +239,9 @@ hipError_t launch_decode_attn(const AttnArgs& a, int head_dim, int group, bool b
 
 // --- offline calibration from sampled pre-RoPE queries
 constexpr int kCalibBands = 4;             // bands per pass-1 lane
-// Samples per pass-1 workgroup (one wave): sized so the grid (layers x chunks
-// x blocks of 64 band groups) is about one round of the one-wave workgroups the
-// chip holds at once (256 CUs x 4 SIMDs x 4 waves); a second, partial round
+// Samples per pass-1 wave: sized so the waves (layers x chunks x blocks of 64
+// band groups) are about one round of what the chip holds at once (256 CUs x
+// 4 SIMDs x 4 waves); a second, partial round
 // would take as long as the first.  At least 64 samples (the fp64 partials
 // then stay under a sixth of the samples' bytes), a multiple of 8 (one batch).
 constexpr int kCalibResidentWaves = 4096;

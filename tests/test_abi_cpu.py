@@ -216,6 +216,7 @@ def test_calibrate_validation():
     assert cal(dt=5) == T.TRI_ERR_INVALID_ARG
     assert cal(ns=0) == T.TRI_ERR_INVALID_ARG
     assert cal(qp=None) == T.TRI_ERR_INVALID_ARG
+    assert cal(qp=ctypes.c_void_p(q.data_ptr() + 4)) == T.TRI_ERR_INVALID_ARG   # rows must be 16-byte aligned
     assert cal(wb=16) == T.TRI_ERR_WORKSPACE
     assert lib.tri_calibrate(T._p(q), T.TRI_DTYPE_F32, 2, 10, 4, 64, T._p(out), T._p(out), T._p(out),
                              ctypes.c_void_p(ws.data_ptr() + 16), ws.numel() - 16, None) == T.TRI_ERR_WORKSPACE
