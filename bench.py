@@ -121,10 +121,11 @@ def kernel_breakdown(T, step, steps):
     return T.tri_timing_read()
 
 
-def timed_steps(T, step, steps, stream, kernels):
+def timed_steps(T, step, steps, stream, kernels, finish=None):
     """The timed region: `steps` steps between two events, with only the named
-    kernels' launches bracketed by library events.  Returns (ms per step,
-    {kernel: (launches, total ms)})."""
+    kernels' launches bracketed by library events; `finish` (optional) orders
+    `stream` after work the last step left on other streams.  Returns (ms per
+    step, {kernel: (launches, total ms)})."""
     import torch
     T.tri_timing_reset()
     T.tri_timing_enable(True, only=kernels)
@@ -133,6 +134,8 @@ def timed_steps(T, step, steps, stream, kernels):
     ev0.record(stream)
     for _ in range(steps):
         step()
+    if finish is not None:
+        finish()
     ev1.record(stream)
     torch.cuda.synchronize()
     T.tri_timing_enable(False)
@@ -211,10 +214,15 @@ def bench_decode_loop(args, T, W):
     which case it compacts into a second cache and the two alternate.  In place
     the cache stays in slot order (every kept row after the first dropped slot
     moves), or with --fill-freed only the kept rows above B move, into the freed
-    slots."""
+    slots.  Then the same windows are timed with the prune overlapped
+    (out of place, on a second stream in --overlap-groups layer groups, beside
+    the window's last attention and the next window's first step), reported
+    under "overlapped"."""
     import math
 
     import torch
+
+    from long_reasoning_decode_amd.decode_loop import LayerGroups, OverlappedPrune, first_step
     cfg = W.CONFIGS["gptoss"]
     B, win = cfg.budget, cfg.window
     st = W.decode_start(cfg, "cuda")
@@ -233,7 +241,8 @@ def bench_decode_loop(args, T, W):
     out = torch.empty(toks[0][2].shape, dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(cfg.head_dim)
     # positions of every window run: warmup, the per-kernel breakdown and the timed steps
-    pos = torch.arange(t0, t0 + (args.warmup + 2 * args.steps + 1) * win, dtype=torch.int32,
+    # (twice: the serial schedule, then the overlapped one)
+    pos = torch.arange(t0, t0 + 2 * (args.warmup + 2 * args.steps + 1) * win, dtype=torch.int32,
                        device="cuda")[:, None].expand(-1, cfg.n_seq).contiguous()      # [token][seq]
     tvec = torch.empty((cfg.n_seq,), dtype=torch.int32, device="cuda")
     state = {"cur": 0, "w": 0}
@@ -269,6 +278,41 @@ def bench_decode_loop(args, T, W):
             state["cur"] = 1 - cur
         state["w"] += 1
 
+    # the overlapped schedule: window w's prune on a second stream, group by group
+    groups = [LayerGroups(c, n_layers=cfg.n_layers, n_seq=cfg.n_seq, n_kv_heads=cfg.n_kv_heads,
+                          n_groups=args.overlap_groups) for c in caches]
+    prune_stream = torch.cuda.Stream()
+    pruners = [OverlappedPrune(calib, groups[i], groups[1 - i], B, ws, stream, prune_stream) for i in (0, 1)]
+
+    def window_overlapped():
+        cur = state["cur"]
+        d = descs[cur]
+        for j in range(win):
+            k_new, v_new, q = toks[j]
+            p = pos[state["w"] * win + j]
+            if state["sample"]:                 # every 8th whole-cache launch (step 0 runs in groups)
+                T.tri_timing_enable(j % 8 == 1, only=["decode_attn"])
+            if j == 0 and state["pending"] is not None:
+                first_step(state["pending"], groups[cur], cfg.n_q_heads, k_new, v_new, p, q, scale, out, stream)
+                state["pending"] = None
+                continue
+            T.tri_append(d, k_new, v_new, p, stream=stream)
+            if j == win - 1:                    # the window's tokens are in: prune beside this step's attention
+                tvec.fill_(t0 + (state["w"] + 1) * win)
+                pruners[cur].launch(tvec)
+                state["pending"] = pruners[cur]
+            T.tri_decode_attn(d, cfg.n_q_heads, q, scale, out, stream=stream)
+        if state["sample"]:
+            T.tri_timing_enable(False)
+        state["cur"] = 1 - cur
+        state["w"] += 1
+
+    def drain():                                # the last window's prune, inside the timed region
+        if state["pending"] is not None:
+            for g in range(args.overlap_groups):
+                state["pending"].wait(g)
+            state["pending"] = None
+
     for i in range(args.warmup):
         window(count_moves=in_place and i == args.warmup - 1)
     torch.cuda.synchronize()
@@ -276,6 +320,12 @@ def bench_decode_loop(args, T, W):
     state["sample"] = True
     ms, kt_timed = timed_steps(T, window, args.steps, stream, ["decode_attn"])
     state["sample"] = False
+    state["pending"] = None
+    for i in range(args.warmup):
+        window_overlapped()
+    drain()
+    torch.cuda.synchronize()
+    ms_ov, _ = timed_steps(T, window_overlapped, args.steps, stream, [], finish=drain)
     es = 2
     # decode attention reads every valid K and V row once per step (lengths B+1 .. B+win over a
     # window); the timed region brackets the launches j = 0, 8, ..., so their bytes are counted
@@ -315,6 +365,10 @@ def bench_decode_loop(args, T, W):
         "prune": {"algorithmic_bytes": prune_bytes, "ms": round(prune_ms, 4),
                   "achieved_GBs": round(prune_bytes / (prune_ms * 1e-3) / 1e9, 1),
                   "in_place": in_place, "rows_copied": copied},
+        "overlapped": {"schedule": (f"prune out of place on a second stream in {args.overlap_groups} layer groups, "
+                                    "beside the window's last attention and the next window's first step"),
+                       "ms_per_step": round(ms_ov, 4), "tokens_per_s": round(tokens / (ms_ov * 1e-3), 1),
+                       "vs_serial": round(ms / ms_ov, 4)},
         "kernels": kernels,
     }
     calib.free()
@@ -455,6 +509,8 @@ def main():
                          "(default: 1024 for caches under 16M keys, else 0)")
     ap.add_argument("--fill-freed", action="store_true",
                     help="gptoss: in-place prune in the fill-freed-slots arrangement instead of slot order")
+    ap.add_argument("--overlap-groups", type=int, default=1,
+                    help="gptoss: layer groups of the overlapped prune, timed after the serial schedule")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device-to-device copy of this many MiB "
                          "(known-size reference for hardware byte counters)")

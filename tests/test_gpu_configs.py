@@ -215,6 +215,28 @@ def test_ragged_paged_full(gpu_lib, part):
     log("  paged decode attention over the pruned pages ok")
 
 
+def _layer_against_oracle(cfg, cal, before, res, layer_segs, t, B, w, slot_order=True):
+    """The pruned segments layer_segs of cache `res` against the oracle's prune
+    of their rows before the prune (`before`: lengths, K, V, positions on the
+    host) at position t."""
+    N0, Kb, Vb, Pb = before
+    refs = oracle.run_parallel(lambda i: oracle_select(cfg, cal, Kb[i, :N0[i]], Pb[i, :N0[i]], t,
+                                                       layer_segs[i], B), range(len(layer_segs)))
+    Kd, Vd = stored(res["k"][layer_segs, :B].cpu()), stored(res["v"][layer_segs, :B].cpu())
+    Pd = res["pos"][layer_segs, :B].cpu().numpy()
+    n_diff = 0
+    for i, (s, ref) in enumerate(zip(layer_segs, refs)):
+        tag = f"gptoss window {w} seg {s}"
+        N = int(N0[i])
+        ix = kept_slots_from_positions(Pb[i, :N], Pd[i])
+        n_diff += check_selection(np.sort(ix), ref["A"], B, tag, pos=Pb[i, :N])
+        check_compaction(Kb[i, :N], Vb[i, :N], Pb[i, :N], Kd[i], Vd[i], Pd[i], ix, tag)
+        if slot_order:
+            assert np.all(np.diff(ix) > 0), f"{tag}: not in slot order"
+    log(f"  window {w}: {len(layer_segs)} segments of layer 11 match the oracle "
+        f"({n_diff} slots differ inside the tie band)")
+
+
 @pytest.mark.parametrize("in_place", [False, True, "fill"])
 def test_gptoss_decode_loop_full(gpu_lib, in_place):
     """16 windows of 128 steps (append + decode attention each step), a prune
@@ -291,21 +313,86 @@ def test_gptoss_decode_loop_full(gpu_lib, in_place):
             assert bool(torch.all(nxt["lengths"] == B)), f"window {w}: kept counts"
             res = nxt
         if checked:
-            refs = oracle.run_parallel(lambda i: oracle_select(cfg, cal, Kb[i, :N0[i]], Pb[i, :N0[i]], t,
-                                                               layer_segs[i], B), range(len(layer_segs)))
-            Kd, Vd = stored(res["k"][layer_segs, :B].cpu()), stored(res["v"][layer_segs, :B].cpu())
-            Pd = res["pos"][layer_segs, :B].cpu().numpy()
-            n_diff = 0
-            for i, (s, ref) in enumerate(zip(layer_segs, refs)):
-                tag = f"gptoss window {w} seg {s}"
-                N = int(N0[i])
-                ix = kept_slots_from_positions(Pb[i, :N], Pd[i])
-                n_diff += check_selection(np.sort(ix), ref["A"], B, tag, pos=Pb[i, :N])
-                check_compaction(Kb[i, :N], Vb[i, :N], Pb[i, :N], Kd[i], Vd[i], Pd[i], ix, tag)
-                if not fill:
-                    assert np.all(np.diff(ix) > 0), f"{tag}: not in slot order"
-            log(f"  window {w}: {len(layer_segs)} segments of layer 11 match the oracle "
-                f"({n_diff} slots differ inside the tie band)")
+            _layer_against_oracle(cfg, cal, (N0, Kb, Vb, Pb), res, layer_segs, t, B, w, slot_order=not fill)
         if not in_place:
             nxt["t"] = c["t"]
             cur = 1 - cur
+
+
+def test_gptoss_decode_loop_overlapped(gpu_lib):
+    """The GPT-OSS-shaped loop with each window's prune overlapped: out of
+    place on a second stream in four layer groups, beside the window's last
+    attention and the next window's first step (appended and attended group by
+    group).  Run in lockstep with the same loop pruned serially on the decode
+    stream: the attention outputs of every window's first, second and last
+    step and both caches after every window's second step are byte for byte
+    the serial loop's; at the first and last window every segment of layer 11
+    of the overlapped prune's result against the oracle."""
+    from long_reasoning_decode_amd.decode_loop import LayerGroups, OverlappedPrune, first_step
+    T = gpu_lib
+    cfg = W.CONFIGS["gptoss"]
+    B, win, Hq = cfg.budget, cfg.window, cfg.n_q_heads
+    n_groups = 4
+    log(f"case gptoss decode loop overlapped: {cfg.windows} windows x {win} steps, {n_groups} layer groups")
+    D = torch.cuda.Stream()
+    with torch.cuda.stream(D):
+        st = W.decode_start(cfg, "cuda")
+        km = st.pop("key_model")
+        calib, cal = calib_for(T, cfg)
+        cap = st["capacity"]
+        keys = ("k", "v", "pos", "lengths")
+        ser = [st, empty_like_dense(st, cap)]
+        ovl = [{k: st[k].clone() for k in keys}, empty_like_dense(st, cap)]
+        dser = [dense_desc(T, cfg, c) for c in ser]
+        dovl = [dense_desc(T, cfg, c) for c in ovl]
+        groups = [LayerGroups(c, n_layers=cfg.n_layers, n_seq=cfg.n_seq, n_kv_heads=cfg.n_kv_heads,
+                              n_groups=n_groups) for c in ovl]
+        ws_s, ws_o = T.workspace(calib, dser[0], B), T.workspace(calib, dovl[0], B)
+        P = torch.cuda.Stream()
+        pruners = [OverlappedPrune(calib, groups[i], groups[1 - i], B, ws_o, D, P) for i in (0, 1)]
+        tv_s = torch.empty((cfg.n_seq,), dtype=torch.int32, device="cuda")
+        tv_o = torch.empty_like(tv_s)
+        q_shape = (cfg.n_layers, cfg.n_seq, Hq, cfg.head_dim)
+        out_s = torch.empty(q_shape, dtype=torch.float32, device="cuda")
+        out_o = torch.empty_like(out_s)
+        per_l = cfg.n_seq * cfg.n_kv_heads
+        layer_segs = list(range(11 * per_l, 12 * per_l))
+        scale = 1.0 / math.sqrt(cfg.head_dim)
+        pending, cur, t = None, 0, cfg.start_pos_range
+        for w in range(cfg.windows):
+            for j in range(win):
+                k_new, v_new, q = W.decode_token(cfg, km, w * win + j, t, "cuda")
+                pos_new = torch.full((cfg.n_seq,), t, dtype=torch.int32, device="cuda")
+                T.tri_append(dser[cur], k_new, v_new, pos_new, stream=D)
+                T.tri_decode_attn(dser[cur], Hq, q, scale, out_s, stream=D)
+                if j == 0 and pending is not None:
+                    first_step(pending, groups[cur], Hq, k_new, v_new, pos_new, q, scale, out_o, D)
+                    pending = None
+                else:
+                    T.tri_append(dovl[cur], k_new, v_new, pos_new, stream=D)
+                    if j == win - 1:
+                        tv_o.fill_(t + 1)
+                        pruners[cur].launch(tv_o)
+                        pending = pruners[cur]
+                    T.tri_decode_attn(dovl[cur], Hq, q, scale, out_o, stream=D)
+                if j in (0, 1, win - 1):
+                    assert torch.equal(out_o, out_s), f"window {w} step {j}: attention differs from the serial loop"
+                if j == 1:
+                    for k in keys:
+                        assert torch.equal(ovl[cur][k], ser[cur][k]), f"window {w} step 1: cache {k} differs"
+                t += 1
+            tv_s.fill_(t)
+            T.tri_prune_window(calib, dser[cur], tv_s, B, dser[1 - cur], ser[1 - cur]["lengths"], ws_s, stream=D)
+            if w in (0, cfg.windows - 1):
+                for g in range(n_groups):
+                    pending.wait(g)
+                D.synchronize()
+                for k in keys:
+                    assert torch.equal(ovl[1 - cur][k], ser[1 - cur][k]), f"window {w}: pruned cache {k} differs"
+                src = ser[cur]
+                before = (src["lengths"][layer_segs].cpu().numpy(), stored(src["k"][layer_segs].cpu()),
+                          stored(src["v"][layer_segs].cpu()), src["pos"][layer_segs].cpu().numpy())
+                _layer_against_oracle(cfg, cal, before, ovl[1 - cur], layer_segs, t, B, w)
+            cur = 1 - cur
+        D.synchronize()
+    calib.free()
