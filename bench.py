@@ -25,9 +25,22 @@ METRIC = "keys scored+pruned/sec (G keys/s) and % of HBM roofline, 32K cache, B=
 HBM_PEAK_GBS = 8000.0
 
 
-def kernel_source_sha():
+# The source file each timed kernel is defined in; every kernel also depends
+# on the shared headers and on the C ABI's launch choices (api.hip).
+KERNEL_SOURCE = {"score": "score.hip", "select_gather": "select.hip", "gather": "select.hip", "decode_attn": "decode.hip",
+                 "calibrate": "calib.hip"}
+SHARED_SOURCES = ["api.hip", "common.h", "launch.h", "stats.h"]
+
+
+def kernel_source_sha(kernel=None):
+    """Hash of the sources a kernel's counters depend on (None: every kernel source)."""
+    csrc = os.path.join(ROOT, "long_reasoning_decode_amd", "csrc")
+    if kernel is None:
+        files = sorted(glob.glob(os.path.join(csrc, "*")))
+    else:
+        files = [os.path.join(csrc, f) for f in sorted(SHARED_SOURCES + [KERNEL_SOURCE[kernel]])]
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "long_reasoning_decode_amd", "csrc", "*"))):
+    for p in files:
         h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
@@ -43,7 +56,7 @@ def read_traffic(kernel, workload):
         if ":" in line:
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha") != kernel_source_sha():
+    if kernel not in KERNEL_SOURCE or vals.get("kernel_source_sha") != kernel_source_sha(kernel):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])

@@ -271,7 +271,7 @@ __device__ __forceinline__ int cand_slot(int n, int N, const uint32_t* pre, cons
 // Instances built for 8 waves per SIMD (at most 64 VGPRs), so two workgroups
 // share a CU and one's gather overlaps the other's select phase.
 constexpr bool select_low_regs(int J, int G, int NT = 1024) {
-    return NT < 1024 || (J <= 16 && G <= 4) || (J <= 2 && G == 8);
+    return NT < 1024 || (J <= 16 && G <= 4);
 }
 
 // Orderable key of a position for the tie rule: an earlier (smaller, signed)
@@ -639,23 +639,26 @@ __device__ __forceinline__ void select_segment(const SelectArgs& a, const int s)
         a.dst.pos[a.dst.row(s, jrow)] = a.src.pos[a.src.row(s, kept[jrow])];
 }
 
-// J <= 16, G <= 4 (and every 256-thread instance): at most 64 VGPRs and the
+// J <= 16, G <= 4 (and the 256-thread instances): at most 64 VGPRs and the
 // SGPRs of 8 waves per SIMD, so two 1024-thread (or eight 256-thread)
 // workgroups share a CU and one's gather overlaps another's select phase.
+// The 256-thread G = 8 instances (eight heads' statistics) spill at 64 VGPRs:
+// they get 5 waves per SIMD (five workgroups per CU; measured as fast on the
+// GPT-OSS-shaped window prune).
+constexpr int select_waves(int J, int G, int NT) { return NT < kSelThreads && G == 8 ? 5 : select_low_regs(J, G, NT) ? 8 : 1; }
 template <int J, int G, int MODE, int NT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(select_low_regs(J, G, NT) ? 8 : 1))) void k_select(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(select_waves(J, G, NT)))) void k_select(
     SelectArgs a) {
     select_segment<J, G, MODE, NT>(a, blockIdx.x);
 }
 
-// Mode S over the segments whose candidate pass failed its certificate.
+// Mode S over the segments whose candidate pass failed its certificate:
+// workgroup i takes list entry i (the grid covers every segment, the most the
+// list can hold; the rest exit at once).  A grid-strided loop over the list
+// made the compiler keep the per-thread key arrays in scratch memory.
 template <int J, int G>
 __global__ __launch_bounds__(kSelThreads) void k_select_fallback(SelectArgs a) {
-    const int n = *a.fb_count;
-    for (int i = blockIdx.x; i < n; i += gridDim.x) {
-        __syncthreads();                                // LDS of the previous segment is no longer read
-        select_segment<J, G, SELECT_S>(a, a.fb_list[i]);
-    }
+    if ((int)blockIdx.x < *a.fb_count) select_segment<J, G, SELECT_S>(a, a.fb_list[blockIdx.x]);
 }
 
 template <int J, int G, int NT>
@@ -663,7 +666,7 @@ static bool select_launch(const SelectArgs& a, int mode, hipStream_t stream) {
     const dim3 block(NT);
     if (mode == SELECT_S_FALLBACK) {
         if constexpr (G > 0 && NT == kSelThreads)
-            hipLaunchKernelGGL((k_select_fallback<J, G>), dim3((unsigned)(a.n_seg < 512 ? a.n_seg : 512)), block, 0, stream, a);
+            hipLaunchKernelGGL((k_select_fallback<J, G>), dim3((unsigned)a.n_seg), block, 0, stream, a);
         return G > 0 && NT == kSelThreads;
     }
     const dim3 grid((unsigned)a.n_seg);
