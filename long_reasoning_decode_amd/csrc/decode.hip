@@ -183,21 +183,33 @@ __global__ __launch_bounds__(256) void k_decode_attn(AttnArgs a) {
 //    vectors as columns (bf16, so the products are exact; fp32 accumulation);
 //  * online softmax per head (base 2) on the fragment layout: lane (grp, row)
 //    holds head `row`'s logits of keys 4 grp + r;
-//  * P.V on the vector units: lane = output dimension(s); the lane's V values
-//    are copied from LDS to registers right after the tile lands, and each
-//    key's probabilities are broadcast from the lanes that computed them
-//    (readlane), so the compute touches no LDS while the next tile loads.
+//  * P.V on the matrix cores too (v_mfma_f32_16x16x16_bf16, one per 16-key
+//    unit, 16-dim block and split part): A = the probabilities in the logits'
+//    own fragment layout, each carried as three bf16 parts (24 bits), B = the
+//    V tile, whose fragments are copied from LDS to registers right after the
+//    tile lands, so the compute touches no LDS while the next tile loads.  On
+//    the vector units (a readlane and an FMA per key, head and dim) this was
+//    about 80% of the SIMDs' issue cycles at head_dim 64, GQA 8.
 // The waves' (max, sum, partial output) are merged at the end.
 // Paged caches: lane l holds the page of key l of the tile the wave issues
 // next, loaded (a plain load into a register) one compute phase ahead.
+// P.V goes to the matrix cores where its vector form is the larger cost: G
+// heads x D dims of multiply-adds (and G readlanes) per key against 4 D bytes
+// of K and V, i.e. G >= 8 at head_dim 64.  At head_dim 128 (G <= 8) the
+// vector form is cheaper than the registers the MFMA form needs (its
+// accumulators and V fragments would not fit four waves per SIMD).
+constexpr bool pv_on_mfma(int D, int G) { return G * 64 / D >= 8; }
+
 template <int D, int G, bool PAGED, int NW>
-__global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(pv_on_mfma(D, G) && NW == 4 ? (PAGED ? 4 : 5) : 1))) void k_decode_attn_mfma(AttnArgs a) {
     constexpr int ROWB = D * 2, CPR = ROWB / 16;
     constexpr int TK = 2048 / D;               // keys per tile
     constexpr int NU = TK / 16;                // 16-key MFMA tiles per tile
     constexpr int TS = D / 32;                 // k-steps
     constexpr int NDMA = TK * CPR / 64;        // DMA instructions per operand and tile
-    constexpr int DPL = D / kWave;             // output dims per lane
+    constexpr int NDB = D / 16;                // 16-dim output blocks
+    constexpr int DPL = D / kWave;             // vector path: output dims per lane
+    constexpr bool PV_MFMA = pv_on_mfma(D, G);
     constexpr float kLog2e = 1.4426950408889634f;
     static_assert(G <= 16 && NU >= 1, "one 16-column B fragment holds the group");
     static_assert(DPL == 1 || DPL == 2, "one or two output dims per lane");
@@ -252,13 +264,40 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
     }
 
     float m = -__builtin_inff(), lsum = 0.0f;              // head `row`'s running max and sum
-    float o[G][DPL];
+    // output accumulators, the D layout of v_mfma_f32_16x16x16_bf16 per block
+    // of 16 dims: lane (row, grp) holds O[head 4 grp + r][dim 16 c + row]
+    f32x4_t oacc[PV_MFMA ? NDB : 1];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int c = 0; c < (PV_MFMA ? NDB : 1); ++c) oacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // otherwise (vector-unit P.V) lane = output dimension(s) DPL * lane + d
+    float o[PV_MFMA ? 1 : G][DPL];
+#pragma unroll
+    for (int g = 0; g < (PV_MFMA ? 1 : G); ++g)
 #pragma unroll
         for (int d = 0; d < DPL; ++d) o[g][d] = 0.0f;
+    constexpr int VW = TK * DPL / 2;                       // vector path: 32-bit words of the lane's V values per tile
 
-    constexpr int VW = TK * DPL / 2;                       // 32-bit words of the lane's V values per tile
+    // Byte offsets of the lane's fragment reads inside its wave's tile.  The
+    // swizzle's XOR splits into a lane part and a compile-time part, so every
+    // read is one of these registers plus an immediate offset.
+    //  K, A fragment (row 16u + row, chunk 4 st + grp): the row's chunk is
+    //  (4 st + grp) ^ (row mod CPR), the same for every u (16 is a multiple of CPR);
+    static_assert(16 % CPR == 0, "a 16-key unit spans whole swizzle periods");
+    int kofs[TS];
+#pragma unroll
+    for (int st = 0; st < TS; ++st) kofs[st] = 16 * (row * CPR + ((4 * st + grp) ^ (row % CPR)));
+    //  V, B fragment (key 16u + 4grp + r, dim 16c + row, head_dim 64: CPR = 8):
+    //  the chunk (2c + row/8) ^ (4 (grp mod 2) + r) has bit 0 = row/8 ^ r mod 2,
+    //  bit 1 = c mod 2 ^ r/2 and bit 2 = c/2 ^ grp mod 2; the lane parts of
+    //  bits 0 and 2 give four bases, the rest is constant.
+    static_assert(!PV_MFMA || D == 64, "the V fragment offsets assume head_dim 64");
+    int vofs[2][2];
+#pragma unroll
+    for (int r0 = 0; r0 < 2; ++r0)
+#pragma unroll
+        for (int c1 = 0; c1 < 2; ++c1)
+            vofs[r0][c1] = 16 * CPR * 4 * grp + 2 * (row & 7) + 16 * ((row >> 3) ^ r0) + 64 * (c1 ^ (grp & 1));
+
     for (int t = w; t < nt; t += NW) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);              // this tile has landed
         __builtin_amdgcn_wave_barrier();
@@ -273,12 +312,28 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int st = 0; st < TS; ++st) {
-                const int kl = 16 * u + row;
-                af[u][st] = kr[kl * CPR + ((4 * st + grp) ^ (kl % CPR))];
-            }
-        uint32_t vw[VW];
-        {
+            for (int st = 0; st < TS; ++st)
+                af[u][st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(kr) + kofs[st] +
+                                                            16 * CPR * 16 * u);
+        // V as B fragments: for 16-key unit u and dim block c, lane (row,
+        // grp) holds V[16 u + 4 grp + r][16 c + row], r = 0..3 (bf16 pairs)
+        // (vector path: the lane's own dims, every key of the tile)
+        uint32_t vf[PV_MFMA ? NU : 1][PV_MFMA ? NDB : 1][2];
+        uint32_t vw[PV_MFMA ? 1 : VW];
+        if constexpr (PV_MFMA) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int c = 0; c < NDB; ++c)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        // key 16u + 4grp + r, dim 16c + row: vofs plus a constant
+                        const uint8_t* cp = vb + vofs[r & 1][c >> 1] + 16 * CPR * (16 * u + r) + 32 * ((c & 1) ^ (r >> 1));
+                        const uint32_t h = *reinterpret_cast<const uint16_t*>(cp);
+                        if (r & 1) vf[u][c][r >> 1] |= h << 16;
+                        else vf[u][c][r >> 1] = h;
+                    }
+        } else {
             const int dim = DPL * lane;                    // the lane's dims share one 16-byte chunk
 #pragma unroll
             for (int k = 0; k < TK; ++k) {
@@ -332,35 +387,73 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
         ts += __shfl_xor(ts, 32, kWave);
         lsum = lsum * alpha + ts;
         m = mn;
-        // P.V: lane owns the DPL adjacent output dims DPL * lane + d; head g's
-        // probability of key 16u + 4q + r sits in lane 16q + g, register x[u][r]
+        if constexpr (!PV_MFMA) {
+            // P.V on the vector units: head g's probability of key 16u + 4q + r
+            // sits in lane 16q + g, register x[u][r]
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), g));
+            for (int g = 0; g < G; ++g) {
+                const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), g));
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) o[g][d] *= al;
+                for (int d = 0; d < DPL; ++d) o[g][d] *= al;
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int k = 16 * u + 4 * q + r;
+                        float v[DPL];
+                        if constexpr (DPL == 2) {
+                            v[0] = bf16_lo(vw[k]);
+                            v[1] = bf16_hi(vw[k]);
+                        } else {
+                            v[0] = (k & 1) ? bf16_hi(vw[k >> 1]) : bf16_lo(vw[k >> 1]);
+                        }
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            const float p = __int_as_float(
+                                __builtin_amdgcn_readlane(__float_as_int(x[u][r]), 16 * q + g));
+#pragma unroll
+                            for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(p, v[d], o[g][d]);
+                        }
+                    }
+            continue;
         }
+        // rescale: the lane's output rows are heads 4 grp + r, whose factors
+        // sit in lanes 4 grp + r
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
+        for (int r = 0; r < 4; ++r) {
+            const float al = __shfl(alpha, 4 * grp + r, kWave);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int c = 0; c < NDB; ++c) oacc[c][r] *= al;
+        }
+        // P.V on the matrix cores: A = P (16 heads x 16 keys of unit u) is the
+        // logits' own layout (lane (row, grp) holds head row's probabilities of
+        // keys 16 u + 4 grp + r); each probability is carried as the sum of
+        // three bf16 parts (hi, mid, lo: 24 bits), so the bf16 products keep
+        // fp32-level accuracy
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int k = 16 * u + 4 * q + r;
-                    float v[DPL];
-                    if constexpr (DPL == 2) {
-                        v[0] = bf16_lo(vw[k]);
-                        v[1] = bf16_hi(vw[k]);
-                    } else {
-                        v[0] = (k & 1) ? bf16_hi(vw[k >> 1]) : bf16_lo(vw[k >> 1]);
-                    }
+        for (int u = 0; u < NU; ++u) {
+            bf16x4_t pa[3];
 #pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const float p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[u][r]), 16 * q + g));
+            for (int r = 0; r < 4; ++r) {
+                const __bf16 hi = (__bf16)x[u][r];
+                const float r1 = x[u][r] - (float)hi;
+                const __bf16 mid = (__bf16)r1;
+                pa[0][r] = hi;
+                pa[1][r] = mid;
+                pa[2][r] = (__bf16)(r1 - (float)mid);
+            }
 #pragma unroll
-                        for (int d = 0; d < DPL; ++d) o[g][d] = fmaf(p, v[d], o[g][d]);
-                    }
-                }
+            for (int c = 0; c < NDB; ++c) {
+                const s16x4_t b = __builtin_bit_cast(s16x4_t, make_uint2(vf[u][c][0], vf[u][c][1]));
+#pragma unroll
+                for (int q = 0; q < 3; ++q)
+                    oacc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, pa[q]), b,
+                                                                       oacc[c], 0, 0, 0);
+            }
+        }
     }
 
     // merge the waves (their tile buffers hold the partial outputs, maxima and sums)
@@ -374,10 +467,18 @@ __global__ __launch_bounds__(NW * 64) void k_decode_attn_mfma(AttnArgs a) {
         wm[w][row] = m;
         wl[w][row] = lsum;
     }
+    if constexpr (PV_MFMA) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+        for (int c = 0; c < NDB; ++c)
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) wo[(w * G + g) * D + DPL * lane + d] = o[g][d];
+            for (int r = 0; r < 4; ++r)
+                if (4 * grp + r < G) wo[(w * G + 4 * grp + r) * D + 16 * c + row] = oacc[c][r];
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int d = 0; d < DPL; ++d) wo[(w * G + g) * D + DPL * lane + d] = o[g][d];
+    }
     __syncthreads();
     float* out = a.out + (((int64_t)l * a.shape.n_seq + b) * a.n_q_heads + (int64_t)h * G) * D;
     for (int i = tid; i < G * D; i += NW * 64) {
