@@ -321,7 +321,11 @@ int tri_append(const tri_cache_desc* kv, const void* k_new, const void* v_new,
  * to the whole cache):  out = softmax(scale * q . K^T) V over the segment's
  * valid keys.  q : device [n_layers][n_seq][n_q_heads][head_dim] (cache dtype);
  * out : device fp32, same shape.  Dense or paged caches (a pruned paged cache
- * is read in place through its page table); lengths[s] >= 1.
+ * is read in place through its page table); lengths[s] >= 1.  Arithmetic:
+ * fp32 sums of exact products (bf16 q and K on the matrix cores; the
+ * probabilities times V either in fp32 or, for eight-head groups at head_dim
+ * 64, on the matrix cores with each probability carried as three bf16 parts,
+ * 24 bits), base-2 online softmax in fp32.
  */
 int tri_decode_attn(const tri_cache_desc* kv, int n_q_heads, const void* q, float scale, float* out,
                     tri_stream_t stream);
