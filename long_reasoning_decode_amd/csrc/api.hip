@@ -240,9 +240,11 @@ int hip_status(hipError_t e, const char* step = "launch") {
 int run_phase_and_score(const tri_calib_s* c, const tri_cache_desc* kv, const int32_t* t, float* s_raw,
                         float* s_int, double2* stats, float* ctab, int chunk, hipStream_t st,
                         const WsPlan* cand = nullptr, char* ws = nullptr, int budget = 0,
-                        int32_t* fb_reset = nullptr) {
+                        int32_t* fb_reset = nullptr, uint32_t* zero = nullptr, int64_t zero_words = 0) {
     PhaseArgs pa;
     pa.fb_reset = fb_reset;
+    pa.zero = zero;
+    pa.zero_words = zero ? zero_words : 0;
     pa.P = c->P;
     pa.omega = c->omega;
     pa.t = t;
@@ -674,9 +676,13 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
     // needs, or the full path asked for): the full path.
     const bool cand = src->dtype == TRI_DTYPE_BF16 && candidate_mode(src->capacity, budget) &&
                       (path == TRI_PATH_CANDIDATES || (path == TRI_PATH_AUTO && n_segments(src) >= kCandidateMinSegs));
-    // (without candidate mode nothing falls back: the phase kernel zeroes the count tri_prune_fallbacks reads)
+    // (without candidate mode nothing falls back: the phase kernel zeroes the count tri_prune_fallbacks reads;
+    // with the split select it also clears that select's histograms)
+    const bool ssel = !in_place && split_select(src);
     if ((rc = run_phase_and_score(calib, src, t, nullptr, s_int, stats, ctab, chunk, st, cand ? &p : nullptr, w,
-                                  budget, cand ? nullptr : reinterpret_cast<int32_t*>(w + p.fb_count))))
+                                  budget, cand ? nullptr : reinterpret_cast<int32_t*>(w + p.fb_count),
+                                  ssel ? reinterpret_cast<uint32_t*>(w + p.shist) : nullptr,
+                                  ssel ? split_select_zero_words(n_segments(src)) : 0)))
         return rc;
     SelectArgs a;
     memset(&a, 0, sizeof a);
@@ -688,7 +694,6 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
     a.lengths = src->lengths;
     a.budget = budget;
     a.n_kept = n_kept;
-    const bool ssel = !in_place && split_select(src);
     const bool split = !in_place && (split_gather(src) || ssel);
     a.gather = in_place ? (fill ? GATHER_IN_PLACE_FILL : GATHER_IN_PLACE) : split ? GATHER_NONE : GATHER_COPY;
     a.tie = TIE_POS_CACHE;
@@ -703,8 +708,10 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
         a.idx_stride = idx_stride;
     }
     // split: every select kernel has written its segments' kept slots; copy them
+    // (the split select's emission copies its rows itself, and its fallback
+    // select gathers the segments it takes)
     auto gather_split = [&]() -> int {
-        if (!split) return TRI_OK;
+        if (!split || ssel) return TRI_OK;
         GatherArgs ga;
         ga.src = a.src;
         ga.dst = a.dst;
@@ -741,9 +748,15 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
         ss.idx_stride = idx_stride;
         ss.n_kept = n_kept;
         ss.n_seg = a.n_seg;
+        ss.zeroed = true;
+        ss.gather = true;
+        ss.src = a.src;
+        ss.dst = a.dst;
+        ss.row_bytes = a.row_bytes;
         if ((rc = hip_status(launch_split_select(ss, calib->G, cand, st), "split select kernels"))) return rc;
         a.fb_list = ss.fb_list;
         a.fb_count = ss.fb_count;
+        a.gather = GATHER_COPY;                       // the fallback select copies its segments' rows
         if (!cand) {
             if ((rc = hip_status(launch_select(a, calib->G, SELECT_S_FALLBACK, src->capacity, st),
                                  "fallback select kernel")))

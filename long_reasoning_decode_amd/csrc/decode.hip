@@ -10,20 +10,26 @@
 namespace tri {
 
 // ------------------------------------------------------------------ append
-__global__ __launch_bounds__(64) void k_append(AppendArgs a) {
-    const int s = blockIdx.x;
-    const int n = a.lengths[s];
-    __syncthreads();                               // every lane has read the length
-    if (n < 0 || n >= a.kv.capacity) return;       // full (or corrupt) segment: unchanged
+// 256 threads append the new rows of 256 / TPS segments: TPS = 2 * row_bytes
+// / 16 threads per segment, one 16-byte chunk of the K or V row each (a step
+// appends a few hundred KB in all, so the launch is latency-bound and fewer,
+// fuller workgroups finish it sooner than one small workgroup per segment).
+__global__ __launch_bounds__(256) void k_append(AppendArgs a) {
+    const int cpr = a.row_bytes >> 4;              // chunks per row
+    const int tps = 2 * cpr;                       // threads per segment (power of two, <= 256)
+    const int s = (int)(((int64_t)blockIdx.x * 256 + threadIdx.x) / tps);
+    const int j = threadIdx.x & (tps - 1);
+    const int n = s < a.n_seg ? a.lengths[s] : -1;
+    __syncthreads();                               // every lane has read its segment's length
+    if (s >= a.n_seg || n < 0 || n >= a.kv.capacity) return;   // full (or corrupt) segment: unchanged
     const int64_t r = a.kv.row(s, n);
-    const int cpr = a.row_bytes >> 4;
-    for (int q = threadIdx.x; q < cpr; q += 64) {
-        reinterpret_cast<uint4*>(a.kv.k + r * a.row_bytes)[q] =
-            reinterpret_cast<const uint4*>(a.k_new + (int64_t)s * a.row_bytes)[q];
-        reinterpret_cast<uint4*>(a.kv.v + r * a.row_bytes)[q] =
-            reinterpret_cast<const uint4*>(a.v_new + (int64_t)s * a.row_bytes)[q];
-    }
-    if (threadIdx.x == 0) {
+    if (j < cpr)
+        reinterpret_cast<uint4*>(a.kv.k + r * a.row_bytes)[j] =
+            reinterpret_cast<const uint4*>(a.k_new + (int64_t)s * a.row_bytes)[j];
+    else
+        reinterpret_cast<uint4*>(a.kv.v + r * a.row_bytes)[j - cpr] =
+            reinterpret_cast<const uint4*>(a.v_new + (int64_t)s * a.row_bytes)[j - cpr];
+    if (j == 0) {
         a.kv.pos[r] = a.pos_new[a.shape.seq(s)];
         a.lengths[s] = n + 1;
     }
@@ -31,8 +37,11 @@ __global__ __launch_bounds__(64) void k_append(AppendArgs a) {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
     if (a.n_seg == 0) return hipSuccess;
+    const int tps = 2 * (a.row_bytes >> 4);
+    if (a.row_bytes % 16 || tps < 1 || tps > 256 || (tps & (tps - 1))) return hipErrorInvalidValue;
+    const int64_t blocks = ((int64_t)a.n_seg * tps + 255) / 256;
     TimedLaunch tl(KID_APPEND, stream);
-    hipLaunchKernelGGL(k_append, dim3((unsigned)a.n_seg), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(k_append, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -66,6 +66,8 @@ struct PhaseArgs {
     const int32_t* t;       // [n_seq]
     float* ctab;            // [n_layers][n_seq][Hq][D]
     int32_t* fb_reset;      // optional: a pruning pass without candidate mode zeroes its fallback count
+    uint32_t* zero;         // optional: words [0, zero_words) cleared (the split select's histograms)
+    int64_t zero_words;
     int32_t layer0, n_layers, n_seq, n_q_heads, head_dim;
 };
 hipError_t launch_phase(const PhaseArgs& a, hipStream_t stream);
@@ -187,7 +189,8 @@ struct SplitSelArgs {
     const int32_t* lengths;
     int32_t budget;
     uint32_t* akey;         // workspace [n_seg][cap]: order keys of the aggregates
-    uint32_t* hist;         // workspace [n_seg][3][2048]: digit histograms (zeroed by the first launch's fill)
+    uint32_t* hist;         // workspace [n_seg][3][2048]: digit histograms (zeroed by the first launch's fill,
+                            // or beforehand when `zeroed`: split_select_zero_words words from hist)
     uint32_t* ccnt;         // workspace [n_seg][n_chunks][2]: keys above / at the cut per chunk
     uint32_t* state;        // workspace [n_seg][4]: N, cut, how many at the cut to keep, fallback flag
     int32_t* fb_list;
@@ -196,7 +199,13 @@ struct SplitSelArgs {
     int64_t idx_stride;
     int32_t* n_kept;
     int32_t n_seg;
+    bool zeroed;            // hist and state already cleared (by the phase kernel of the same pass)
+    bool gather;            // the emission also copies each kept row (K, V, position) from src to dst
+    CacheView src;
+    CacheOut dst;
+    int32_t row_bytes;
 };
+int64_t split_select_zero_words(int64_t n_seg);
 hipError_t launch_split_select(const SplitSelArgs& a, int group, bool cand, hipStream_t stream);
 
 // --- gather (unfused compaction)

@@ -17,31 +17,37 @@
 namespace tri {
 
 // ------------------------------------------------------------------ phase
+// One thread per (layer, sequence, query head, band): C = P e^{i w_f t} in
+// fp64, rounded once to fp32.  The same threads (grid-stride) clear the words
+// a later kernel of the pass accumulates into.
 __global__ __launch_bounds__(256) void k_phase(PhaseArgs a) {
     const int F = a.head_dim / 2;
-    const int64_t total = (int64_t)a.n_layers * a.n_seq * F;
+    const int64_t total = (int64_t)a.n_layers * a.n_seq * a.n_q_heads * F;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i == 0 && a.fb_reset) *a.fb_reset = 0;
+    for (int64_t z = i; z < a.zero_words; z += (int64_t)gridDim.x * blockDim.x) a.zero[z] = 0u;
     if (i >= total) return;
     const int f = (int)(i % F);
-    const int b = (int)((i / F) % a.n_seq);
-    const int l = (int)(i / ((int64_t)F * a.n_seq));
+    const int64_t r = i / F;                       // (l, b, hq)
+    const int hq = (int)(r % a.n_q_heads);
+    const int b = (int)((r / a.n_q_heads) % a.n_seq);
+    const int l = (int)(r / ((int64_t)a.n_q_heads * a.n_seq));
     double sn, cs;
     sincos(a.omega[f] * (double)a.t[b], &sn, &cs);
-    const double2* P = a.P + ((int64_t)(a.layer0 + l) * a.n_q_heads) * F + f;
-    float* out = a.ctab + ((int64_t)(l * a.n_seq + b) * a.n_q_heads) * a.head_dim + f;
-    for (int hq = 0; hq < a.n_q_heads; ++hq) {
-        const double2 p = P[(int64_t)hq * F];
-        out[(int64_t)hq * a.head_dim] = (float)(p.x * cs - p.y * sn);
-        out[(int64_t)hq * a.head_dim + F] = (float)(p.x * sn + p.y * cs);
-    }
+    const double2 p = a.P[((int64_t)(a.layer0 + l) * a.n_q_heads + hq) * F + f];
+    float* out = a.ctab + r * a.head_dim + f;
+    out[0] = (float)(p.x * cs - p.y * sn);
+    out[F] = (float)(p.x * sn + p.y * cs);
 }
 
 hipError_t launch_phase(const PhaseArgs& a, hipStream_t stream) {
-    const int64_t total = (int64_t)a.n_layers * a.n_seq * (a.head_dim / 2);
-    if (total == 0) return hipSuccess;
+    const int64_t total = (int64_t)a.n_layers * a.n_seq * a.n_q_heads * (a.head_dim / 2);
+    const int64_t zb = (a.zero_words + 1023) / 1024;           // four words per thread
+    int64_t blocks = (total + 255) / 256;
+    if (zb > blocks) blocks = zb < 4096 ? zb : 4096;
+    if (blocks == 0) return hipSuccess;
     TimedLaunch tl(KID_PHASE, stream);
-    hipLaunchKernelGGL(k_phase, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_phase, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

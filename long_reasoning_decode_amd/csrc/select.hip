@@ -1000,11 +1000,32 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_count(SplitSelArgs a) {
     }
 }
 
+// Copy of kept rows [o0, o0 + n) of segment s, whose source slots are
+// src_of[0 .. n), by the whole workgroup (16-byte chunks; positions after).
+__device__ __forceinline__ void split_copy_rows(const SplitSelArgs& a, int s, int o0, int n, const int32_t* src_of) {
+    const int cpr = a.row_bytes >> 4;
+    const int lg = 31 - __clz(cpr);
+    for (int u = threadIdx.x; u < n * cpr; u += kSplitThreads) {
+        const int jrow = u >> lg, q = u & (cpr - 1);
+        const int64_t sr = a.src.row(s, src_of[jrow]);
+        const int64_t dr = a.dst.row(s, o0 + jrow);
+        const uint4 kv = reinterpret_cast<const uint4*>(a.src.k + sr * a.row_bytes)[q];
+        const uint4 vv = reinterpret_cast<const uint4*>(a.src.v + sr * a.row_bytes)[q];
+        reinterpret_cast<uint4*>(a.dst.k + dr * a.row_bytes)[q] = kv;
+        reinterpret_cast<uint4*>(a.dst.v + dr * a.row_bytes)[q] = vv;
+    }
+    for (int jrow = threadIdx.x; jrow < n; jrow += kSplitThreads)
+        a.dst.pos[a.dst.row(s, o0 + jrow)] = a.src.pos[a.src.row(s, src_of[jrow])];
+}
+
 // Launch 5: kept slots of the chunk, each at its place in slot order
 // (out = keys above the cut before it + min(keys at the cut before it, need)).
+// A chunk's kept keys take consecutive places, so with `gather` the
+// workgroup then copies that run of rows.
 __global__ __launch_bounds__(kSplitThreads) void k_split_emit(SplitSelArgs a) {
     __shared__ uint32_t wsum[kSplitThreads / kWave], bg_w[kSplitThreads / kWave], be_w[kSplitThreads / kWave];
     __shared__ uint32_t base[2];
+    __shared__ int32_t src_of[2048];                  // gather: source slot of the chunk's kept place o0 + j
     const int s = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & (kWave - 1), w = tid / kWave;
     const uint32_t* st = a.state + (int64_t)s * kSplitState;
@@ -1012,8 +1033,16 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_emit(SplitSelArgs a) {
     const int c0 = c * a.chunk;
     int32_t* idx = a.idx + (int64_t)s * a.idx_stride;
     if (N <= a.budget) {                              // every key kept, in slot order
-        for (int i = c0 + tid; i < min(N, c0 + a.chunk); i += kSplitThreads) idx[i] = i;
+        const int end = min(N, c0 + a.chunk);
+        for (int i = c0 + tid; i < end; i += kSplitThreads) {
+            idx[i] = i;
+            if (a.gather) src_of[i - c0] = i;
+        }
         if (c == 0 && tid == 0 && a.n_kept) a.n_kept[s] = N;
+        if (a.gather && end > c0) {
+            __syncthreads();
+            split_copy_rows(a, s, c0, end - c0, src_of);
+        }
         return;
     }
     if (c0 >= N || st[3]) return;                     // no keys here, or left to the fallback
@@ -1034,6 +1063,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_emit(SplitSelArgs a) {
         __syncthreads();
     }
     uint32_t gb = base[0], eb = base[1];
+    const int o0 = (int)min(gb + min(eb, (uint32_t)need), (uint32_t)a.budget);   // the chunk's first place
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     const uint32_t* ak = a.akey + (int64_t)s * a.cap + c0;
     for (int i0 = 0; i0 < cnt; i0 += kSplitThreads) {   // block-uniform
@@ -1058,13 +1088,26 @@ __global__ __launch_bounds__(kSplitThreads) void k_split_emit(SplitSelArgs a) {
         }
         if (gt || (eq && (int)e_before < need)) {
             const uint32_t out = g_before + min(e_before, (uint32_t)need);
-            if (out < (uint32_t)a.budget) idx[out] = c0 + i;
+            if (out < (uint32_t)a.budget) {
+                idx[out] = c0 + i;
+                if (a.gather) src_of[out - o0] = c0 + i;
+            }
         }
         gb += g_all;
         eb += e_all;
         __syncthreads();                                // bg_w / be_w are rewritten next pass
     }
     if (c == 0 && tid == 0 && a.n_kept) a.n_kept[s] = a.budget;
+    if (a.gather) {
+        const int o1 = (int)min(gb + min(eb, (uint32_t)need), (uint32_t)a.budget);   // past the chunk's last place
+        if (o1 > o0) split_copy_rows(a, s, o0, o1 - o0, src_of);      // (src_of complete: the loop's last barrier)
+    }
+}
+
+// Histograms, then the state words, from SplitSelArgs::hist.
+int64_t split_select_zero_words(int64_t n_seg) {
+    static_assert(kSplitHist % 64 == 0, "the state words follow the histograms");
+    return n_seg * (kSplitHist + kSplitState);
 }
 
 template <int G>
@@ -1084,10 +1127,11 @@ hipError_t launch_split_select(const SplitSelArgs& a, int group, bool cand, hipS
     if (a.budget > kMaxBudget || a.chunk % 32 || a.chunk > 2048 || a.n_chunks > 65535) return hipErrorInvalidValue;
     TimedLaunch tl(KID_SPLIT_SELECT, stream);
     // histograms and state start at zero
-    const int64_t words = (int64_t)a.n_seg * (kSplitHist + kSplitState);
-    static_assert(kSplitHist % 64 == 0, "the state words follow the histograms");
-    const int64_t fill_blocks = (words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096;
-    hipLaunchKernelGGL(k_split_fill, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.hist, words);
+    if (!a.zeroed) {
+        const int64_t words = split_select_zero_words(a.n_seg);
+        const int64_t fill_blocks = (words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096;
+        hipLaunchKernelGGL(k_split_fill, dim3((unsigned)fill_blocks), dim3(256), 0, stream, a.hist, words);
+    }
     switch (group) {
         case 1: split_launch_g<1>(a, cand, stream); break;
         case 2: split_launch_g<2>(a, cand, stream); break;
