@@ -299,6 +299,74 @@ def test_paged_prune_into_fresh_pages_of_the_same_pool(gpu_lib):
         assert torch.equal(pool[key][:n_src], g[key]), f"{key}: source pages were written"
 
 
+@pytest.mark.parametrize("page_size", [16, 24])
+def test_paged_split_select_into_fresh_pages(gpu_lib, page_size):
+    """Few paged segments of at least 8192 slots, out of place: the split
+    select, whose emission copies each chunk's kept rows into the fresh pages.
+    Byte for byte the unfused chain's result (tri_compact's gather) on every
+    segment, and the oracle's selection and compaction on a sample."""
+    T = gpu_lib
+    cfg = W.CONFIGS["ragged"].replace(n_seq=2, len_range=(7000, 12000), budget=1024, seed=17, page_size=page_size)
+    log(f"case paged split select, {page_size}-token pages")
+    pc = W.paged_cache(cfg, "cpu")
+    g = _to(pc, "cuda")
+    calib, cal = calib_for(T, cfg)
+    B, n_seg = cfg.budget, cfg.n_seg
+    src = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["page_table"], page_size=cfg.page_size,
+                       max_pages=g["max_pages"])
+    cap = cfg.page_size * g["max_pages"]
+    assert n_seg < 256 and cap >= 8192, "the case must take the split select"
+    ws = T.workspace(calib, src, B)
+    agg = torch.zeros((n_seg, cap), device="cuda")
+    T.tri_score(calib, src, g["t"], agg, ws)
+    idx = torch.full((n_seg, B), -1, dtype=torch.int32, device="cuda")
+    nk = torch.zeros((n_seg,), dtype=torch.int32, device="cuda")
+    T.tri_select_topb(agg, g["lengths"], B, idx, nk)
+    dst = T.cache_desc(g["out_k"], g["out_v"], g["out_pos"], nk, n_layers=1, n_seq=cfg.n_seq,
+                       n_kv_heads=cfg.n_kv_heads, page_table=g["out_page_table"], page_size=cfg.page_size,
+                       max_pages=g["out_max_pages"])
+    T.tri_compact(src, idx, nk, B, dst)
+    torch.cuda.synchronize()
+    first = {k: g[k].clone() for k in ("out_k", "out_v", "out_pos")}
+    for k in ("out_k", "out_v", "out_pos"):
+        g[k].fill_(-1)
+    nk2 = torch.zeros_like(nk)
+    dst2 = T.cache_desc(g["out_k"], g["out_v"], g["out_pos"], nk2, n_layers=1, n_seq=cfg.n_seq,
+                        n_kv_heads=cfg.n_kv_heads, page_table=g["out_page_table"], page_size=cfg.page_size,
+                        max_pages=g["out_max_pages"])
+    T.tri_prune_window(calib, src, g["t"], B, dst2, nk2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(nk2, nk)
+    lengths = pc["lengths"].numpy()
+    for s in range(n_seg):
+        nks = min(int(lengths[s]), B)
+        opt = pc["out_page_table"][s].numpy()
+        for k in ("out_k", "out_v", "out_pos"):
+            a = oracle.paged_rows(stored_t(g[k].cpu()).numpy() if k != "out_pos" else g[k].cpu().numpy(),
+                                  opt, cfg.page_size, nks)
+            b = oracle.paged_rows(stored_t(first[k].cpu()).numpy() if k != "out_pos" else first[k].cpu().numpy(),
+                                  opt, cfg.page_size, nks)
+            assert np.array_equal(a, b), f"seg {s}: {k} differs from the unfused chain"
+    for s in (0, n_seg // 2, n_seg - 1):
+        N = int(lengths[s])
+        t = int(pc["t"][seg_seq(cfg, s)])
+        pt = pc["page_table"][s].numpy()
+        K = oracle.paged_rows(stored(pc["k"]), pt, cfg.page_size, N)
+        V = oracle.paged_rows(stored(pc["v"]), pt, cfg.page_size, N)
+        P = oracle.paged_rows(pc["pos"].numpy(), pt, cfg.page_size, N)
+        ref = oracle_segment(cfg, cal, K, V, P, t, s, B)
+        tag = f"paged split seg {s} N={N}"
+        nks = min(N, B)
+        ix = idx[s, :nks].cpu().numpy()
+        check_selection(ix, ref["A"], B, tag)
+        opt = pc["out_page_table"][s].numpy()
+        Kd = oracle.paged_rows(stored(g["out_k"].cpu()), opt, cfg.page_size, nks)
+        Vd = oracle.paged_rows(stored(g["out_v"].cpu()), opt, cfg.page_size, nks)
+        Pd = oracle.paged_rows(g["out_pos"].cpu().numpy(), opt, cfg.page_size, nks)
+        check_compaction(K, V, P, Kd, Vd, Pd, ix, tag)
+
+
 @pytest.mark.parametrize("in_place", [False, True, "fill"])
 def test_decode_loop_small(gpu_lib, in_place):
     """Append + decode attention each step, prune after each window (into the
@@ -658,20 +726,25 @@ def test_decode_attention_batch_sizes(gpu_lib, d, G, n_seq):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_append_rows_and_full_segments(gpu_lib, dtype):
+@pytest.mark.parametrize("d,n_seq,hkv", [(64, 2, 3), (128, 7, 5), (64, 9, 4)])
+def test_append_rows_and_full_segments(gpu_lib, dtype, d, n_seq, hkv):
     """tri_append writes row lengths[s] of each segment (K, V bit-exact, the
-    sequence's position) and grows the length; a full segment is unchanged."""
+    sequence's position) and grows the length; a full segment is unchanged.
+    Workgroups hold several segments (16, 8 or 4 per 256 threads): batches of
+    up to 36 segments span several of them and end part-way through one."""
     T = gpu_lib
-    n_seq, hkv, d, cap = 2, 3, 64, 40
+    cap = 40
     n_seg = n_seq * hkv
-    gen = torch.Generator().manual_seed(43)
+    gen = torch.Generator().manual_seed(43 + d + n_seg)
     K = torch.randn((n_seg, cap, d), generator=gen).to(dtype)
     V = torch.randn((n_seg, cap, d), generator=gen).to(dtype)
     pos = torch.randint(0, 1000, (n_seg, cap), generator=gen, dtype=torch.int32)
-    ln = torch.tensor([0, 5, cap - 1, cap, 17, 39], dtype=torch.int32)
+    ln = torch.randint(0, cap + 1, (n_seg,), generator=gen, dtype=torch.int32)
+    ln[:6] = torch.tensor([0, 5, cap - 1, cap, 17, 39], dtype=torch.int32)
+    ln[-1] = cap
     kn = torch.randn((n_seg, d), generator=gen).to(dtype)
     vn = torch.randn((n_seg, d), generator=gen).to(dtype)
-    pn = torch.tensor([7001, 7002], dtype=torch.int32)
+    pn = 7001 + torch.arange(n_seq, dtype=torch.int32)
     g = {"k": K.cuda(), "v": V.cuda(), "pos": pos.cuda(), "lengths": ln.cuda()}
     desc = T.cache_desc(g["k"], g["v"], g["pos"], g["lengths"], n_layers=1, n_seq=n_seq, n_kv_heads=hkv)
     T.tri_append(desc, kn.cuda(), vn.cuda(), pn.cuda())
