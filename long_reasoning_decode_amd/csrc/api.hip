@@ -601,6 +601,13 @@ int tri_compact(const tri_cache_desc* src, const int32_t* idx, const int32_t* n_
 // more than the score writes it saves (one 32K-key layer, 8 segments: 0.17 ms
 // with the candidate pass, 0.13 ms without).
 constexpr int64_t kCandidateMinSegs = 256;
+// Candidate lists the automatic path lets one select workgroup hold: up to
+// 16 entries per thread, two workgroups share a CU and one's gather hides the
+// other's list rebuild.  Longer lists (segments below 8B keep every key, so
+// a cache of 64K-key capacity at B = 4096 holds 32K) leave one workgroup per
+// CU, where rebuilding the lists costs more than the score writes the pass
+// saves (the ragged batch: 1.74 ms with the candidate pass, 1.65 ms without).
+constexpr int64_t kCandidateMaxHeld = 16 * 1024;
 
 // ---------------------------------------------------------------- library-owned scratch
 // Workspace of tri_prune_window_static: a file-scope device array, so the
@@ -675,7 +682,9 @@ static int prune_window(tri_calib_t calib, const tri_cache_desc* src, const int3
     // to fill the GPU.  Otherwise (fp32, capacity below what candidate mode
     // needs, or the full path asked for): the full path.
     const bool cand = src->dtype == TRI_DTYPE_BF16 && candidate_mode(src->capacity, budget) &&
-                      (path == TRI_PATH_CANDIDATES || (path == TRI_PATH_AUTO && n_segments(src) >= kCandidateMinSegs));
+                      (path == TRI_PATH_CANDIDATES ||
+                       (path == TRI_PATH_AUTO && n_segments(src) >= kCandidateMinSegs &&
+                        candidate_select_held(src->capacity, budget) <= kCandidateMaxHeld));
     // (without candidate mode nothing falls back: the phase kernel zeroes the count tri_prune_fallbacks reads;
     // with the split select it also clears that select's histograms)
     const bool ssel = !in_place && split_select(src);

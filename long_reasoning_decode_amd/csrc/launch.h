@@ -31,6 +31,16 @@ enum KernelId : int {
 // candidate list (keys whose score can reach the top B) instead of every key.
 // Small segments, and budgets above 1/8 of the segment, keep every key.
 __host__ __device__ inline bool candidate_mode(int64_t N, int64_t B) { return N >= 4096 && N >= 8 * B; }
+// Entries the candidate-mode select holds per workgroup for segments of up to
+// max_len keys: every key of a segment outside candidate mode (N < max(4096,
+// 8B)), or half of the longest segment's keys (the sampled threshold admits
+// about 3B/N of them, at most 3/8 since N >= 8B); a longer list sends its
+// segment to the fallback.
+inline int64_t candidate_select_held(int64_t max_len, int64_t budget) {
+    const int64_t small = 8 * budget > 4096 ? 8 * budget : 4096;
+    const int64_t half = (max_len + 1) / 2 > small ? (max_len + 1) / 2 : small;
+    return half < max_len ? half : max_len;
+}
 
 // In candidate mode, wave w of a scoring workgroup scores the 32-key blocks
 // w, w+4, w+8, ... of its chunk; its candidate list starts after the keys of

@@ -706,13 +706,7 @@ hipError_t launch_select(const SelectArgs& a, int group, int mode, int64_t max_l
     if (a.budget > kMaxBudget || max_len > 64 * kSelThreads) return hipErrorInvalidValue;
     int64_t held = max_len;                             // entries one thread block holds in registers
     if (mode == SELECT_C) {
-        // every key of a segment outside candidate mode (N < max(4096, 8B)), or
-        // half of the longest segment's keys (the sampled threshold admits about
-        // 3 B/N of them, at most 3/8 since N >= 8 B); a longer list sends its
-        // segment to the fallback (full rescoring, mode S)
-        const int64_t small = 8 * (int64_t)a.budget > 4096 ? 8 * (int64_t)a.budget : 4096;
-        const int64_t half = (max_len + 1) / 2 > small ? (max_len + 1) / 2 : small;
-        held = half < max_len ? half : max_len;
+        held = candidate_select_held(max_len, a.budget);   // a longer list: fallback (full rescoring, mode S)
         if (a.chunk % 512 || a.chunk > 2048) return hipErrorInvalidValue;
     }
     const KernelId id = mode == SELECT_S_FALLBACK ? KID_SELECT_FALLBACK : a.gather ? KID_SELECT_GATHER : KID_SELECT;

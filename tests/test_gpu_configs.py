@@ -195,6 +195,25 @@ def test_ragged_paged_full(gpu_lib, part):
     if part:
         return
 
+    # the candidate pass (which the automatic path leaves out on this batch:
+    # its lists of up to 32K entries need one select workgroup per CU) writes
+    # the same pages on every segment
+    cand = {k: torch.zeros_like(pc["out_" + k]) for k in ("k", "v", "pos")}
+    nkc = torch.zeros_like(nk)
+    dstc = T.cache_desc(cand["k"], cand["v"], cand["pos"], nkc, n_layers=1, n_seq=cfg.n_seq,
+                        n_kv_heads=cfg.n_kv_heads, page_table=pc["out_page_table"], page_size=cfg.page_size,
+                        max_pages=pc["out_max_pages"])
+    T.tri_prune_window(calib, src, pc["t"], B, dstc, nkc, ws, path=T.TRI_PATH_CANDIDATES)
+    torch.cuda.synchronize()
+    log(f"  candidate pass: {T.tri_prune_fallbacks(ws)} fallbacks")
+    assert torch.equal(nkc, nk)
+    CK, CV, CP = stored(cand["k"].cpu()), stored(cand["v"].cpu()), cand["pos"].cpu().numpy()
+    for s in range(cfg.n_seg):
+        nks = min(int(lengths[s]), B)
+        for a, b, key in ((CK, OKp, "k"), (CV, OVp, "v"), (CP, OPp, "pos")):
+            assert np.array_equal(oracle.paged_rows(a, opt[s], cfg.page_size, nks),
+                                  oracle.paged_rows(b, opt[s], cfg.page_size, nks)), f"seg {s}: candidate pass {key}"
+
     # decode attention reading the pruned pages in place
     sample = [0, 101, 257, cfg.n_seg - 1]
     gq = torch.Generator().manual_seed(5)
