@@ -34,7 +34,7 @@ __host__ __device__ inline bool candidate_mode(int64_t N, int64_t B) { return N 
 // Entries the candidate-mode select holds per workgroup for segments of up to
 // max_len keys: every key of a segment outside candidate mode (N < max(4096,
 // 8B)), or half of the longest segment's keys (the sampled threshold admits
-// about 3B/N of them, at most 3/8 since N >= 8B); a longer list sends its
+// about 2.5B/N of them, at most 5/16 since N >= 8B); a longer list sends its
 // segment to the fallback.
 inline int64_t candidate_select_held(int64_t max_len, int64_t budget) {
     const int64_t small = 8 * budget > 4096 ? 8 * budget : 4096;

@@ -617,14 +617,17 @@ __global__ __launch_bounds__(256) void k_score_mfma_fallback(ScoreArgs a) {
 // ------------------------------------------------------------------ candidate thresholds
 // One workgroup per segment scores an evenly spaced sample of kSample keys in
 // fp32, estimates each head's mean and spread and the aggregated score at rank
-// kCandMul * B/N of the sample, and stores per-head score thresholds
+// (kCandNum / kCandDen) * B/N of the sample, and stores per-head score thresholds
 // L_h = mean_h + tau * spread_h.  Keys with no S_h >= L_h are left out of the
 // candidate list; the select kernel then proves with the exact statistics that
 // none of them can be among the B kept (else the segment is redone in full).
 // The thresholds only decide how much work is skipped, never the result.
 constexpr int kSample = 256;
 static_assert(kSample <= 256, "sample index fits the low 8 bits of a rank key");
-constexpr int kCandMul = 3;
+// rank 2.5 B/N: about 2.5 B candidates per segment, a margin of about 3.4
+// threshold errors to the cut (rank 2 B/N left 19 of the main workload's 4608
+// segments to the fallback; 3 B/N lists a fifth more records)
+constexpr int kCandNum = 5, kCandDen = 2;
 
 template <int D, int G>
 __global__ __launch_bounds__(kSample) void k_sample(SampleArgs a) {
@@ -734,8 +737,8 @@ __global__ __launch_bounds__(kSample) void k_sample(SampleArgs a) {
     ak[tid] = mykey;
     if (tid == 0) tau_s = -__builtin_inff();   // (every rank is taken once)
     __syncthreads();
-    // tau = the r-th largest sample aggregate, r = ceil(kCandMul B kSample / N)
-    const int64_t r64 = ((int64_t)kCandMul * a.budget * kSample + N - 1) / N;
+    // tau = the r-th largest sample aggregate, r = ceil(kCandNum B kSample / (kCandDen N))
+    const int64_t r64 = ((int64_t)kCandNum * a.budget * kSample + (int64_t)kCandDen * N - 1) / ((int64_t)kCandDen * N);
     const int r = (int)(r64 < 1 ? 1 : r64 > kSample ? kSample : r64);
     int rank = 0;
     const uint4* ak4 = reinterpret_cast<const uint4*>(ak);
