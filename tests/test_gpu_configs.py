@@ -52,6 +52,30 @@ def _dense_properties(g, out, B, what):
             assert bool(torch.all(same | ~valid[sl])), f"{what}: {key} rows"
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_candidate_pass_equals_full_path_on_other_draws(gpu_lib, seed):
+    """32 segments of the main workload's shape (32,768 bf16 keys, d = 128,
+    GQA 4, B = 2048) drawn with other seeds: the candidate pass (threshold at
+    sample rank 2.5B/N, certified or redone) writes the same cache byte for
+    byte as the full-score path; the fallback count is logged."""
+    T = gpu_lib
+    cfg = W.CONFIGS["qwen1l"].replace(n_seq=4, n_keys=32768, seed=seed)
+    B = cfg.budget
+    log(f"case candidate pass vs full path, seed {seed}: {cfg.n_seg} segments x {cfg.n_keys}")
+    g = W.dense_cache(cfg, "cuda")
+    calib, _ = calib_for(T, cfg)
+    _, _, full = _dense_prune(T, cfg, g, calib, B, path=T.TRI_PATH_FULL)
+    _, ws, cand = _dense_prune(T, cfg, g, calib, B, path=T.TRI_PATH_CANDIDATES)
+    torch.cuda.synchronize()
+    log(f"  candidate pass: {T.tri_prune_fallbacks(ws)} fallbacks")
+    for key in ("k", "v", "pos", "lengths"):
+        a, b = full[key], cand[key]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), f"seed {seed}: {key} differs between the paths"
+    _dense_properties(g, full, B, f"seed {seed}")
+
+
 def test_qwen_single_layer_full(gpu_lib):
     T = gpu_lib
     cfg = W.CONFIGS["qwen1l"]
